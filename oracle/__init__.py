@@ -1,0 +1,23 @@
+"""CPU oracle for paged attention decode.
+
+TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT. Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import or call anything in this package. The HIP library never imports it, and
+nothing here imports the HIP library or its Python binding.
+
+Everything is plain NumPy in float64; see ``paged_attention.py`` for the
+passages each function follows.
+"""
+
+from .paged_attention import (  # noqa: F401
+    blocks_needed,
+    copy_blocks,
+    decode,
+    decode_partitions,
+    gather_rows,
+    kv_append,
+    last_block_waste,
+    slot_of,
+    splitkv_merge,
+    to_f64,
+)

@@ -1,0 +1,329 @@
+"""Plain float64 CPU oracle of paged attention decode and its KV writes.
+
+TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT: only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import this module. It shares no code with the HIP library and imports nothing
+from it.
+
+The method (paged attention, as described on the five pages this work follows)
+changes only *where* a sequence's keys and values live: the KV cache is cut into
+fixed-size physical blocks, and a per-sequence block table maps logical block j
+to a physical block. Attention itself is the textbook one. So this oracle is
+that definition written out plainly:
+
+1. gather the sequence's key/value rows in logical order through the block
+   table (the indexing rule of "How Paged Attention and Continuous Batching
+   Actually Work", section "Paged attention: virtual memory for the KV cache";
+   "LLM paged attention arch", section "The architecture: every piece
+   explained", which states that table entry i backs logical tokens
+   [16i, 16i+15]);
+2. score every past token with q.k / sqrt(d_k) ("Paged Attention as a Memory
+   Manager", section "How the Kernel Executes Paged Attention");
+3. subtract the maximum score, exponentiate, normalise, and take the weighted
+   sum of value rows (same section, "Softmax and output reduction"; "PagedAttention
+   and continuous batching", section "Attention kernel modification").
+
+The oracle deliberately uses the two-pass form (max first, then the weighted
+sum); the GPU kernels use a running softmax, which is the same function in exact
+arithmetic.
+
+Storage conventions (shared with the caller only as array shapes):
+
+* A KV pool is an array ``[num_blocks][num_kv_heads][block_size][head_dim]``.
+  K and V live in two separate pools of that shape.
+* Values of dtype ``"f32"`` are ``numpy.float32`` arrays; values of dtype
+  ``"bf16"`` are ``numpy.uint16`` arrays holding bfloat16 bit patterns.
+* ``block_tables`` is ``[num_seqs][max_blocks]`` of int32; only the first
+  ceil(L_i / block_size) entries of row i are ever read.
+* ``context_lens[i]`` = L_i counts every token sequence i attends to, including
+  the token appended this step.
+* Query head h belongs to KV head h // G, with G = num_heads / num_kv_heads
+  (contiguous query-head groups; the pages only name grouped-query attention).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# Value decoding (exact)
+# ---------------------------------------------------------------------------
+
+def to_f64(values, dtype: str) -> np.ndarray:
+    """Widen stored values to float64 without rounding.
+
+    bfloat16 is the upper half of an IEEE binary32, so its bit pattern shifted
+    left by 16 is the binary32 with the same value; binary32 widens exactly to
+    binary64.
+    """
+    if dtype == "f32":
+        return np.asarray(values, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        bits = np.asarray(values, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# ---------------------------------------------------------------------------
+# Block arithmetic
+# ---------------------------------------------------------------------------
+
+def blocks_needed(num_tokens: int, block_size: int) -> int:
+    """Blocks held by a sequence of ``num_tokens`` tokens: ceil(t / B).
+
+    "How Paged Attention and Continuous Batching Actually Work", section "Paged
+    attention: virtual memory for the KV cache" (a request with t tokens holds
+    ceil(t/16) blocks).
+    """
+    if num_tokens < 0 or block_size <= 0:
+        raise ValueError("num_tokens must be >= 0 and block_size > 0")
+    return -(-num_tokens // block_size)
+
+
+def last_block_waste(num_tokens: int, block_size: int) -> int:
+    """Unused token slots in the sequence's last block: B*ceil(t/B) - t.
+
+    Same section: the waste is bounded by one partial block, i.e. at most B-1
+    slots (15 for 16-token blocks).
+    """
+    return blocks_needed(num_tokens, block_size) * block_size - num_tokens
+
+
+def slot_of(table_row, position: int, block_size: int) -> int:
+    """Flat slot of logical token ``position`` of one sequence.
+
+    The indexing rule of "How Paged Attention and Continuous Batching Actually
+    Work", section "Paged attention: virtual memory for the KV cache" (the
+    formula itself is lost from the extracted page; its prose survives): divide
+    the position by the block size to find the logical block, look up the
+    physical block in the table, multiply by the block size and add the offset
+    inside the block.  The slot s addresses row (s // B, s % B) of the pool.
+    """
+    logical_block = position // block_size
+    offset = position % block_size
+    return int(table_row[logical_block]) * block_size + offset
+
+
+def gather_rows(pool: np.ndarray, table_row, length: int, block_size: int,
+                kv_head: int) -> np.ndarray:
+    """Rows 0..length-1 of one KV head of one sequence, in logical order.
+
+    Returns the stored values (no conversion), shape ``[length][head_dim]``.
+    Follows the block-level loop of "Paged Attention as a Memory Manager",
+    section "How the Kernel Executes Paged Attention": for every logical block,
+    read its physical block from the table, then read the rows inside it.
+    Only rows of positions < length are read, which is the padding mask of the
+    same section applied before anything is computed.
+    """
+    if pool.shape[2] != block_size:
+        raise ValueError("pool block dimension does not match block_size")
+    pieces = [pool[:0, kv_head, 0, :]]
+    for logical_block in range(blocks_needed(length, block_size)):
+        physical_block = int(table_row[logical_block])
+        rows_here = min(block_size, length - logical_block * block_size)
+        pieces.append(pool[physical_block, kv_head, :rows_here, :])
+    return np.concatenate(pieces)
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+
+def _check_shapes(q, k_pool, v_pool, block_tables, context_lens):
+    num_seqs, num_heads, head_dim = q.shape
+    num_blocks, num_kv_heads, block_size, head_dim_k = k_pool.shape
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("K and V pools differ in shape")
+    if head_dim_k != head_dim:
+        raise ValueError("head_dim of q and of the pools differ")
+    if num_heads % num_kv_heads:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    if len(block_tables) != num_seqs or len(context_lens) != num_seqs:
+        raise ValueError("one block-table row and one context length per sequence")
+    return num_seqs, num_heads, head_dim, num_kv_heads, block_size
+
+
+def _softmax_weighted_sum(scores: np.ndarray, values: np.ndarray):
+    """Two-pass softmax-weighted sum of value rows.
+
+    "Paged Attention as a Memory Manager", section "How the Kernel Executes
+    Paged Attention" (softmax and output reduction): reduce to the maximum
+    score for numerical stability, then accumulate the weighted sum of value
+    vectors.  Returns (output, max_score, sum_of_weights).
+    """
+    m = scores.max()
+    w = np.exp(scores - m)
+    total = w.sum()
+    return (w @ values) / total, m, total
+
+
+def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float,
+           dtype: str) -> np.ndarray:
+    """Decode attention of one query token per sequence over a paged KV cache.
+
+    For sequence i and query head h (KV head g = h // G):
+        s_t = scale * q[i,h] . k_t        for t < L_i
+        out[i,h] = sum_t softmax(s)_t * v_t
+    with k_t, v_t gathered through ``block_tables[i]``.  Score and scale are
+    those of "Paged Attention as a Memory Manager", section "How the Kernel
+    Executes Paged Attention"; the attended range K_{0:t} is that of
+    "PagedAttention and continuous batching", section "Attention kernel
+    modification".  A sequence with L_i = 0 gets an all-zero output (the pages
+    never produce one; decode always has the new token).
+
+    Returns float64 ``[num_seqs][num_heads][head_dim]``.
+    """
+    num_seqs, num_heads, head_dim, num_kv_heads, block_size = _check_shapes(
+        q, k_pool, v_pool, block_tables, context_lens)
+    group = num_heads // num_kv_heads
+    q64 = to_f64(q, dtype)
+    out = np.zeros((num_seqs, num_heads, head_dim), dtype=np.float64)
+    for i in range(num_seqs):
+        length = int(context_lens[i])
+        if length == 0:
+            continue
+        for g in range(num_kv_heads):
+            keys = to_f64(gather_rows(k_pool, block_tables[i], length, block_size, g), dtype)
+            values = to_f64(gather_rows(v_pool, block_tables[i], length, block_size, g), dtype)
+            for h in range(g * group, (g + 1) * group):
+                scores = scale * (keys @ q64[i, h])
+                out[i, h], _, _ = _softmax_weighted_sum(scores, values)
+    return out
+
+
+def decode_partitions(q, k_pool, v_pool, block_tables, context_lens, scale: float,
+                      dtype: str, partition_size: int, max_parts: int | None = None):
+    """Per-partition attention results for split-KV decode.
+
+    The pages never split a sequence's context; this follows the split-KV
+    reading used by this library: partition p of sequence i covers positions
+    [p*P, min((p+1)*P, L_i)).  For each (i, h, p) it returns
+
+        part_out  = softmax-weighted sum of v_t over the partition,
+        part_max  = max of the partition's scores s_t (natural units),
+        part_sum  = sum over the partition of exp(s_t - part_max).
+
+    An empty partition has part_out = 0, part_max = -inf, part_sum = 0.
+    Returns three float64 arrays shaped [S][Hq][max_parts][D], [S][Hq][max_parts]
+    and [S][Hq][max_parts].
+    """
+    num_seqs, num_heads, head_dim, num_kv_heads, block_size = _check_shapes(
+        q, k_pool, v_pool, block_tables, context_lens)
+    if partition_size <= 0:
+        raise ValueError("partition_size must be positive")
+    group = num_heads // num_kv_heads
+    if max_parts is None:
+        max_parts = max([blocks_needed(int(n), partition_size) for n in context_lens] + [1])
+    q64 = to_f64(q, dtype)
+    part_out = np.zeros((num_seqs, num_heads, max_parts, head_dim), dtype=np.float64)
+    part_max = np.full((num_seqs, num_heads, max_parts), -np.inf, dtype=np.float64)
+    part_sum = np.zeros((num_seqs, num_heads, max_parts), dtype=np.float64)
+    for i in range(num_seqs):
+        length = int(context_lens[i])
+        nparts = blocks_needed(length, partition_size)
+        if nparts > max_parts:
+            raise ValueError("max_parts too small for context_lens")
+        for g in range(num_kv_heads):
+            keys = to_f64(gather_rows(k_pool, block_tables[i], length, block_size, g), dtype)
+            values = to_f64(gather_rows(v_pool, block_tables[i], length, block_size, g), dtype)
+            for h in range(g * group, (g + 1) * group):
+                scores = scale * (keys @ q64[i, h])
+                for p in range(nparts):
+                    lo, hi = p * partition_size, min((p + 1) * partition_size, length)
+                    o, m, total = _softmax_weighted_sum(scores[lo:hi], values[lo:hi])
+                    part_out[i, h, p] = o
+                    part_max[i, h, p] = m
+                    part_sum[i, h, p] = total
+    return part_out, part_max, part_sum
+
+
+def splitkv_merge(part_out, part_max, part_sum, context_lens, partition_size: int):
+    """Merge per-partition results with their log-sum-exp weights.
+
+    Not on the pages (they describe one running softmax over the whole
+    context); this is the exact regrouping of that softmax over partitions:
+        M   = max_p part_max[p]
+        w_p = part_sum[p] * exp(part_max[p] - M)
+        out = sum_p w_p * part_out[p] / sum_p w_p
+        lse = M + ln(sum_p w_p)
+    over the ceil(L_i / P) partitions sequence i has; partitions with
+    part_sum = 0 get weight 0.  A sequence with L_i = 0 gets out = 0 and
+    lse = -inf.  Returns (out [S][Hq][D], lse [S][Hq]) in float64.
+    """
+    part_out = np.asarray(part_out, dtype=np.float64)
+    part_max = np.asarray(part_max, dtype=np.float64)
+    part_sum = np.asarray(part_sum, dtype=np.float64)
+    num_seqs, num_heads, max_parts, head_dim = part_out.shape
+    out = np.zeros((num_seqs, num_heads, head_dim), dtype=np.float64)
+    lse = np.full((num_seqs, num_heads), -np.inf, dtype=np.float64)
+    for i in range(num_seqs):
+        nparts = blocks_needed(int(context_lens[i]), partition_size)
+        if nparts > max_parts:
+            raise ValueError("context_lens need more partitions than part_out holds")
+        for h in range(num_heads):
+            live = [p for p in range(nparts) if part_sum[i, h, p] > 0]
+            if not live:
+                continue
+            big_m = max(part_max[i, h, p] for p in live)
+            weights = np.array([part_sum[i, h, p] * math.exp(part_max[i, h, p] - big_m) for p in live])
+            total = weights.sum()
+            out[i, h] = (weights @ part_out[i, h, live]) / total
+            lse[i, h] = big_m + math.log(total)
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# KV writes (byte-exact)
+# ---------------------------------------------------------------------------
+
+def kv_append(k_pool, v_pool, k_new, v_new, slot_mapping):
+    """Pools after writing each new token's K/V rows at its slot.
+
+    "How Paged Attention and Continuous Batching Actually Work", section "One
+    step, end to end" (the forward pass writes KV through the slot mapping);
+    "LLM paged attention arch", section "The architecture: every piece
+    explained" (the new token's K/V go into the right physical block).  Token n
+    with slot s >= 0 overwrites row (s // B, :, s % B, :) of both pools with
+    ``k_new[n]`` / ``v_new[n]`` (all KV heads), bit for bit; a negative slot
+    means "no write".  Every other byte stays as it was.  Two tokens with the
+    same slot are a caller error.
+    """
+    k_out = np.array(k_pool, copy=True)
+    v_out = np.array(v_pool, copy=True)
+    block_size = k_pool.shape[2]
+    slots = [int(s) for s in slot_mapping]
+    live = [s for s in slots if s >= 0]
+    if len(set(live)) != len(live):
+        raise ValueError("slot_mapping has a repeated slot")
+    for n, s in enumerate(slots):
+        if s < 0:
+            continue
+        k_out[s // block_size, :, s % block_size, :] = k_new[n]
+        v_out[s // block_size, :, s % block_size, :] = v_new[n]
+    return k_out, v_out
+
+
+def copy_blocks(k_pool, v_pool, pairs):
+    """Pools after the copy step of copy-on-write.
+
+    "Paged Attention as a Memory Manager", section "Prefix Caching and
+    Copy-on-Write": on a write to a shared block the runtime allocates a fresh
+    physical block and copies the existing content into it (refcount and table
+    updates are the block manager's, not this copy's).  Each (src, dst) pair
+    copies every KV head and row of block src to block dst in both pools, bit
+    for bit, from the state before any copy.  Destinations must be distinct and
+    no destination may also be a source.
+    """
+    k_out = np.array(k_pool, copy=True)
+    v_out = np.array(v_pool, copy=True)
+    pairs = [(int(a), int(b)) for a, b in pairs]
+    dsts = [b for _, b in pairs]
+    if len(set(dsts)) != len(dsts) or set(dsts) & {a for a, _ in pairs}:
+        raise ValueError("copy pairs need distinct destinations that are not sources")
+    for src, dst in pairs:
+        k_out[dst] = k_pool[src]
+        v_out[dst] = v_pool[src]
+    return k_out, v_out

@@ -1,0 +1,134 @@
+"""Host-side checks of the seeded workloads and the block-manager harness (no GPU)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_93_amd import workloads as W
+
+
+@pytest.fixture(scope="module")
+def configs():
+    return {k: W.make_config(k) for k in (1, 3, 4)} | {
+        2: W.make_config(2, num_seqs=8), 5: W.make_config(5, num_seqs=2, context=2048)}
+
+
+def _nan_rows(w):
+    pool = w.k_pool.view(np.uint32 if w.dtype == "f32" else np.uint16)
+    bits = W.nan_bits(w.dtype)
+    return (pool == bits).all(axis=(1, 3))  # [num_blocks][block_size]
+
+
+def test_bf16_rounding_matches_torch():
+    x = np.random.default_rng(5).standard_normal(200000).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(W.f32_to_bf16_bits(x), ref)
+
+
+def test_deterministic_from_seed():
+    a = W.make_config(1)
+    b = W.make_config(1)
+    for f in ("q", "k_pool", "v_pool", "block_tables", "context_lens", "slot_mapping", "k_new"):
+        assert np.array_equal(getattr(a, f), getattr(b, f), equal_nan=True), f
+    c = W.make_config(2, num_seqs=4)
+    d = W.make_config(2, num_seqs=4)
+    assert np.array_equal(c.k_pool, d.k_pool) and np.array_equal(c.block_tables, d.block_tables)
+
+
+def test_named_shapes(configs):
+    c1 = configs[1]
+    assert (c1.dtype, c1.num_heads, c1.num_kv_heads, c1.head_dim, c1.block_size) == ("f32", 2, 1, 64, 16)
+    assert c1.context_lens.tolist() == [5, 37] and c1.num_blocks == 8
+    full2 = W.make_config(2)
+    assert full2.num_seqs == 64 and full2.num_heads == 32 and full2.num_kv_heads == 8
+    assert full2.context_lens.min() >= 128 and full2.context_lens.max() <= 4096
+    need = sum(oracle.blocks_needed(int(n), 16) for n in full2.context_lens)
+    assert full2.num_blocks == int(np.ceil(1.25 * need))
+    assert configs[3].num_seqs == 256 and configs[3].context_lens.max() <= 4096
+    c4 = configs[4]
+    assert c4.num_heads == 64 and c4.num_seqs == 60
+    assert (c4.context_lens >= 1009).all() and (c4.context_lens <= 2008).all()
+
+
+def test_slot_mapping_agrees_with_the_oracle_slot_rule(configs):
+    """The harness's slots for the new tokens are the oracle's slot_of."""
+    for w in configs.values():
+        for i in range(w.num_seqs):
+            last = int(w.context_lens[i]) - 1
+            assert w.slot_mapping[i] == oracle.slot_of(w.block_tables[i], last, w.block_size)
+
+
+def test_poison_covers_exactly_the_unowned_rows(configs):
+    for w in configs.values():
+        nan_rows = _nan_rows(w)
+        owned = np.zeros_like(nan_rows)
+        for i in range(w.num_seqs):
+            n = int(w.context_lens[i])
+            for j in range(oracle.blocks_needed(n, w.block_size)):
+                b = int(w.block_tables[i, j])
+                owned[b, : min(w.block_size, n - j * w.block_size)] = True
+        writes = set(int(s) for s in w.slot_mapping)
+        for b in range(w.num_blocks):
+            for r in range(w.block_size):
+                written = (b * w.block_size + r) in writes or b in set(w.copy_pairs[:, 1].tolist())
+                if owned[b, r] and not written:
+                    assert not nan_rows[b, r], (w.name, b, r)
+                elif not owned[b, r]:
+                    assert nan_rows[b, r], (w.name, b, r)
+
+
+def test_refcounts_match_table_references(configs):
+    for w in configs.values():
+        refs = np.zeros(w.num_blocks, np.int64)
+        for i in range(w.num_seqs):
+            for j in range(oracle.blocks_needed(int(w.context_lens[i]), w.block_size)):
+                refs[w.block_tables[i, j]] += 1
+        assert np.array_equal(refs, w.refcount.astype(np.int64)), w.name
+
+
+def test_shared_prefix_and_copy_on_write(configs):
+    w = configs[4]
+    d = w.info["divergent_seq"]
+    src, dst = w.info["cow_src"], w.info["cow_dst"]
+    assert w.copy_pairs.tolist() == [[src, dst]]
+    shared = w.info["shared_blocks"]
+    assert len(shared) == 63
+    for b in shared[:-1]:
+        assert w.refcount[b] == 60
+    assert w.refcount[src] == 59 and w.refcount[dst] == 1
+    assert w.block_tables[d, 62] == dst
+    others = [i for i in range(60) if i != d]
+    assert all(w.block_tables[i, 62] == src for i in others)
+    # the divergent write lands in the copy at the last prefix row
+    assert w.slot_mapping[-1] == dst * 16 + 15 and len(w.slot_mapping) == 61
+    assert w.unique_kv_bytes() < w.kv_bytes()
+
+
+def test_fragmented_pool(configs):
+    w = configs[3]
+    assert w.info["preemptions"] > 0 and w.info["finished"] > 0
+    assert w.info["contiguity"] < 0.5
+    assert np.median(w.context_lens) == pytest.approx(200, rel=0.25)
+
+
+def test_block_pool_bookkeeping():
+    pool = W.BlockPool(4, order=[2, 0, 3, 1])
+    a, b = pool.alloc(), pool.alloc()
+    assert (a, b) == (2, 0)
+    pool.share(a)
+    pool.release(a)
+    assert pool.num_free() == 2
+    pool.release(a)
+    assert pool.num_free() == 3 and pool.alloc() == a  # LIFO
+    with pytest.raises(ValueError):
+        pool.release(3)
+    with pytest.raises(MemoryError):
+        for _ in range(5):
+            pool.alloc()
+
+
+def test_random_partials_poison_unused_partitions():
+    out, mx, sm = W.random_partials(3, 2, 4, 8, 5, [100, 20], 32)
+    assert np.isfinite(out[0, :, :4]).all() and np.isnan(out[0, :, 4:]).all()
+    assert np.isfinite(sm[1, :, :1]).all() and np.isnan(sm[1, :, 1:]).all()
