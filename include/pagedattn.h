@@ -1,0 +1,192 @@
+/*
+ * pagedattn.h - C ABI of libpagedattn: paged attention decode on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The KV cache is cut into fixed-size physical blocks; each sequence reaches
+ * its blocks through a block table, and attention gathers K/V through that
+ * indirection ("How Paged Attention and Continuous Batching Actually Work",
+ * section "Paged attention: virtual memory for the KV cache"; "Paged Attention
+ * as a Memory Manager", section "How the Kernel Executes Paged Attention").
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ * - Pointers marked DEVICE are HIP device pointers; HOST pointers are read
+ *   before the call returns.  The caller allocates and frees every buffer;
+ *   the library allocates nothing and keeps no state besides a per-thread
+ *   error message.
+ * - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *   enqueues work on it and returns without synchronising; results are
+ *   visible after the stream is synchronised.
+ * - Every entry point returns a pa_status.  Argument errors are found on the
+ *   host before anything is enqueued (nothing is written then); a failed
+ *   launch returns PA_ERR_LAUNCH.  pa_last_error() describes the last
+ *   non-OK status of the calling thread.
+ * - Pools: two separate buffers, K and V, each laid out
+ *   [num_blocks][num_kv_heads][block_size][head_dim] row-major, so the rows of
+ *   one (block, KV head) pair are one contiguous run.  Token slot s of the
+ *   cache is row (s / block_size, :, s % block_size, :).
+ * - Element types: PA_F32 (IEEE binary32) or PA_BF16 (bfloat16).  Decode
+ *   accumulates in binary32 and rounds a bf16 output to nearest-even.
+ * - Device-side contents are not validated beyond what keeps every access in
+ *   bounds: a block id outside [0, num_blocks) in a table or pair, or a slot
+ *   outside [0, num_blocks*block_size), is skipped (its rows take no part);
+ *   context lengths are clamped to max_blocks_per_seq*block_size.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,       /* sizes are negative, inconsistent, or misaligned */
+  PA_ERR_UNSUPPORTED = 3, /* a valid request this build has no kernel for */
+  PA_ERR_WORKSPACE = 4,   /* split-KV partial buffers missing or too small */
+  PA_ERR_LAUNCH = 5       /* the HIP runtime refused a launch */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Description of the two KV pools (a HOST struct holding DEVICE pointers). */
+typedef struct pa_cache {
+  void *k_pool;          /* DEVICE [num_blocks][num_kv_heads][block_size][head_dim] */
+  void *v_pool;          /* DEVICE, same shape and type as k_pool */
+  int64_t num_blocks;    /* physical blocks in each pool, > 0 */
+  int32_t num_kv_heads;  /* > 0 */
+  int32_t block_size;    /* tokens per block: 16 or 32 */
+  int32_t head_dim;      /* 64 or 128 */
+  int32_t dtype;         /* pa_dtype of both pools */
+} pa_cache;
+
+/* Version of this header the library was built from (PA_ABI_VERSION). */
+int32_t pa_abi_version(void);
+
+/* Runtime version reported by the HIP runtime the library is bound to
+ * (hipRuntimeGetVersion), or -1 if it cannot be queried. */
+int32_t pa_hip_runtime_version(void);
+
+/* Message for the calling thread's last non-OK status (HOST string owned by
+ * the library, valid until the thread's next failing call); "" if none. */
+const char *pa_last_error(void);
+
+/*
+ * pa_kv_append - write each new token's K and V rows into the cache.
+ *
+ * The forward pass writes the new token's K/V through the slot mapping
+ * ("How Paged Attention and Continuous Batching Actually Work", section "One
+ * step, end to end"; "LLM paged attention arch", section "The architecture:
+ * every piece explained").  For token n with s = slot_mapping[n] >= 0, every
+ * KV head h gets
+ *     K[s / B][h][s % B][:] = k_new[n][h][:],   V likewise from v_new,
+ * copied bit for bit (no conversion).  A negative slot means "no write".
+ * No other byte of either pool changes.
+ *
+ *   cache         HOST   pool description
+ *   k_new, v_new  DEVICE [num_tokens][num_kv_heads][head_dim], cache->dtype
+ *   slot_mapping  DEVICE int64 [num_tokens]; live slots must be distinct
+ *   num_tokens    >= 0 (0 enqueues nothing)
+ * Requires head_dim * element size to be a multiple of 16 bytes and every
+ * pointer 16-byte aligned.
+ */
+int pa_kv_append(const pa_cache *cache, const void *k_new, const void *v_new,
+                 const int64_t *slot_mapping, int32_t num_tokens, void *stream);
+
+/*
+ * pa_copy_blocks - the copy step of copy-on-write.
+ *
+ * When a sequence writes into a block it shares, the runtime takes a fresh
+ * block and copies the shared content into it ("Paged Attention as a Memory
+ * Manager", section "Prefix Caching and Copy-on-Write").  For each pair
+ * (src, dst) = (block_pairs[2p], block_pairs[2p+1]) every KV head and row of
+ * block src is copied to block dst, in both pools, bit for bit.  Reference
+ * counts and table updates belong to the caller's block manager.
+ *
+ *   block_pairs  DEVICE int64 [num_pairs][2]; destinations distinct and never
+ *                also a source (the copies then do not depend on order)
+ *   num_pairs    >= 0
+ */
+int pa_copy_blocks(const pa_cache *cache, const int64_t *block_pairs, int32_t num_pairs,
+                   void *stream);
+
+/*
+ * pa_decode - attention of one query token per sequence over its paged cache.
+ *
+ * For sequence i, query head h and its KV head g = h / (num_heads/num_kv_heads):
+ *     s_t = scale * q[i][h] . K_t      for t < L_i = context_lens[i]
+ *     out[i][h] = sum_t softmax(s)_t * V_t
+ * with K_t, V_t the rows of logical token t, found through block_tables[i]
+ * ("Paged Attention as a Memory Manager", section "How the Kernel Executes
+ * Paged Attention": one table read per block, keys loaded per block, scores
+ * q.k/sqrt(d_k), padding masked, softmax-weighted value sum; "PagedAttention
+ * and continuous batching", section "Attention kernel modification": blocks
+ * accumulated with a running softmax).  L_i includes the token appended this
+ * step.  Rows at positions >= L_i never affect the result, whatever they hold.
+ *
+ *   q             DEVICE [num_seqs][num_heads][head_dim], cache->dtype
+ *   block_tables  DEVICE int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                 ceil(L_i / block_size) are not read
+ *   context_lens  DEVICE int32 [num_seqs], 0 <= L_i <= max_blocks_per_seq*block_size
+ *   num_heads     multiple of num_kv_heads; ratio 1, 2, 4 or 8
+ *   scale         > 0 and finite (normally 1/sqrt(head_dim))
+ *   partition_size
+ *     0   single pass: writes out[i][h][:] (L_i = 0 gives zeros);
+ *     > 0 split-KV: a multiple of block_size; partition p of sequence i covers
+ *         positions [p*P, min((p+1)*P, L_i)) and, for p < ceil(L_i/P), writes
+ *           part_out[i][h][p][:] = that partition's softmax-weighted V sum,
+ *           part_max[i][h][p]    = its largest score s_t,
+ *           part_sum[i][h][p]    = sum over it of exp(s_t - part_max),
+ *         leaving `out` untouched; pa_splitkv_reduce then merges them.
+ *         Requires L_i <= max_parts * P; later partitions are not computed.
+ *   out           DEVICE [num_seqs][num_heads][head_dim] of out_dtype
+ *                 (single pass only; may be NULL when partition_size > 0)
+ *   out_dtype     PA_F32, or cache->dtype
+ *   part_out      DEVICE float [num_seqs][num_heads][max_parts][head_dim]
+ *   part_max, part_sum  DEVICE float [num_seqs][num_heads][max_parts]
+ *                 (split-KV only; may be NULL when partition_size == 0)
+ */
+int pa_decode(const pa_cache *cache, const void *q, const int32_t *block_tables,
+              const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+              int32_t max_blocks_per_seq, float scale, int32_t partition_size, void *out,
+              int32_t out_dtype, float *part_out, float *part_max, float *part_sum,
+              int32_t max_parts, void *stream);
+
+/*
+ * pa_splitkv_reduce - merge split-KV partials with their log-sum-exp weights.
+ *
+ * Not described on the pages, which run one softmax over the whole context;
+ * this is the exact regrouping of that softmax over partitions.  For each
+ * (i, h), over the ceil(L_i / partition_size) partitions of sequence i:
+ *     M   = max_p part_max[p];   w_p = part_sum[p] * exp(part_max[p] - M)
+ *     out = sum_p w_p * part_out[p] / sum_p w_p
+ *     lse = M + ln(sum_p w_p)
+ * Partitions past a sequence's last are not read.  L_i = 0 gives out = 0 and
+ * lse = -inf.
+ *
+ *   part_out, part_max, part_sum  DEVICE, as written by pa_decode
+ *   context_lens  DEVICE int32 [num_seqs], the same lengths pa_decode saw
+ *   out           DEVICE [num_seqs][num_heads][head_dim] of out_dtype
+ *   lse           DEVICE float [num_seqs][num_heads], or NULL
+ */
+int pa_splitkv_reduce(const float *part_out, const float *part_max, const float *part_sum,
+                      const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+                      int32_t head_dim, int32_t max_parts, int32_t partition_size, void *out,
+                      int32_t out_dtype, float *lse, void *stream);
+
+/* Bytes of part_out + part_max + part_sum for the given sizes (0 on overflow
+ * or a negative size). */
+size_t pa_partials_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                         int32_t max_parts);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

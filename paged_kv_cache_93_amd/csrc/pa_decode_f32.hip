@@ -1,0 +1,8 @@
+// binary32-cache instantiations of the decode kernel.
+#include "pa_decode_kernel.h"
+
+namespace pa {
+bool launch_decode_f32(int d, int bs, int g, const DecodeArgs& a, dim3 grid, hipStream_t s) {
+  return launch_decode_impl<false>(d, bs, g, a, grid, s);
+}
+}  // namespace pa

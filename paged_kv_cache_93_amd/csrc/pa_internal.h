@@ -1,0 +1,27 @@
+// Host-side helpers shared by the libpagedattn entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pagedattn.h"
+
+#define PA_API extern "C" __attribute__((visibility("default")))
+
+namespace pa {
+
+// Records a formatted message for pa_last_error() and returns `status`.
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// Checks hipGetLastError() after a launch; PA_OK or PA_ERR_LAUNCH.
+int launch_result(const char* what);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int element_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_BF16 ? 2 : 0); }
+
+// Validates the pool description shared by every cache entry point.
+int check_cache(const pa_cache* cache, const char* fn);
+
+}  // namespace pa

@@ -1,0 +1,136 @@
+// KV writes of a decode step: the new-token append through the slot mapping
+// and the block copy of copy-on-write.  Both are pure 16-byte data movement:
+// every thread moves one 16-byte chunk, consecutive threads move consecutive
+// chunks of a row, so each wave reads and writes whole contiguous runs.
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int64_t kMaxGrid = 65536;
+
+struct AppendArgs {
+  uint8_t* k_pool;
+  uint8_t* v_pool;
+  const uint8_t* k_new;
+  const uint8_t* v_new;
+  const int64_t* slots;
+  int64_t num_slots;        // num_blocks * block_size
+  int64_t total_chunks;     // num_tokens * 2 * heads * chunks_per_row
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t chunks_per_row;   // head_dim * element bytes / 16
+};
+
+// "How Paged Attention and Continuous Batching Actually Work", section "One
+// step, end to end": the forward pass writes the new token's K/V through the
+// slot mapping.  Slot s is row (s / B, :, s % B, :) of each pool.
+__global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x; idx < a.total_chunks;
+       idx += stride) {
+    const int64_t chunk = idx % a.chunks_per_row;
+    int64_t rest = idx / a.chunks_per_row;
+    const int64_t head = rest % a.num_kv_heads;
+    rest /= a.num_kv_heads;
+    const bool is_v = rest & 1;
+    const int64_t token = rest >> 1;
+    const int64_t slot = a.slots[token];
+    if (slot < 0 || slot >= a.num_slots) continue;
+    const int64_t block = slot / a.block_size;
+    const int64_t row = slot - block * a.block_size;
+    const int64_t src_chunk = (token * a.num_kv_heads + head) * a.chunks_per_row + chunk;
+    const int64_t dst_chunk =
+        ((block * a.num_kv_heads + head) * a.block_size + row) * a.chunks_per_row + chunk;
+    const uint4* src = reinterpret_cast<const uint4*>(is_v ? a.v_new : a.k_new) + src_chunk;
+    uint4* dst = reinterpret_cast<uint4*>(is_v ? a.v_pool : a.k_pool) + dst_chunk;
+    *dst = *src;
+  }
+}
+
+struct CopyArgs {
+  uint8_t* k_pool;
+  uint8_t* v_pool;
+  const int64_t* pairs;
+  int64_t num_blocks;
+  int64_t chunks_per_block;  // heads * block_size * head_dim * element bytes / 16
+  int64_t total_chunks;      // num_pairs * 2 * chunks_per_block
+};
+
+// "Paged Attention as a Memory Manager", section "Prefix Caching and
+// Copy-on-Write": the fresh block receives a copy of the shared block's content.
+__global__ void __launch_bounds__(kThreads) copy_kernel(CopyArgs a) {
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x; idx < a.total_chunks;
+       idx += stride) {
+    const int64_t chunk = idx % a.chunks_per_block;
+    const int64_t rest = idx / a.chunks_per_block;
+    const bool is_v = rest & 1;
+    const int64_t pair = rest >> 1;
+    const int64_t src = a.pairs[2 * pair];
+    const int64_t dst = a.pairs[2 * pair + 1];
+    if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) continue;
+    uint4* pool = reinterpret_cast<uint4*>(is_v ? a.v_pool : a.k_pool);
+    pool[dst * a.chunks_per_block + chunk] = pool[src * a.chunks_per_block + chunk];
+  }
+}
+
+unsigned grid_for(int64_t total) {
+  int64_t blocks = (total + kThreads - 1) / kThreads;
+  if (blocks > kMaxGrid) blocks = kMaxGrid;
+  return unsigned(blocks < 1 ? 1 : blocks);
+}
+
+}  // namespace
+}  // namespace pa
+
+PA_API int pa_kv_append(const pa_cache* cache, const void* k_new, const void* v_new,
+                        const int64_t* slot_mapping, int32_t num_tokens, void* stream) {
+  using namespace pa;
+  if (int st = check_cache(cache, "pa_kv_append")) return st;
+  if (num_tokens < 0) return fail(PA_ERR_SHAPE, "pa_kv_append: num_tokens < 0");
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping)
+    return fail(PA_ERR_NULL, "pa_kv_append: k_new, v_new or slot_mapping is NULL");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(PA_ERR_SHAPE, "pa_kv_append: k_new/v_new must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(slot_mapping) & 7u) != 0)
+    return fail(PA_ERR_SHAPE, "pa_kv_append: slot_mapping must be 8-byte aligned");
+  AppendArgs a;
+  a.k_pool = static_cast<uint8_t*>(cache->k_pool);
+  a.v_pool = static_cast<uint8_t*>(cache->v_pool);
+  a.k_new = static_cast<const uint8_t*>(k_new);
+  a.v_new = static_cast<const uint8_t*>(v_new);
+  a.slots = slot_mapping;
+  a.num_slots = cache->num_blocks * cache->block_size;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.block_size = cache->block_size;
+  a.chunks_per_row = cache->head_dim * element_bytes(cache->dtype) / 16;
+  a.total_chunks = int64_t(num_tokens) * 2 * cache->num_kv_heads * a.chunks_per_row;
+  hipLaunchKernelGGL(append_kernel, dim3(grid_for(a.total_chunks)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return launch_result("pa_kv_append");
+}
+
+PA_API int pa_copy_blocks(const pa_cache* cache, const int64_t* block_pairs, int32_t num_pairs,
+                          void* stream) {
+  using namespace pa;
+  if (int st = check_cache(cache, "pa_copy_blocks")) return st;
+  if (num_pairs < 0) return fail(PA_ERR_SHAPE, "pa_copy_blocks: num_pairs < 0");
+  if (num_pairs == 0) return PA_OK;
+  if (!block_pairs) return fail(PA_ERR_NULL, "pa_copy_blocks: block_pairs is NULL");
+  if ((reinterpret_cast<uintptr_t>(block_pairs) & 7u) != 0)
+    return fail(PA_ERR_SHAPE, "pa_copy_blocks: block_pairs must be 8-byte aligned");
+  CopyArgs a;
+  a.k_pool = static_cast<uint8_t*>(cache->k_pool);
+  a.v_pool = static_cast<uint8_t*>(cache->v_pool);
+  a.pairs = block_pairs;
+  a.num_blocks = cache->num_blocks;
+  a.chunks_per_block = int64_t(cache->num_kv_heads) * cache->block_size * cache->head_dim *
+                       element_bytes(cache->dtype) / 16;
+  a.total_chunks = int64_t(num_pairs) * 2 * a.chunks_per_block;
+  hipLaunchKernelGGL(copy_kernel, dim3(grid_for(a.total_chunks)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return launch_result("pa_copy_blocks");
+}

@@ -1,0 +1,111 @@
+"""Helpers shared by the GPU parity tests: upload a workload, run one decode
+step through the C ABI, and build the oracle's expected results."""
+
+from __future__ import annotations
+
+import functools
+import math
+
+import numpy as np
+import torch
+
+import oracle
+from paged_kv_cache_93_amd import lib
+from paged_kv_cache_93_amd import workloads as W
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def torch_dtype(dtype: str):
+    return torch.float32 if dtype == "f32" else torch.bfloat16
+
+
+def to_device(arr: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def to_host_bits(t: torch.Tensor) -> np.ndarray:
+    """Raw element bits of a device tensor (uint16 for bf16, uint32 for f32)."""
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.view(torch.int32).numpy().view(np.uint32)
+
+
+def bits(arr: np.ndarray, dtype: str) -> np.ndarray:
+    return arr.view(np.uint16) if dtype == "bf16" else arr.view(np.uint32)
+
+
+def upload(w: W.Workload) -> dict:
+    return dict(
+        k_pool=to_device(w.k_pool, w.dtype), v_pool=to_device(w.v_pool, w.dtype),
+        q=to_device(w.q, w.dtype), k_new=to_device(w.k_new, w.dtype),
+        v_new=to_device(w.v_new, w.dtype),
+        block_tables=torch.from_numpy(w.block_tables).cuda(),
+        context_lens=torch.from_numpy(w.context_lens).cuda(),
+        slot_mapping=torch.from_numpy(w.slot_mapping).cuda(),
+        copy_pairs=torch.from_numpy(w.copy_pairs).cuda())
+
+
+def max_parts_for(w: W.Workload, partition_size: int) -> int:
+    return max(1, max(math.ceil(int(n) / partition_size) for n in w.context_lens))
+
+
+def run_writes(t: dict) -> None:
+    if t["copy_pairs"].numel():
+        lib.pa_copy_blocks(t["k_pool"], t["v_pool"], t["copy_pairs"])
+    lib.pa_kv_append(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"], t["slot_mapping"])
+
+
+def run_decode(t: dict, w: W.Workload, partition_size: int = 0, out_f32: bool = False,
+               lse: bool = False):
+    """pa_decode (+ pa_splitkv_reduce); returns (out, lse or None) on the device."""
+    scale = 1.0 / math.sqrt(w.head_dim)
+    out_dt = torch.float32 if (out_f32 or w.dtype == "f32") else torch.bfloat16
+    out = torch.empty((w.num_seqs, w.num_heads, w.head_dim), dtype=out_dt, device="cuda")
+    lse_t = None
+    if partition_size == 0:
+        lib.pa_decode(t["k_pool"], t["v_pool"], t["q"], t["block_tables"], t["context_lens"],
+                      scale, out=out)
+    else:
+        mp = max_parts_for(w, partition_size)
+        po = torch.empty((w.num_seqs, w.num_heads, mp, w.head_dim), dtype=torch.float32,
+                         device="cuda")
+        pm = torch.empty((w.num_seqs, w.num_heads, mp), dtype=torch.float32, device="cuda")
+        ps = torch.empty_like(pm)
+        lib.pa_decode(t["k_pool"], t["v_pool"], t["q"], t["block_tables"], t["context_lens"],
+                      scale, partition_size=partition_size, part_out=po, part_max=pm,
+                      part_sum=ps)
+        if lse:
+            lse_t = torch.empty((w.num_seqs, w.num_heads), dtype=torch.float32, device="cuda")
+        lib.pa_splitkv_reduce(po, pm, ps, t["context_lens"], partition_size, out, lse=lse_t)
+    return out, lse_t
+
+
+def oracle_pools(w: W.Workload):
+    kp, vp = oracle.copy_blocks(w.k_pool, w.v_pool, w.copy_pairs)
+    return oracle.kv_append(kp, vp, w.k_new, w.v_new, w.slot_mapping)
+
+
+def oracle_out(w: W.Workload, pools=None):
+    kp, vp = oracle_pools(w) if pools is None else pools
+    return oracle.decode(w.q, kp, vp, w.block_tables, w.context_lens, 1.0 / math.sqrt(w.head_dim),
+                         w.dtype)
+
+
+@functools.lru_cache(maxsize=16)
+def named(k: int, dtype: str | None = None, block_size: int | None = None,
+          num_seqs: int | None = None):
+    """Named workload with its oracle pools and output (cached across tests)."""
+    w = W.make_config(k, dtype=dtype, block_size=block_size, num_seqs=num_seqs)
+    pools = oracle_pools(w)
+    return w, pools, oracle_out(w, pools)
+
+
+def max_abs_err(out: torch.Tensor, ref: np.ndarray) -> float:
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert got.shape == ref.shape
+    assert np.isfinite(got).all(), "non-finite output"
+    return float(np.abs(got - ref).max())

@@ -1,0 +1,134 @@
+"""The C ABI of libpagedattn without a GPU: the library loads, exports every
+symbol the header declares, and rejects bad arguments on the host before any
+HIP call (these calls never reach a kernel)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from paged_kv_cache_93_amd import lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(lib.LIB_PATH),
+                                reason="libpagedattn.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", lib.LIB_PATH], stdout=subprocess.PIPE,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in declared_functions():
+        assert name in exported, name
+    # nothing else leaks out under the pa_ prefix
+    assert {n for n in exported if n.startswith("pa_")} == set(declared_functions())
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define PA_ABI_VERSION (\d+)", open(HEADER).read())
+    assert lib.abi_version() == int(m.group(1))
+
+
+def test_partials_bytes():
+    assert lib.partials_bytes(8, 32, 128, 64) == 8 * 32 * 64 * 130 * 4
+    assert lib.partials_bytes(-1, 32, 128, 64) == 0
+
+
+def _cache(**kw):
+    c = dict(k_pool=16, v_pool=32, num_blocks=4, num_kv_heads=2, block_size=16, head_dim=128,
+             dtype=lib.PA_BF16)
+    c.update(kw)
+    return lib.PaCache(c["k_pool"], c["v_pool"], c["num_blocks"], c["num_kv_heads"],
+                       c["block_size"], c["head_dim"], c["dtype"])
+
+
+def _decode(cache, **kw):
+    a = dict(q=16, tables=16, lens=16, num_seqs=1, num_heads=4, max_blocks=4, scale=0.1,
+             partition=0, out=16, out_dtype=lib.PA_BF16, po=16, pm=16, ps=16, max_parts=1)
+    a.update(kw)
+    return lib.raw_call("pa_decode", ctypes.byref(cache) if cache is not None else None,
+                        a["q"], a["tables"], a["lens"], a["num_seqs"], a["num_heads"],
+                        a["max_blocks"], a["scale"], a["partition"], a["out"], a["out_dtype"],
+                        a["po"], a["pm"], a["ps"], a["max_parts"], None)
+
+
+@pytest.mark.parametrize("cache_kw,call_kw,status", [
+    (None, {}, 1),
+    (dict(k_pool=0), {}, 1),
+    (dict(dtype=7), {}, 3),
+    (dict(num_blocks=0), {}, 2),
+    (dict(head_dim=96), {}, 3),
+    (dict(block_size=8), {}, 3),
+    (dict(k_pool=8), {}, 2),                       # misaligned pool
+    ({}, dict(num_heads=3), 2),                    # not a multiple of num_kv_heads
+    ({}, dict(num_heads=32), 3),                   # 16 query heads per KV head
+    ({}, dict(scale=0.0), 2),
+    ({}, dict(scale=float("inf")), 2),
+    ({}, dict(num_seqs=-1), 2),
+    ({}, dict(max_blocks=0), 2),
+    ({}, dict(out=0), 1),
+    ({}, dict(out_dtype=9), 3),
+    ({}, dict(q=0), 1),
+    ({}, dict(q=8), 2),                            # misaligned q
+    ({}, dict(partition=24), 2),                   # not a multiple of the block size
+    ({}, dict(partition=32, max_parts=0), 4),
+    ({}, dict(partition=32, po=0), 4),
+    ({}, dict(partition=-16), 2),
+])
+def test_decode_rejects_bad_arguments(cache_kw, call_kw, status):
+    cache = None if cache_kw is None else _cache(**cache_kw)
+    assert _decode(cache, **call_kw) == status
+    assert lib.load().pa_last_error().decode().startswith("pa_decode:")
+
+
+def test_zero_sequences_is_a_no_op():
+    assert _decode(_cache(), num_seqs=0, q=0, tables=0, lens=0) == 0
+
+
+def test_append_and_copy_reject_bad_arguments():
+    c = _cache()
+    call = lib.raw_call
+    assert call("pa_kv_append", None, 16, 16, 16, 1, None) == 1
+    assert call("pa_kv_append", ctypes.byref(c), 16, 16, 16, -1, None) == 2
+    assert call("pa_kv_append", ctypes.byref(c), 16, 16, 16, 0, None) == 0
+    assert call("pa_kv_append", ctypes.byref(c), 0, 16, 16, 1, None) == 1
+    assert call("pa_kv_append", ctypes.byref(c), 8, 16, 16, 1, None) == 2
+    assert call("pa_kv_append", ctypes.byref(c), 16, 16, 12, 1, None) == 2
+    odd = _cache(head_dim=4, dtype=lib.PA_BF16)  # 8-byte rows cannot move in 16-byte chunks
+    assert call("pa_kv_append", ctypes.byref(odd), 16, 16, 16, 1, None) == 3
+    assert call("pa_copy_blocks", ctypes.byref(c), None, 1, None) == 1
+    assert call("pa_copy_blocks", ctypes.byref(c), 16, -2, None) == 2
+    assert call("pa_copy_blocks", ctypes.byref(c), 16, 0, None) == 0
+    assert call("pa_copy_blocks", ctypes.byref(_cache(num_kv_heads=0)), 16, 1, None) == 2
+
+
+def test_reduce_rejects_bad_arguments():
+    call = lib.raw_call
+    ok = dict(po=16, pm=16, ps=16, lens=16, S=1, H=4, D=128, P=2, psize=16, out=16, od=lib.PA_F32)
+
+    def r(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return call("pa_splitkv_reduce", a["po"], a["pm"], a["ps"], a["lens"], a["S"], a["H"],
+                    a["D"], a["P"], a["psize"], a["out"], a["od"], None, None)
+    assert r(D=96) == 3
+    assert r(P=0) == 2
+    assert r(psize=0) == 2
+    assert r(od=5) == 3
+    assert r(po=0) == 4
+    assert r(out=0) == 1
+    assert r(S=0) == 0
