@@ -37,7 +37,6 @@ from paged_kv_cache_93_amd import lib  # noqa: E402
 from paged_kv_cache_93_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
-DEFAULT_PARTITION = {1: 16, 2: 256, 3: 256, 4: 256, 5: 512}
 
 
 def to_device(arr, dtype):
@@ -96,8 +95,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--block-size", type=int, default=None)
-    ap.add_argument("--partition", type=int, default=None,
-                    help="split-KV partition size in tokens (0 = single pass)")
+    ap.add_argument("--mode", default="balanced",
+                    help="balanced | single | <partition size in tokens> (split-KV + merge)")
     ap.add_argument("--rotate", type=int, default=3, help="independent copies of the KV pools")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for cpu_baseline (0 = skip)")
@@ -113,11 +112,11 @@ def main() -> int:
     lib.load()
 
     w = W.make_config(args.workload, block_size=args.block_size)
-    psize = DEFAULT_PARTITION[args.workload] if args.partition is None else args.partition
+    mode = args.mode if args.mode in ("balanced", "single") else int(args.mode)
     scale = 1.0 / math.sqrt(w.head_dim)
     nbytes = algorithmic_bytes(w)
     print(f"# workload {w.name}: {w.num_seqs} seqs, KV {nbytes['kv'] / 1e6:.1f} MB, "
-          f"pool {w.num_blocks} blocks, partition {psize}", file=sys.stderr, flush=True)
+          f"pool {w.num_blocks} blocks, mode {mode}", file=sys.stderr, flush=True)
 
     shared = dict(q=to_device(w.q, w.dtype),
                   tables=torch.from_numpy(w.block_tables).cuda(),
@@ -130,10 +129,15 @@ def main() -> int:
     for r in range(args.rotate):
         pools.append((k0, v0) if r == 0 else (k0.clone(), v0.clone()))
     out = torch.empty((w.num_seqs, w.num_heads, w.head_dim), dtype=k0.dtype, device="cuda")
+    psize = mode if isinstance(mode, int) else 0
     mp = max(1, max(math.ceil(int(n) / psize) for n in w.context_lens)) if psize else 1
     po = torch.empty((w.num_seqs, w.num_heads, mp, w.head_dim), device="cuda")
     pm = torch.empty((w.num_seqs, w.num_heads, mp), device="cuda")
     ps = torch.empty_like(pm)
+    ws = None
+    if mode == "balanced":
+        ws = torch.empty(lib.decode_workspace_bytes(w.num_seqs, w.num_heads, w.head_dim),
+                         dtype=torch.uint8, device="cuda")
 
     def step(r, ev=None):
         kp, vp = pools[r]
@@ -143,13 +147,14 @@ def main() -> int:
         if ev is not None:
             ev[0].record()
         if psize:
-            lib.pa_decode(kp, vp, shared["q"], shared["tables"], shared["lens"], scale,
-                          partition_size=psize, part_out=po, part_max=pm, part_sum=ps)
+            lib.pa_decode_partitions(kp, vp, shared["q"], shared["tables"], shared["lens"],
+                                     scale, psize, po, pm, ps)
             if ev is not None:
                 ev[1].record()
             lib.pa_splitkv_reduce(po, pm, ps, shared["lens"], psize, out)
         else:
-            lib.pa_decode(kp, vp, shared["q"], shared["tables"], shared["lens"], scale, out=out)
+            lib.pa_decode(kp, vp, shared["q"], shared["tables"], shared["lens"], scale, out,
+                          workspace=ws)
             if ev is not None:
                 ev[1].record()
 
@@ -188,7 +193,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
-                   "block_size": w.block_size, "partition_size": psize,
+                   "block_size": w.block_size, "decode_mode": str(mode),
                    "context_lens": f"{int(w.context_lens.min())}..{int(w.context_lens.max())}, "
                                    f"mean {float(w.context_lens.mean()):.0f}",
                    "seed": w.seed, "rotating_caches": args.rotate},

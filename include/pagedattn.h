@@ -42,14 +42,14 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_NULL = 1,        /* a required pointer is NULL */
   PA_ERR_SHAPE = 2,       /* sizes are negative, inconsistent, or misaligned */
   PA_ERR_UNSUPPORTED = 3, /* a valid request this build has no kernel for */
-  PA_ERR_WORKSPACE = 4,   /* split-KV partial buffers missing or too small */
+  PA_ERR_WORKSPACE = 4,   /* workspace or split-KV partial buffers missing or too small */
   PA_ERR_LAUNCH = 5       /* the HIP runtime refused a launch */
 } pa_status;
 
@@ -128,7 +128,14 @@ int pa_copy_blocks(const pa_cache *cache, const int64_t *block_pairs, int32_t nu
  * q.k/sqrt(d_k), padding masked, softmax-weighted value sum; "PagedAttention
  * and continuous batching", section "Attention kernel modification": blocks
  * accumulated with a running softmax).  L_i includes the token appended this
- * step.  Rows at positions >= L_i never affect the result, whatever they hold.
+ * step.  Rows at positions >= L_i never affect the result, whatever they hold;
+ * L_i = 0 gives a zero output.
+ *
+ * With a workspace, the (sequence, block) pairs of the whole batch are split
+ * evenly over a fixed grid of workgroups, so long and short sequences finish
+ * together; a sequence split between workgroups is merged with the
+ * log-sum-exp rule by a second kernel enqueued on the same stream.  Without
+ * one (workspace = NULL), one workgroup walks each sequence.
  *
  *   q             DEVICE [num_seqs][num_heads][head_dim], cache->dtype
  *   block_tables  DEVICE int32 [num_seqs][max_blocks_per_seq]; entries past
@@ -136,27 +143,44 @@ int pa_copy_blocks(const pa_cache *cache, const int64_t *block_pairs, int32_t nu
  *   context_lens  DEVICE int32 [num_seqs], 0 <= L_i <= max_blocks_per_seq*block_size
  *   num_heads     multiple of num_kv_heads; ratio 1, 2, 4 or 8
  *   scale         > 0 and finite (normally 1/sqrt(head_dim))
- *   partition_size
- *     0   single pass: writes out[i][h][:] (L_i = 0 gives zeros);
- *     > 0 split-KV: a multiple of block_size; partition p of sequence i covers
- *         positions [p*P, min((p+1)*P, L_i)) and, for p < ceil(L_i/P), writes
- *           part_out[i][h][p][:] = that partition's softmax-weighted V sum,
- *           part_max[i][h][p]    = its largest score s_t,
- *           part_sum[i][h][p]    = sum over it of exp(s_t - part_max),
- *         leaving `out` untouched; pa_splitkv_reduce then merges them.
- *         Requires L_i <= max_parts * P; later partitions are not computed.
- *   out           DEVICE [num_seqs][num_heads][head_dim] of out_dtype
- *                 (single pass only; may be NULL when partition_size > 0)
+ *   out           DEVICE [num_seqs][num_heads][head_dim] of out_dtype, 16-byte aligned
  *   out_dtype     PA_F32, or cache->dtype
- *   part_out      DEVICE float [num_seqs][num_heads][max_parts][head_dim]
- *   part_max, part_sum  DEVICE float [num_seqs][num_heads][max_parts]
- *                 (split-KV only; may be NULL when partition_size == 0)
+ *   workspace     DEVICE scratch of workspace_bytes >= pa_decode_workspace_bytes(),
+ *                 256-byte aligned, or NULL; its contents need no initialising
+ *                 and are meaningless afterwards.  Two calls in flight at once
+ *                 must not share one.
  */
 int pa_decode(const pa_cache *cache, const void *q, const int32_t *block_tables,
               const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
-              int32_t max_blocks_per_seq, float scale, int32_t partition_size, void *out,
-              int32_t out_dtype, float *part_out, float *part_max, float *part_sum,
-              int32_t max_parts, void *stream);
+              int32_t max_blocks_per_seq, float scale, void *out, int32_t out_dtype,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes pa_decode needs on the current device for these sizes
+ * (0 for a negative or zero size). */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim);
+
+/*
+ * pa_decode_partitions - split-KV decode: per-partition partial results.
+ *
+ * Same attention as pa_decode, cut along each sequence's context into
+ * partitions of partition_size tokens (a multiple of block_size): partition p
+ * of sequence i covers positions [p*P, min((p+1)*P, L_i)).  For p < ceil(L_i/P)
+ * it writes, for every query head h,
+ *     part_out[i][h][p][:] = the partition's softmax-weighted V sum,
+ *     part_max[i][h][p]    = its largest score s_t (natural units),
+ *     part_sum[i][h][p]    = sum over it of exp(s_t - part_max),
+ * and nothing else; pa_splitkv_reduce merges them.  Requires
+ * L_i <= max_parts * P; later partitions are not computed.
+ *
+ *   part_out      DEVICE float [num_seqs][num_heads][max_parts][head_dim], 16-byte aligned
+ *   part_max, part_sum  DEVICE float [num_seqs][num_heads][max_parts]
+ *   max_parts     in [1, 65535]
+ */
+int pa_decode_partitions(const pa_cache *cache, const void *q, const int32_t *block_tables,
+                         const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+                         int32_t max_blocks_per_seq, float scale, int32_t partition_size,
+                         float *part_out, float *part_max, float *part_sum, int32_t max_parts,
+                         void *stream);
 
 /*
  * pa_splitkv_reduce - merge split-KV partials with their log-sum-exp weights.
@@ -170,8 +194,8 @@ int pa_decode(const pa_cache *cache, const void *q, const int32_t *block_tables,
  * Partitions past a sequence's last are not read.  L_i = 0 gives out = 0 and
  * lse = -inf.
  *
- *   part_out, part_max, part_sum  DEVICE, as written by pa_decode
- *   context_lens  DEVICE int32 [num_seqs], the same lengths pa_decode saw
+ *   part_out, part_max, part_sum  DEVICE, as written by pa_decode_partitions
+ *   context_lens  DEVICE int32 [num_seqs], the same lengths pa_decode_partitions saw
  *   out           DEVICE [num_seqs][num_heads][head_dim] of out_dtype
  *   lse           DEVICE float [num_seqs][num_heads], or NULL
  */

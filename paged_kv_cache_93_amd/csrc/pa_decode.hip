@@ -1,16 +1,65 @@
-// pa_decode: host-side validation and dispatch of the decode kernel.
+// pa_decode, pa_decode_partitions, pa_decode_workspace_bytes: host-side
+// validation, work decomposition and launch of the decode kernels.
 #include <cmath>
 
 #include "pa_decode_kernel.h"
 #include "pa_internal.h"
 
-PA_API int pa_decode(const pa_cache* cache, const void* q, const int32_t* block_tables,
-                     const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
-                     int32_t max_blocks_per_seq, float scale, int32_t partition_size, void* out,
-                     int32_t out_dtype, float* part_out, float* part_max, float* part_sum,
-                     int32_t max_parts, void* stream) {
-  using namespace pa;
-  const char* fn = "pa_decode";
+namespace pa {
+namespace {
+
+// Largest workgroup (in waves, at most 8) made of whole KV heads.
+int waves_per_group(int num_kv_heads) {
+  for (int w : {8, 4, 2, 1})
+    if (num_kv_heads % w == 0) return w;
+  return 1;
+}
+
+// Workgroups of the balanced split for the current device: four per CU at most.
+int balanced_groups_max() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  return cus * 4;
+}
+
+// Workgroups the balanced split actually uses: one per CU and resident slot.
+int balanced_groups(int waves_per_wg) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  // 8 waves per CU keep two waves per SIMD; smaller workgroups share a CU.
+  int per_cu = 8 / waves_per_wg;
+  if (per_cu > 4) per_cu = 4;
+  return cus * per_cu;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct WorkspaceLayout {
+  size_t info, piece_out, piece_max, piece_sum, total;
+};
+
+WorkspaceLayout layout_for(int64_t groups, int64_t num_seqs, int64_t num_heads, int64_t head_dim) {
+  WorkspaceLayout w;
+  const int64_t rows = (groups + num_seqs) * num_heads;
+  w.info = 0;
+  w.piece_out = align_up(size_t(num_seqs + 2) * sizeof(int32_t));
+  w.piece_max = w.piece_out + align_up(size_t(rows) * head_dim * sizeof(float));
+  w.piece_sum = w.piece_max + align_up(size_t(rows) * sizeof(float));
+  w.total = w.piece_sum + align_up(size_t(rows) * sizeof(float));
+  return w;
+}
+
+// Checks shared by pa_decode and pa_decode_partitions; fills the common args.
+int prepare(const char* fn, const pa_cache* cache, const void* q, const int32_t* block_tables,
+            const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+            int32_t max_blocks_per_seq, float scale, DecodeArgs* a, int* group) {
   if (int st = check_cache(cache, fn)) return st;
   if (num_seqs < 0 || num_heads <= 0 || max_blocks_per_seq <= 0)
     return fail(PA_ERR_SHAPE, "%s: need num_seqs >= 0, num_heads > 0, max_blocks_per_seq > 0",
@@ -18,10 +67,10 @@ PA_API int pa_decode(const pa_cache* cache, const void* q, const int32_t* block_
   if (num_heads % cache->num_kv_heads != 0)
     return fail(PA_ERR_SHAPE, "%s: num_heads (%d) is not a multiple of num_kv_heads (%d)", fn,
                 num_heads, cache->num_kv_heads);
-  const int group = num_heads / cache->num_kv_heads;
-  if (group != 1 && group != 2 && group != 4 && group != 8)
+  *group = num_heads / cache->num_kv_heads;
+  if (*group != 1 && *group != 2 && *group != 4 && *group != 8)
     return fail(PA_ERR_UNSUPPORTED, "%s: query heads per KV head must be 1, 2, 4 or 8 (got %d)",
-                fn, group);
+                fn, *group);
   if (cache->head_dim != 64 && cache->head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "%s: head_dim must be 64 or 128 (got %d)", fn,
                 cache->head_dim);
@@ -34,51 +83,135 @@ PA_API int pa_decode(const pa_cache* cache, const void* q, const int32_t* block_
     return fail(PA_ERR_UNSUPPORTED, "%s: at most 65535 sequences and KV heads", fn);
   if (int64_t(max_blocks_per_seq) * cache->block_size > INT32_MAX)
     return fail(PA_ERR_SHAPE, "%s: max_blocks_per_seq too large", fn);
-  const bool bf16 = cache->dtype == PA_BF16;
-  const bool split = partition_size > 0;
-  if (partition_size < 0) return fail(PA_ERR_SHAPE, "%s: partition_size < 0", fn);
-  if (split) {
-    if (partition_size % cache->block_size != 0)
-      return fail(PA_ERR_SHAPE, "%s: partition_size must be a multiple of block_size", fn);
-    if (max_parts <= 0) return fail(PA_ERR_WORKSPACE, "%s: max_parts must be positive", fn);
-    if (!part_out || !part_max || !part_sum)
-      return fail(PA_ERR_WORKSPACE, "%s: split-KV needs part_out, part_max and part_sum", fn);
-    if (!aligned16(part_out))
-      return fail(PA_ERR_SHAPE, "%s: part_out must be 16-byte aligned", fn);
-  } else {
-    if (!out) return fail(PA_ERR_NULL, "%s: out is NULL", fn);
-    if (out_dtype != PA_F32 && out_dtype != cache->dtype)
-      return fail(PA_ERR_UNSUPPORTED, "%s: out_dtype must be PA_F32 or the cache dtype", fn);
+  if (num_seqs > 0) {
+    if (!q || !block_tables || !context_lens)
+      return fail(PA_ERR_NULL, "%s: q, block_tables or context_lens is NULL", fn);
+    if (!aligned16(q)) return fail(PA_ERR_SHAPE, "%s: q must be 16-byte aligned", fn);
   }
-  if (num_seqs == 0) return PA_OK;
-  if (!q || !block_tables || !context_lens)
-    return fail(PA_ERR_NULL, "%s: q, block_tables or context_lens is NULL", fn);
-  if (!aligned16(q)) return fail(PA_ERR_SHAPE, "%s: q must be 16-byte aligned", fn);
+  *a = DecodeArgs{};
+  a->q = static_cast<const uint8_t*>(q);
+  a->k_pool = static_cast<const uint8_t*>(cache->k_pool);
+  a->v_pool = static_cast<const uint8_t*>(cache->v_pool);
+  a->block_tables = block_tables;
+  a->context_lens = context_lens;
+  a->num_blocks = cache->num_blocks;
+  a->num_seqs = num_seqs;
+  a->num_kv_heads = cache->num_kv_heads;
+  a->num_heads = num_heads;
+  a->max_blocks = max_blocks_per_seq;
+  a->out_f32 = 1;
+  a->scale_log2 = scale * 1.4426950408889634f;
+  return PA_OK;
+}
 
+int launch(const char* fn, const pa_cache* cache, int group, const DecodeArgs& a, dim3 grid,
+           int waves, size_t lds, hipStream_t s) {
+  const bool ok =
+      cache->dtype == PA_BF16
+          ? launch_decode_bf16(cache->head_dim, cache->block_size, group, a, grid, waves, lds, s)
+          : launch_decode_f32(cache->head_dim, cache->block_size, group, a, grid, waves, lds, s);
+  if (!ok) return fail(PA_ERR_UNSUPPORTED, "%s: no kernel for this shape", fn);
+  return launch_result(fn);
+}
+
+constexpr int kMaxBalancedSeqs = 16000;  // the unit prefix of all sequences lives in LDS
+
+}  // namespace
+}  // namespace pa
+
+PA_API size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim) {
+  using namespace pa;
+  if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0) return 0;
+  return layout_for(balanced_groups_max(), num_seqs, num_heads, head_dim).total;
+}
+
+PA_API int pa_decode(const pa_cache* cache, const void* q, const int32_t* block_tables,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                     int32_t max_blocks_per_seq, float scale, void* out, int32_t out_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace pa;
+  const char* fn = "pa_decode";
   DecodeArgs a;
-  a.q = static_cast<const uint8_t*>(q);
-  a.k_pool = static_cast<const uint8_t*>(cache->k_pool);
-  a.v_pool = static_cast<const uint8_t*>(cache->v_pool);
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
+  int group = 0;
+  if (int st = prepare(fn, cache, q, block_tables, context_lens, num_seqs, num_heads,
+                       max_blocks_per_seq, scale, &a, &group))
+    return st;
+  if (!out) return fail(PA_ERR_NULL, "%s: out is NULL", fn);
+  if (out_dtype != PA_F32 && out_dtype != cache->dtype)
+    return fail(PA_ERR_UNSUPPORTED, "%s: out_dtype must be PA_F32 or the cache dtype", fn);
+  if (!aligned16(out)) return fail(PA_ERR_SHAPE, "%s: out must be 16-byte aligned", fn);
+  if (num_seqs == 0) return PA_OK;
   a.out = out;
+  a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
+  const int waves = waves_per_group(cache->num_kv_heads);
+  const unsigned head_groups = unsigned(cache->num_kv_heads / waves);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (workspace == nullptr || num_seqs > kMaxBalancedSeqs) {
+    a.mode = kModeSingle;
+    return launch(fn, cache, group, a, dim3(unsigned(num_seqs), head_groups), waves, 0, s);
+  }
+  const int groups = balanced_groups(waves);
+  const WorkspaceLayout w = layout_for(groups, num_seqs, num_heads, cache->head_dim);
+  if (workspace_bytes < w.total)
+    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes is smaller than the %zu needed", fn,
+                workspace_bytes, w.total);
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+    return fail(PA_ERR_SHAPE, "%s: workspace must be 256-byte aligned", fn);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.mode = kModeBalanced;
+  a.num_groups = groups;
+  a.info = reinterpret_cast<int32_t*>(ws + w.info);
+  a.part_out = reinterpret_cast<float*>(ws + w.piece_out);
+  a.part_max = reinterpret_cast<float*>(ws + w.piece_max);
+  a.part_sum = reinterpret_cast<float*>(ws + w.piece_sum);
+  const size_t lds = size_t(num_seqs + 1) * sizeof(int32_t);
+  if (int st = launch(fn, cache, group, a, dim3(unsigned(groups), head_groups), waves, lds, s))
+    return st;
+  MergeArgs m;
+  m.piece_out = a.part_out;
+  m.piece_max = a.part_max;
+  m.piece_sum = a.part_sum;
+  m.info = a.info;
+  m.out = out;
+  m.num_heads = num_heads;
+  m.num_groups = groups;
+  m.out_f32 = a.out_f32;
+  const dim3 mgrid(static_cast<unsigned>(num_heads), static_cast<unsigned>(num_seqs));
+  if (cache->head_dim == 64)
+    hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(64), 0, s, m);
+  else
+    hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(64), 0, s, m);
+  return launch_result(fn);
+}
+
+PA_API int pa_decode_partitions(const pa_cache* cache, const void* q, const int32_t* block_tables,
+                                const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                int32_t max_blocks_per_seq, float scale, int32_t partition_size,
+                                float* part_out, float* part_max, float* part_sum,
+                                int32_t max_parts, void* stream) {
+  using namespace pa;
+  const char* fn = "pa_decode_partitions";
+  DecodeArgs a;
+  int group = 0;
+  if (int st = prepare(fn, cache, q, block_tables, context_lens, num_seqs, num_heads,
+                       max_blocks_per_seq, scale, &a, &group))
+    return st;
+  if (partition_size <= 0 || partition_size % cache->block_size != 0)
+    return fail(PA_ERR_SHAPE, "%s: partition_size must be a positive multiple of block_size", fn);
+  if (max_parts <= 0 || max_parts > 65535)
+    return fail(PA_ERR_WORKSPACE, "%s: max_parts must be in [1, 65535]", fn);
+  if (!part_out || !part_max || !part_sum)
+    return fail(PA_ERR_WORKSPACE, "%s: part_out, part_max and part_sum are required", fn);
+  if (!aligned16(part_out)) return fail(PA_ERR_SHAPE, "%s: part_out must be 16-byte aligned", fn);
+  if (num_seqs == 0) return PA_OK;
+  a.mode = kModePartition;
+  a.partition_blocks = partition_size / cache->block_size;
+  a.max_parts = max_parts;
   a.part_out = part_out;
   a.part_max = part_max;
   a.part_sum = part_sum;
-  a.num_blocks = cache->num_blocks;
-  a.num_kv_heads = cache->num_kv_heads;
-  a.num_heads = num_heads;
-  a.max_blocks = max_blocks_per_seq;
-  a.partition_blocks = split ? partition_size / cache->block_size : 0;
-  a.max_parts = split ? max_parts : 1;
-  a.out_f32 = (!bf16 || out_dtype == PA_F32) ? 1 : 0;
-  a.scale_log2 = scale * 1.4426950408889634f;
-
-  const dim3 grid(unsigned(split ? max_parts : 1), unsigned(cache->num_kv_heads),
-                  unsigned(num_seqs));
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool ok = bf16 ? launch_decode_bf16(cache->head_dim, cache->block_size, group, a, grid, s)
-                       : launch_decode_f32(cache->head_dim, cache->block_size, group, a, grid, s);
-  if (!ok) return fail(PA_ERR_UNSUPPORTED, "%s: no kernel for this shape", fn);
-  return launch_result(fn);
+  const int waves = waves_per_group(cache->num_kv_heads);
+  const dim3 grid(unsigned(max_parts), unsigned(cache->num_kv_heads / waves), unsigned(num_seqs));
+  return launch(fn, cache, group, a, grid, waves, 0, static_cast<hipStream_t>(stream));
 }

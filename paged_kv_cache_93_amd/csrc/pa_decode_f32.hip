@@ -2,7 +2,8 @@
 #include "pa_decode_kernel.h"
 
 namespace pa {
-bool launch_decode_f32(int d, int bs, int g, const DecodeArgs& a, dim3 grid, hipStream_t s) {
-  return launch_decode_impl<false>(d, bs, g, a, grid, s);
+bool launch_decode_f32(int d, int bs, int g, const DecodeArgs& a, dim3 grid, int waves,
+                        size_t lds, hipStream_t s) {
+  return launch_decode_impl<false>(d, bs, g, a, grid, waves, lds, s);
 }
 }  // namespace pa

@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSU
 
 # Every symbol include/pagedattn.h declares.
 EXPORTED = ("pa_abi_version", "pa_hip_runtime_version", "pa_last_error", "pa_kv_append",
-            "pa_copy_blocks", "pa_decode", "pa_splitkv_reduce", "pa_partials_bytes")
+            "pa_copy_blocks", "pa_decode", "pa_decode_workspace_bytes", "pa_decode_partitions",
+            "pa_splitkv_reduce", "pa_partials_bytes")
 
 
 class PagedAttnError(RuntimeError):
@@ -49,7 +50,10 @@ _SIGNATURES = {
     "pa_kv_append": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _vp, _vp, _i32, _vp]),
     "pa_copy_blocks": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _i32, _vp]),
     "pa_decode": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _vp, _vp, _i32, _i32, _i32, _f32,
-                                 _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp]),
+                                 _vp, _i32, _vp, ctypes.c_size_t, _vp]),
+    "pa_decode_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32]),
+    "pa_decode_partitions": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _vp, _vp, _i32, _i32,
+                                            _i32, _f32, _i32, _vp, _vp, _vp, _i32, _vp]),
     "pa_splitkv_reduce": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp,
                                          _i32, _vp, _vp]),
     "pa_partials_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32]),
@@ -145,41 +149,66 @@ def pa_copy_blocks(k_pool, v_pool, block_pairs, stream=None) -> None:
                                  _stream(stream)))
 
 
-def pa_decode(k_pool, v_pool, q, block_tables, context_lens, scale: float, *, out=None,
-              partition_size: int = 0, part_out=None, part_max=None, part_sum=None,
-              stream=None) -> None:
-    """Decode attention; see include/pagedattn.h for the split-KV partial outputs."""
+def decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int) -> int:
+    """Bytes of workspace pa_decode needs on the current device."""
+    return load().pa_decode_workspace_bytes(num_seqs, num_heads, head_dim)
+
+
+def _decode_common(k_pool, v_pool, q, block_tables, context_lens):
     cache = make_cache(k_pool, v_pool)
     _require(q.dim() == 3 and q.is_contiguous() and q.dtype == k_pool.dtype and
              q.shape[2] == cache.head_dim, "q must be contiguous [num_seqs][num_heads][head_dim]")
-    num_seqs, num_heads = q.shape[0], q.shape[1]
+    num_seqs = q.shape[0]
     _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
              block_tables.is_contiguous() and block_tables.shape[0] == num_seqs,
              "block_tables must be contiguous int32 [num_seqs][max_blocks]")
     _require(context_lens.dtype == torch.int32 and context_lens.is_contiguous() and
              context_lens.numel() == num_seqs, "context_lens must be contiguous int32 [num_seqs]")
-    max_parts = 0
-    out_code = PA_F32
-    if partition_size > 0:
-        _require(part_out is not None and part_out.dim() == 4 and part_out.is_contiguous() and
-                 part_out.dtype == torch.float32 and
-                 tuple(part_out.shape[:2]) == (num_seqs, num_heads) and
-                 part_out.shape[3] == cache.head_dim,
-                 "part_out must be contiguous float32 [num_seqs][num_heads][max_parts][head_dim]")
-        max_parts = part_out.shape[2]
-        for t in (part_max, part_sum):
-            _require(t is not None and t.dtype == torch.float32 and t.is_contiguous() and
-                     tuple(t.shape) == (num_seqs, num_heads, max_parts),
-                     "part_max/part_sum must be contiguous float32 [num_seqs][num_heads][max_parts]")
-    else:
-        _require(out is not None and out.is_contiguous() and
-                 tuple(out.shape) == (num_seqs, num_heads, cache.head_dim),
-                 "out must be contiguous [num_seqs][num_heads][head_dim]")
-        out_code = _dtype_code(out)
+    return cache
+
+
+def pa_decode(k_pool, v_pool, q, block_tables, context_lens, scale: float, out, workspace=None,
+              stream=None) -> None:
+    """Decode attention into out [num_seqs][num_heads][head_dim].
+
+    ``workspace`` (a uint8 device tensor of at least decode_workspace_bytes())
+    enables the balanced split of the batch; None walks each sequence in one
+    workgroup.
+    """
+    cache = _decode_common(k_pool, v_pool, q, block_tables, context_lens)
+    num_seqs, num_heads = q.shape[0], q.shape[1]
+    _require(out is not None and out.is_contiguous() and
+             tuple(out.shape) == (num_seqs, num_heads, cache.head_dim),
+             "out must be contiguous [num_seqs][num_heads][head_dim]")
+    ws_bytes = 0
+    if workspace is not None:
+        _require(workspace.is_contiguous(), "workspace must be contiguous")
+        ws_bytes = workspace.numel() * workspace.element_size()
     _check(load().pa_decode(ctypes.byref(cache), _ptr(q), _ptr(block_tables), _ptr(context_lens),
-                            num_seqs, num_heads, block_tables.shape[1], float(scale),
-                            int(partition_size), _ptr(out), out_code, _ptr(part_out),
-                            _ptr(part_max), _ptr(part_sum), max_parts, _stream(stream)))
+                            num_seqs, num_heads, block_tables.shape[1], float(scale), _ptr(out),
+                            _dtype_code(out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pa_decode_partitions(k_pool, v_pool, q, block_tables, context_lens, scale: float,
+                         partition_size: int, part_out, part_max, part_sum, stream=None) -> None:
+    """Split-KV decode partials; see include/pagedattn.h."""
+    cache = _decode_common(k_pool, v_pool, q, block_tables, context_lens)
+    num_seqs, num_heads = q.shape[0], q.shape[1]
+    _require(part_out is not None and part_out.dim() == 4 and part_out.is_contiguous() and
+             part_out.dtype == torch.float32 and
+             tuple(part_out.shape[:2]) == (num_seqs, num_heads) and
+             part_out.shape[3] == cache.head_dim,
+             "part_out must be contiguous float32 [num_seqs][num_heads][max_parts][head_dim]")
+    max_parts = part_out.shape[2]
+    for t in (part_max, part_sum):
+        _require(t is not None and t.dtype == torch.float32 and t.is_contiguous() and
+                 tuple(t.shape) == (num_seqs, num_heads, max_parts),
+                 "part_max/part_sum must be contiguous float32 [num_seqs][num_heads][max_parts]")
+    _check(load().pa_decode_partitions(ctypes.byref(cache), _ptr(q), _ptr(block_tables),
+                                       _ptr(context_lens), num_seqs, num_heads,
+                                       block_tables.shape[1], float(scale), int(partition_size),
+                                       _ptr(part_out), _ptr(part_max), _ptr(part_sum), max_parts,
+                                       _stream(stream)))
 
 
 def pa_splitkv_reduce(part_out, part_max, part_sum, context_lens, partition_size: int, out,

@@ -59,28 +59,36 @@ def run_writes(t: dict) -> None:
     lib.pa_kv_append(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"], t["slot_mapping"])
 
 
-def run_decode(t: dict, w: W.Workload, partition_size: int = 0, out_f32: bool = False,
+def run_decode(t: dict, w: W.Workload, mode="balanced", out_f32: bool = False,
                lse: bool = False):
-    """pa_decode (+ pa_splitkv_reduce); returns (out, lse or None) on the device."""
+    """One decode through the C ABI; returns (out, lse or None) on the device.
+
+    mode: "balanced" (pa_decode with a workspace), "single" (pa_decode without
+    one) or a partition size in tokens (pa_decode_partitions + pa_splitkv_reduce).
+    """
     scale = 1.0 / math.sqrt(w.head_dim)
     out_dt = torch.float32 if (out_f32 or w.dtype == "f32") else torch.bfloat16
     out = torch.empty((w.num_seqs, w.num_heads, w.head_dim), dtype=out_dt, device="cuda")
     lse_t = None
-    if partition_size == 0:
+    if mode in ("balanced", "single"):
+        ws = None
+        if mode == "balanced":
+            nbytes = lib.decode_workspace_bytes(w.num_seqs, w.num_heads, w.head_dim)
+            ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")  # garbage is fine
         lib.pa_decode(t["k_pool"], t["v_pool"], t["q"], t["block_tables"], t["context_lens"],
-                      scale, out=out)
+                      scale, out, workspace=ws)
     else:
-        mp = max_parts_for(w, partition_size)
+        psize = int(mode)
+        mp = max_parts_for(w, psize)
         po = torch.empty((w.num_seqs, w.num_heads, mp, w.head_dim), dtype=torch.float32,
                          device="cuda")
         pm = torch.empty((w.num_seqs, w.num_heads, mp), dtype=torch.float32, device="cuda")
         ps = torch.empty_like(pm)
-        lib.pa_decode(t["k_pool"], t["v_pool"], t["q"], t["block_tables"], t["context_lens"],
-                      scale, partition_size=partition_size, part_out=po, part_max=pm,
-                      part_sum=ps)
+        lib.pa_decode_partitions(t["k_pool"], t["v_pool"], t["q"], t["block_tables"],
+                                 t["context_lens"], scale, psize, po, pm, ps)
         if lse:
             lse_t = torch.empty((w.num_seqs, w.num_heads), dtype=torch.float32, device="cuda")
-        lib.pa_splitkv_reduce(po, pm, ps, t["context_lens"], partition_size, out, lse=lse_t)
+        lib.pa_splitkv_reduce(po, pm, ps, t["context_lens"], psize, out, lse=lse_t)
     return out, lse_t
 
 

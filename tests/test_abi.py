@@ -58,12 +58,21 @@ def _cache(**kw):
 
 def _decode(cache, **kw):
     a = dict(q=16, tables=16, lens=16, num_seqs=1, num_heads=4, max_blocks=4, scale=0.1,
-             partition=0, out=16, out_dtype=lib.PA_BF16, po=16, pm=16, ps=16, max_parts=1)
+             out=16, out_dtype=lib.PA_BF16, ws=None, ws_bytes=0)
     a.update(kw)
     return lib.raw_call("pa_decode", ctypes.byref(cache) if cache is not None else None,
                         a["q"], a["tables"], a["lens"], a["num_seqs"], a["num_heads"],
-                        a["max_blocks"], a["scale"], a["partition"], a["out"], a["out_dtype"],
-                        a["po"], a["pm"], a["ps"], a["max_parts"], None)
+                        a["max_blocks"], a["scale"], a["out"], a["out_dtype"], a["ws"],
+                        a["ws_bytes"], None)
+
+
+def _partitions(cache, **kw):
+    a = dict(q=16, tables=16, lens=16, num_seqs=1, num_heads=4, max_blocks=4, scale=0.1,
+             psize=32, po=16, pm=16, ps=16, max_parts=1)
+    a.update(kw)
+    return lib.raw_call("pa_decode_partitions", ctypes.byref(cache), a["q"], a["tables"],
+                        a["lens"], a["num_seqs"], a["num_heads"], a["max_blocks"], a["scale"],
+                        a["psize"], a["po"], a["pm"], a["ps"], a["max_parts"], None)
 
 
 @pytest.mark.parametrize("cache_kw,call_kw,status", [
@@ -81,13 +90,11 @@ def _decode(cache, **kw):
     ({}, dict(num_seqs=-1), 2),
     ({}, dict(max_blocks=0), 2),
     ({}, dict(out=0), 1),
+    ({}, dict(out=8), 2),                          # misaligned out
     ({}, dict(out_dtype=9), 3),
     ({}, dict(q=0), 1),
     ({}, dict(q=8), 2),                            # misaligned q
-    ({}, dict(partition=24), 2),                   # not a multiple of the block size
-    ({}, dict(partition=32, max_parts=0), 4),
-    ({}, dict(partition=32, po=0), 4),
-    ({}, dict(partition=-16), 2),
+    ({}, dict(ws=256, ws_bytes=64), 4),            # workspace too small
 ])
 def test_decode_rejects_bad_arguments(cache_kw, call_kw, status):
     cache = None if cache_kw is None else _cache(**cache_kw)
@@ -95,8 +102,29 @@ def test_decode_rejects_bad_arguments(cache_kw, call_kw, status):
     assert lib.load().pa_last_error().decode().startswith("pa_decode:")
 
 
+@pytest.mark.parametrize("call_kw,status", [
+    (dict(psize=24), 2),                           # not a multiple of the block size
+    (dict(psize=0), 2),
+    (dict(max_parts=0), 4),
+    (dict(max_parts=70000), 4),
+    (dict(po=0), 4),
+    (dict(po=8), 2),                               # misaligned part_out
+    (dict(q=0), 1),
+])
+def test_partitions_reject_bad_arguments(call_kw, status):
+    assert _partitions(_cache(), **call_kw) == status
+    assert lib.load().pa_last_error().decode().startswith("pa_decode_partitions:")
+
+
 def test_zero_sequences_is_a_no_op():
     assert _decode(_cache(), num_seqs=0, q=0, tables=0, lens=0) == 0
+    assert _partitions(_cache(), num_seqs=0, q=0, tables=0, lens=0) == 0
+
+
+def test_workspace_bytes():
+    n = lib.decode_workspace_bytes(64, 32, 128)
+    assert n >= (64 + 256) * 32 * 130 * 4  # at least a piece row per (group + sequence)
+    assert lib.decode_workspace_bytes(-1, 32, 128) == 0
 
 
 def test_append_and_copy_reject_bad_arguments():
