@@ -136,8 +136,7 @@ def main() -> int:
     ps = torch.empty_like(pm)
     ws = None
     if mode == "balanced":
-        ws = torch.empty(lib.decode_workspace_bytes(w.num_seqs, w.num_heads, w.head_dim),
-                         dtype=torch.uint8, device="cuda")
+        ws = lib.decode_workspace(w.num_seqs, w.num_heads, w.head_dim)
 
     def step(r, ev=None):
         kp, vp = pools[r]

@@ -133,9 +133,9 @@ int pa_copy_blocks(const pa_cache *cache, const int64_t *block_pairs, int32_t nu
  *
  * With a workspace, the (sequence, block) pairs of the whole batch are split
  * evenly over a fixed grid of workgroups, so long and short sequences finish
- * together; a sequence split between workgroups is merged with the
- * log-sum-exp rule by a second kernel enqueued on the same stream.  Without
- * one (workspace = NULL), one workgroup walks each sequence.
+ * together; the parts of a sequence split between workgroups are merged with
+ * the log-sum-exp rule by a second kernel enqueued on the same stream.
+ * Without one (workspace = NULL), one workgroup walks each sequence.
  *
  *   q             DEVICE [num_seqs][num_heads][head_dim], cache->dtype
  *   block_tables  DEVICE int32 [num_seqs][max_blocks_per_seq]; entries past
@@ -147,8 +147,8 @@ int pa_copy_blocks(const pa_cache *cache, const int64_t *block_pairs, int32_t nu
  *   out_dtype     PA_F32, or cache->dtype
  *   workspace     DEVICE scratch of workspace_bytes >= pa_decode_workspace_bytes(),
  *                 256-byte aligned, or NULL; its contents need no initialising
- *                 and are meaningless afterwards.  Two calls in flight at once
- *                 must not share one.
+ *                 and are meaningless afterwards.  Calls in flight at the same
+ *                 time must not share one.
  */
 int pa_decode(const pa_cache *cache, const void *q, const int32_t *block_tables,
               const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,

@@ -53,26 +53,32 @@ def _run(cmd):
     return text
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile every csrc/*.hip and link libpagedattn.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, jobs: int | None = None, defines=(), out: str = LIB_PATH,
+          build_dir: str = BUILD_DIR) -> str:
+    """Compile every csrc/*.hip and link a shared library; returns its path.
+
+    ``defines`` are extra ``NAME=VALUE`` preprocessor definitions (tuning
+    knobs); ``out`` is the library path (default: the in-tree libpagedattn.so).
+    """
+    os.makedirs(build_dir, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not sources:
         raise RuntimeError("no HIP sources found")
     cc = hipcc()
-    objects = [os.path.join(BUILD_DIR, os.path.basename(s) + ".o") for s in sources]
-    cmds = [[cc, *COMMON_FLAGS, "-c", src, "-o", obj] for src, obj in zip(sources, objects)]
+    flags = [*COMMON_FLAGS, *(f"-D{d}" for d in defines)]
+    objects = [os.path.join(build_dir, os.path.basename(s) + ".o") for s in sources]
+    cmds = [[cc, *flags, "-c", src, "-o", obj] for src, obj in zip(sources, objects)]
     jobs = jobs or min(len(cmds), os.cpu_count() or 4, 16)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        for out in ex.map(_run, cmds):
-            if verbose and out.strip():
-                print(out)
-    tmp = LIB_PATH + ".tmp"
-    out = _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objects])
-    if verbose and out.strip():
-        print(out)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+        for log in ex.map(_run, cmds):
+            if verbose and log.strip():
+                print(log)
+    tmp = out + ".tmp"
+    log = _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objects])
+    if verbose and log.strip():
+        print(log)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -8,39 +8,41 @@
 namespace pa {
 namespace {
 
-// Largest workgroup (in waves, at most 8) made of whole KV heads.
+// Largest workgroup (in waves) made of whole KV heads, at most PA_MAX_WAVES.
 int waves_per_group(int num_kv_heads) {
   for (int w : {8, 4, 2, 1})
-    if (num_kv_heads % w == 0) return w;
+    if (w <= PA_MAX_WAVES && num_kv_heads % w == 0) return w;
   return 1;
 }
 
-// Workgroups of the balanced split for the current device: four per CU at most.
-int balanced_groups_max() {
+int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     cus = 256;
-  return cus * 4;
+  return cus;
 }
 
-// Workgroups the balanced split actually uses: one per CU and resident slot.
-int balanced_groups(int waves_per_wg) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    cus = 256;
-  // 8 waves per CU keep two waves per SIMD; smaller workgroups share a CU.
-  int per_cu = 8 / waves_per_wg;
-  if (per_cu > 4) per_cu = 4;
-  return cus * per_cu;
+// Upper bound on the workgroups of the balanced split: 32 waves per CU.
+constexpr int kMaxGroupsPerCu = 32;
+
+// Workgroups the balanced split uses: as many as the device holds at once.
+int balanced_groups(const pa_cache* cache, int group, int waves, size_t lds) {
+  int per_cu = cache->dtype == PA_BF16
+                   ? decode_groups_per_cu_bf16(cache->head_dim, cache->block_size, group, waves, lds)
+                   : decode_groups_per_cu_f32(cache->head_dim, cache->block_size, group, waves, lds);
+  if (per_cu < 1) per_cu = 1;
+  if (per_cu > kMaxGroupsPerCu) per_cu = kMaxGroupsPerCu;
+  return device_cus() * per_cu;
 }
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Workspace of the balanced split: the split description (workgroups used,
+// units, first unit of every sequence), then the piece partials, one row per
+// (workgroup + sequence, query head).
 struct WorkspaceLayout {
   size_t info, piece_out, piece_max, piece_sum, total;
 };
@@ -49,7 +51,7 @@ WorkspaceLayout layout_for(int64_t groups, int64_t num_seqs, int64_t num_heads, 
   WorkspaceLayout w;
   const int64_t rows = (groups + num_seqs) * num_heads;
   w.info = 0;
-  w.piece_out = align_up(size_t(num_seqs + 2) * sizeof(int32_t));
+  w.piece_out = align_up(size_t(num_seqs + 3) * sizeof(int32_t));
   w.piece_max = w.piece_out + align_up(size_t(rows) * head_dim * sizeof(float));
   w.piece_sum = w.piece_max + align_up(size_t(rows) * sizeof(float));
   w.total = w.piece_sum + align_up(size_t(rows) * sizeof(float));
@@ -122,7 +124,7 @@ constexpr int kMaxBalancedSeqs = 16000;  // the unit prefix of all sequences liv
 PA_API size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim) {
   using namespace pa;
   if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0) return 0;
-  return layout_for(balanced_groups_max(), num_seqs, num_heads, head_dim).total;
+  return layout_for(int64_t(device_cus()) * kMaxGroupsPerCu, num_seqs, num_heads, head_dim).total;
 }
 
 PA_API int pa_decode(const pa_cache* cache, const void* q, const int32_t* block_tables,
@@ -147,11 +149,14 @@ PA_API int pa_decode(const pa_cache* cache, const void* q, const int32_t* block_
   const unsigned head_groups = unsigned(cache->num_kv_heads / waves);
   const hipStream_t s = static_cast<hipStream_t>(stream);
 
+  const size_t wave_lds =
+      size_t(waves) * decode_wave_lds_bytes(cache->dtype == PA_BF16, cache->head_dim, group);
   if (workspace == nullptr || num_seqs > kMaxBalancedSeqs) {
     a.mode = kModeSingle;
-    return launch(fn, cache, group, a, dim3(unsigned(num_seqs), head_groups), waves, 0, s);
+    return launch(fn, cache, group, a, dim3(unsigned(num_seqs), head_groups), waves, wave_lds, s);
   }
-  const int groups = balanced_groups(waves);
+  const size_t lds = decode_prefix_lds_bytes(num_seqs, true) + wave_lds;
+  const int groups = balanced_groups(cache, group, waves, lds);
   const WorkspaceLayout w = layout_for(groups, num_seqs, num_heads, cache->head_dim);
   if (workspace_bytes < w.total)
     return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes is smaller than the %zu needed", fn,
@@ -165,7 +170,6 @@ PA_API int pa_decode(const pa_cache* cache, const void* q, const int32_t* block_
   a.part_out = reinterpret_cast<float*>(ws + w.piece_out);
   a.part_max = reinterpret_cast<float*>(ws + w.piece_max);
   a.part_sum = reinterpret_cast<float*>(ws + w.piece_sum);
-  const size_t lds = size_t(num_seqs + 1) * sizeof(int32_t);
   if (int st = launch(fn, cache, group, a, dim3(unsigned(groups), head_groups), waves, lds, s))
     return st;
   MergeArgs m;
@@ -175,7 +179,6 @@ PA_API int pa_decode(const pa_cache* cache, const void* q, const int32_t* block_
   m.info = a.info;
   m.out = out;
   m.num_heads = num_heads;
-  m.num_groups = groups;
   m.out_f32 = a.out_f32;
   const dim3 mgrid(static_cast<unsigned>(num_heads), static_cast<unsigned>(num_seqs));
   if (cache->head_dim == 64)
@@ -213,5 +216,7 @@ PA_API int pa_decode_partitions(const pa_cache* cache, const void* q, const int3
   a.part_sum = part_sum;
   const int waves = waves_per_group(cache->num_kv_heads);
   const dim3 grid(unsigned(max_parts), unsigned(cache->num_kv_heads / waves), unsigned(num_seqs));
-  return launch(fn, cache, group, a, grid, waves, 0, static_cast<hipStream_t>(stream));
+  const size_t lds =
+      size_t(waves) * decode_wave_lds_bytes(cache->dtype == PA_BF16, cache->head_dim, group);
+  return launch(fn, cache, group, a, grid, waves, lds, static_cast<hipStream_t>(stream));
 }

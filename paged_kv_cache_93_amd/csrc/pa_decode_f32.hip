@@ -6,4 +6,7 @@ bool launch_decode_f32(int d, int bs, int g, const DecodeArgs& a, dim3 grid, int
                         size_t lds, hipStream_t s) {
   return launch_decode_impl<false>(d, bs, g, a, grid, waves, lds, s);
 }
+int decode_groups_per_cu_f32(int d, int bs, int g, int waves, size_t lds) {
+  return decode_groups_per_cu_impl<false>(d, bs, g, waves, lds);
+}
 }  // namespace pa

@@ -33,8 +33,7 @@
 // * Block-table entries of up to 64 units are fetched with one vector load
 //   (one per lane) and handed out with v_readlane, so each is read once.
 // * K/V tiles sit in a ring of PF+1 register buffers: the loads of the next
-//   PF tiles are in flight while the current tile is scored and accumulated,
-//   across sequence boundaries too.
+//   PF tiles are in flight while the current tile is scored and accumulated.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -55,7 +54,7 @@ struct DecodeArgs {
   float* part_out;      // partition partials, or balanced-mode pieces
   float* part_max;
   float* part_sum;
-  int32_t* info;        // balanced: [0] total units, [1 + i] first unit of sequence i (i <= S)
+  int32_t* info;        // balanced: [0] workgroups used, [1] units, [2 + i] first unit of sequence i
   int64_t num_blocks;
   int32_t num_seqs;
   int32_t num_kv_heads;
@@ -64,20 +63,9 @@ struct DecodeArgs {
   int32_t mode;
   int32_t partition_blocks;  // partition mode: blocks per partition
   int32_t max_parts;         // partition mode: partitions per (sequence, head) row
-  int32_t num_groups;        // balanced mode: workgroups sharing the units
+  int32_t num_groups;        // balanced mode: workgroups in the grid (those past the unit count idle)
   int32_t out_f32;           // 1: binary32 output; 0: bf16 output (bf16 cache only)
   float scale_log2;          // score scale * log2(e)
-};
-
-struct MergeArgs {
-  const float* piece_out;
-  const float* piece_max;
-  const float* piece_sum;
-  const int32_t* info;
-  void* out;
-  int32_t num_heads;
-  int32_t num_groups;
-  int32_t out_f32;
 };
 
 namespace dev {
@@ -163,6 +151,9 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
   return u >> 16;
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 // Workgroup that processes unit u when `total` units are split evenly over
 // `groups` workgroups (workgroup g takes [g*total/groups, (g+1)*total/groups)).
 __device__ __forceinline__ int group_of_unit(int64_t u, int64_t total, int64_t groups) {
@@ -171,6 +162,21 @@ __device__ __forceinline__ int group_of_unit(int64_t u, int64_t total, int64_t g
 
 }  // namespace dev
 
+// Scores on the matrix cores: bf16 caches with 128-dim heads.
+constexpr bool decode_uses_mfma(bool bf16, int d) { return bf16 && d == 128; }
+
+// LDS bytes each wave of the MFMA path uses: a 16-row K tile padded to 17
+// chunks per row (conflict-free transposed reads), then the softmax weights
+// [4 row groups][G heads][4 rows] and the rescale factors [4][G].
+constexpr int decode_wave_lds_bytes(bool bf16, int d, int g) {
+  return decode_uses_mfma(bf16, d) ? 16 * 17 * 16 + 64 * g + 16 * g : 0;
+}
+
+// Byte offset of the per-wave LDS areas behind the unit prefix (balanced mode).
+constexpr size_t decode_prefix_lds_bytes(int num_seqs, bool balanced) {
+  return balanced ? (size_t(num_seqs + 1) * 4 + 15) / 16 * 16 : 0;
+}
+
 template <bool BF16, int D, int BS, int G, int PF, bool NT>
 __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   using namespace dev;
@@ -178,14 +184,15 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   constexpr int VEC = 16 / EB;                       // elements per 16-byte chunk
   constexpr int LPR = D / VEC;                       // lanes per row
   constexpr int RPI = 64 / LPR;                      // rows per load instruction
-  constexpr int TRW = (G >= 8 ? 2 : 4) * RPI;        // wide groups keep smaller tiles
+  constexpr bool MF = decode_uses_mfma(BF16, D);     // q.k on MFMA (16-row tiles)
+  constexpr int TRW = MF ? 16 : (G >= 8 ? 2 : 4) * RPI;  // wide groups keep smaller tiles
   constexpr int TR = BS < TRW ? BS : TRW;            // rows per register tile
   constexpr int NI = TR / RPI;                       // load instructions per tile
   constexpr int TPB = BS / TR;                       // tiles per block
   constexpr int NB = PF + 1;                         // ring buffers
-  constexpr bool QPF = G <= 4;                       // prefetch the next piece's query
   static_assert(D % VEC == 0 && 64 % LPR == 0 && TR % RPI == 0 && BS % TR == 0, "tiling");
   static_assert(RPI * D * EB == 1024, "one load instruction covers 1 KiB");
+  static_assert(!MF || (RPI == 4 && NI == 4 && TR == 16), "MFMA tiles are 16 rows of 4 groups");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -202,6 +209,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   extern __shared__ int32_t s_prefix[];
   int fixed_seq = -1;
   int64_t ubeg, uend;
+  int64_t total_units = 0, num_groups = 0;
   if (a.mode == kModeBalanced) {
     const int S = a.num_seqs;
     for (int i = threadIdx.x; i < S; i += blockDim.x) {
@@ -226,13 +234,19 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
       }
     }
     __syncthreads();
-    const int64_t total_units = s_prefix[S];
+    total_units = s_prefix[S];
+    // never more workgroups than units, so no workgroup's range is empty and
+    // the pieces of a sequence come from consecutive workgroups g0..g1
+    num_groups = min(int64_t(a.num_groups), total_units);
     if (blockIdx.x == 0 && blockIdx.y == 0) {
-      for (int i = threadIdx.x; i <= S; i += blockDim.x) a.info[1 + i] = s_prefix[i];
-      if (threadIdx.x == 0) a.info[0] = int32_t(total_units);
+      for (int i = threadIdx.x; i <= S; i += blockDim.x) a.info[2 + i] = s_prefix[i];
+      if (threadIdx.x == 0) {
+        a.info[0] = int32_t(num_groups);
+        a.info[1] = int32_t(total_units);
+      }
     }
-    ubeg = int64_t(blockIdx.x) * total_units / a.num_groups;
-    uend = int64_t(blockIdx.x + 1) * total_units / a.num_groups;
+    ubeg = blockIdx.x < num_groups ? int64_t(blockIdx.x) * total_units / num_groups : 0;
+    uend = blockIdx.x < num_groups ? int64_t(blockIdx.x + 1) * total_units / num_groups : 0;
   } else {
     fixed_seq = a.mode == kModeSingle ? blockIdx.x : blockIdx.z;
     int len = a.context_lens[fixed_seq];
@@ -246,6 +260,14 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
       if (ubeg >= uend) return;  // whole workgroup, before any barrier
     }
   }
+
+  // Per-wave LDS of the MFMA path, behind the unit prefix.
+  uint8_t* wave_lds = reinterpret_cast<uint8_t*>(s_prefix) +
+                      decode_prefix_lds_bytes(a.num_seqs, a.mode == kModeBalanced) +
+                      size_t(wave) * decode_wave_lds_bytes(BF16, D, G);
+  u32x4* lds_k = reinterpret_cast<u32x4*>(wave_lds);              // [16 rows][17 chunks]
+  float* lds_p = reinterpret_cast<float*>(wave_lds + 16 * 17 * 16);  // [4][G][4]
+  float* lds_a = lds_p + 16 * G;                                   // [4][G]
 
   const size_t head_bytes = size_t(BS) * D * EB;
   const size_t block_bytes = head_bytes * a.num_kv_heads;
@@ -271,27 +293,31 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   }
 
   // ---- per-piece state -------------------------------------------------------
+  // Row group r = lane / LPR accumulates, for its D/LPR dims, the rows it sees.
+  // VALU path: every lane of a group keeps the group's running max m and sum l
+  // for all G heads.  MFMA path: lane 16g + h (h < G) keeps them for group g,
+  // head h in mf_m / mf_l; m[] and l[] are filled only when a piece is emitted.
   float m[G], l[G], acc[G][VEC];
-  auto reset = [&]() {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      m[h] = kNegInf;
-      l[h] = 0.f;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[h][e] = 0.f;
-    }
-  };
-  reset();
-  u32x4 qc[G], qn[QPF ? G : 1];
-  auto load_q = [&](u32x4(&dst)[G], int seq) {
-    const u32x4* qrow = reinterpret_cast<const u32x4*>(
-        a.q + (size_t(seq) * a.num_heads + head0) * D * EB);
-#pragma unroll
-    for (int h = 0; h < G; ++h) dst[h] = qrow[h * LPR + c];
-  };
+  float mf_m = kNegInf, mf_l = 0.f;
+  u32x4 qc[MF ? 1 : G];  // VALU path: chunk c of each head's query
+  u32x4 qf[MF ? 4 : 1];  // MFMA path: B operands (Q^T slices of 32 dims)
 
   // Emit the finished piece (blocks j_first..j_last) of sequence `seq`.
   auto emit = [&](int seq, int j_first, int j_last, int len) {
+    if constexpr (MF) {
+      // hand each row group's (m, l) of every head to all lanes of the group
+      if ((lane & 15) < G) {
+        lds_p[(lane >> 4) * G + (lane & 15)] = mf_m;
+        lds_p[4 * G + (lane >> 4) * G + (lane & 15)] = mf_l;
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        m[h] = lds_p[r * G + h];
+        l[h] = lds_p[4 * G + r * G + h];
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
     // merge the RPI row groups (lanes that differ in r)
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -352,92 +378,171 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     }
   };
 
-  // ---- chunks of up to 64 units ------------------------------------------------
-  // A piece may run on into the next chunk (same sequence): then its state,
-  // query and first block carry over.
-  bool carry = false;
-  int cur_seq = 0, cur_first = 0;
-  for (int64_t c0 = ubeg; c0 < uend; c0 += 64) {
-    const int n = int(min(int64_t(64), uend - c0));
-    // per-lane unit description: sequence, block index, context length, physical block
-    int sk = 0, jk = 0, lk = 0, pk = -1;
-    if (lane < n) {
-      const int64_t u = c0 + lane;
-      if (fixed_seq >= 0) {
-        sk = fixed_seq;
-        jk = int(u);
+  // ---- pieces: maximal runs of the range's units that share a sequence -------
+  // The steady-state tile loop issues the same loads every iteration (no
+  // load sits behind a branch), so the compiler's wait before scoring a tile
+  // leaves the later tiles' loads in flight.  Prefetches past the end of a
+  // chunk, and tiles whose table entry is out of range, read block 0 instead
+  // (their data is never used).
+  for (int64_t u = ubeg; u < uend;) {
+    int seq, j0;
+    int64_t pend;
+    if (fixed_seq >= 0) {
+      seq = fixed_seq;
+      j0 = int(u);
+      pend = uend;
+    } else {
+      int lo = 0, hi = a.num_seqs;  // s_prefix[lo] <= u < s_prefix[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_prefix[mid] <= u) lo = mid; else hi = mid;
+      }
+      seq = __builtin_amdgcn_readfirstlane(lo);
+      j0 = int(u - s_prefix[seq]);
+      pend = min(uend, int64_t(s_prefix[seq + 1]));
+    }
+    int len = a.context_lens[seq];
+    len = len < 0 ? 0 : (len > max_tokens ? max_tokens : len);
+    const int32_t* trow = a.block_tables + size_t(seq) * a.max_blocks;
+
+    {
+      const u32x4* qrow = reinterpret_cast<const u32x4*>(
+          a.q + (size_t(seq) * a.num_heads + head0) * D * EB);
+      if constexpr (MF) {
+        // lane 16g + h: head h's dims [32mm + 8g, 32mm + 8g + 8) of MFMA mm
+        const int h = lane & 15;
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm)
+          qf[mm] = h < G ? qrow[h * LPR + 4 * mm + (lane >> 4)] : u32x4{0, 0, 0, 0};
+        mf_m = kNegInf;
+        mf_l = 0.f;
       } else {
-        int lo = 0, hi = a.num_seqs;  // s_prefix[lo] <= u < s_prefix[hi]
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (s_prefix[mid] <= u) lo = mid; else hi = mid;
+#pragma unroll
+        for (int h = 0; h < G; ++h) qc[h] = qrow[h * LPR + c];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          m[h] = kNegInf;
+          l[h] = 0.f;
         }
-        sk = lo;
-        jk = int(u - s_prefix[lo]);
       }
-      const int len = a.context_lens[sk];
-      lk = len < 0 ? 0 : (len > max_tokens ? max_tokens : len);
-      const int e = a.block_tables[size_t(sk) * a.max_blocks + jk];
-      pk = (e >= 0 && int64_t(e) < a.num_blocks) ? e : -1;
-    }
-    // piece starts: units whose sequence differs from the previous unit's
-    const int sprev = __shfl_up(sk, 1);
-    const uint64_t starts = __ballot(lane < n && (lane == 0 ? !carry : sk != sprev));
-    // does the piece open at the chunk's end continue into the next chunk?
-    const int last_seq = __builtin_amdgcn_readlane(sk, n - 1);
-    const bool cont = c0 + n < uend && (fixed_seq >= 0 || c0 + n < s_prefix[last_seq + 1]);
-
-    if (!carry) {
-      cur_seq = __builtin_amdgcn_readlane(sk, 0);
-      cur_first = __builtin_amdgcn_readlane(jk, 0);
-      load_q(qc, cur_seq);
-    }
-    uint64_t later = starts & ~uint64_t(1);  // piece starts after the current piece
-    if constexpr (QPF)
-      if (later) load_q(qn, __builtin_amdgcn_readlane(sk, __builtin_ctzll(later)));
-
-    auto load_tile = [&](u32x4(&kr)[NI], u32x4(&vr)[NI], int t) {
-      const int phys = __builtin_amdgcn_readlane(pk, t / TPB);
-      if (phys < 0) return;
-      const size_t off = size_t(phys) * block_bytes + size_t(t % TPB) * (TR * D * EB);
-      const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + off) + lane;
-      const u32x4* vp = reinterpret_cast<const u32x4*>(vbase + off) + lane;
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        kr[i] = load16<NT>(kp + i * 64);
-        vr[i] = load16<NT>(vp + i * 64);
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[h][e] = 0.f;
+    }
+
+    for (int64_t c0 = u; c0 < pend; c0 += 64) {
+      const int n = int(min(int64_t(64), pend - c0));
+      const int jc = j0 + int(c0 - u);  // block index of the chunk's first unit
+      int pk = -1;                      // lane k: physical block of unit c0 + k
+      if (lane < n) {
+        const int e = trow[jc + lane];
+        pk = (e >= 0 && int64_t(e) < a.num_blocks) ? e : -1;
       }
-    };
+      const int ntiles = n * TPB;
 
-    auto process_tile = [&](const u32x4(&kr)[NI], const u32x4(&vr)[NI], int t) {
-      const int ut = t / TPB;
-      const int sub = t % TPB;
-      if (sub == 0 && ut > 0 && ((starts >> ut) & 1)) {
-        // a new piece begins (its query was prefetched into qn when QPF)
-        cur_seq = __builtin_amdgcn_readlane(sk, ut);
-        cur_first = __builtin_amdgcn_readlane(jk, ut);
-        if constexpr (QPF) {
+      auto load_tile = [&](u32x4(&kr)[NI], u32x4(&vr)[NI], int t) {
+        const int tt = t < ntiles ? t : ntiles - 1;
+        int phys = __builtin_amdgcn_readlane(pk, tt / TPB);
+        size_t off = size_t(tt % TPB) * (TR * D * EB);
+        if (t >= ntiles || phys < 0) {
+          phys = 0;
+          off = 0;
+        }
+        off += size_t(phys) * block_bytes;
+        // VALU path: instruction i holds rows i*RPI + r.  MFMA path: rows 4r + i,
+        // so each row group sees 4 consecutive rows, as the MFMA result rows.
+        const int lo = MF ? r * 64 + c : lane;
+        constexpr int step = MF ? 16 : 64;
+        const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + off) + lo;
+        const u32x4* vp = reinterpret_cast<const u32x4*>(vbase + off) + lo;
 #pragma unroll
-          for (int h = 0; h < G; ++h) qc[h] = qn[h];
-          later &= ~((uint64_t(2) << ut) - 1);
-          if (later) load_q(qn, __builtin_amdgcn_readlane(sk, __builtin_ctzll(later)));
+        for (int i = 0; i < NI; ++i) {
+          kr[i] = load16<NT>(kp + i * step);
+          vr[i] = load16<NT>(vp + i * step);
+        }
+      };
+
+      auto process_tile = [&](const u32x4(&kr)[NI], const u32x4(&vr)[NI], int t) {
+        const int ut = t / TPB;
+        const int sub = t % TPB;
+        const int phys = __builtin_amdgcn_readlane(pk, ut);
+        const int tok0 = (jc + ut) * BS + sub * TR;
+        const int nvalid = phys < 0 ? 0 : min(TR, len - tok0);
+        if (nvalid <= 0) return;
+        const bool partial = nvalid < TR;
+        if constexpr (MF) {
+          // K tile -> LDS, then read back transposed: lane 16g + t gets row t's
+          // dims [32mm + 8g, 32mm + 8g + 8) as the A operand of MFMA mm.
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lds_k[(4 * r + i) * 17 + c] = kr[i];
+          __builtin_amdgcn_wave_barrier();
+          f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int mm = 0; mm < 4; ++mm) {
+            const u32x4 kf = lds_k[(lane & 15) * 17 + 4 * mm + (lane >> 4)];
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf),
+                                                         __builtin_bit_cast(bf16x8, qf[mm]),
+                                                         sc, 0, 0, 0);
+          }
+          // lane 16g + h: scores of rows 4g + v (v = 0..3), head h
+          const int g4 = 4 * (lane >> 4);
+          float sv[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            sv[v] = sc[v] * cl2;
+            if (partial && g4 + v >= nvalid) sv[v] = kNegInf;
+          }
+          const float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+          const float mnew = fmaxf(mf_m, mx);
+          const float base = (mnew == kNegInf) ? 0.f : mnew;
+          const float alpha = fast_exp2(mf_m - base);
+          float pv[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) pv[v] = fast_exp2(sv[v] - base);
+          mf_l = fmaf(mf_l, alpha, (pv[0] + pv[1]) + (pv[2] + pv[3]));
+          mf_m = mnew;
+          const bool live = (lane & 15) < G;
+          if (live) {
+            float* dst = lds_p + ((lane >> 4) * G + (lane & 15)) * 4;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) dst[v] = pv[v];
+            lds_a[(lane >> 4) * G + (lane & 15)] = alpha;
+          }
+          const bool rescale = __ballot(live && alpha != 1.f) != 0;
+          __builtin_amdgcn_wave_barrier();
+          // row group r reads its weights: rows 4r + i, every head
+          if (rescale) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              const float al = lds_a[r * G + h];
+#pragma unroll
+              for (int e = 0; e < VEC; ++e) acc[h][e] *= al;
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float v[VEC];
+            unpack16<BF16>(vr[i], v);
+            if (partial && 4 * r + i >= nvalid) {
+#pragma unroll
+              for (int e = 0; e < VEC; ++e) v[e] = 0.f;  // masked rows may hold NaN
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              const float ph = lds_p[(r * G + h) * 4 + i];
+#pragma unroll
+              for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(ph, v[e], acc[h][e]);
+            }
+          }
+          __builtin_amdgcn_wave_barrier();
         } else {
-          load_q(qc, cur_seq);
-        }
-      }
-      const int phys = __builtin_amdgcn_readlane(pk, ut);
-      const int j = __builtin_amdgcn_readlane(jk, ut);
-      const int len = __builtin_amdgcn_readlane(lk, ut);
-      const int tok0 = j * BS + sub * TR;
-      const int nvalid = phys < 0 ? 0 : min(TR, len - tok0);
-      if (nvalid > 0) {
         float s[NI][G];
 #pragma unroll
         for (int i = 0; i < NI; ++i)
 #pragma unroll
           for (int h = 0; h < G; ++h)
             s[i][h] = group_sum<LPR>(dot16<BF16>(0.f, qc[h], kr[i])) * cl2;
-        const bool partial = nvalid < TR;
         if (partial) {
 #pragma unroll
           for (int i = 0; i < NI; ++i)
@@ -478,37 +583,40 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(p[i][h], v[e], acc[h][e]);
         }
-      }
-      const bool piece_end =
-          sub == TPB - 1 && (ut == n - 1 ? !cont : ((starts >> (ut + 1)) & 1));
-      if (piece_end) {
-        emit(cur_seq, cur_first, j, len);
-        reset();
-      }
-    };
+        }
+      };
 
-    const int ntiles = n * TPB;
-    u32x4 kb[NB][NI], vb[NB][NI];
+      u32x4 kb[NB][NI], vb[NB][NI];
 #pragma unroll
-    for (int i = 0; i < PF; ++i)
-      if (i < ntiles) load_tile(kb[i], vb[i], i);
-    for (int t0 = 0; t0 < ntiles; t0 += NB) {
+      for (int i = 0; i < PF; ++i) load_tile(kb[i], vb[i], i);
+      for (int t0 = 0; t0 < ntiles; t0 += NB) {
 #pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const int t = t0 + u;
-        if (t < ntiles) {
-          if (t + PF < ntiles) load_tile(kb[(u + PF) % NB], vb[(u + PF) % NB], t + PF);
-          process_tile(kb[u], vb[u], t);
+        for (int k = 0; k < NB; ++k) {
+          const int t = t0 + k;
+          load_tile(kb[(k + PF) % NB], vb[(k + PF) % NB], t + PF);
+          if (t < ntiles) process_tile(kb[k], vb[k], t);
         }
       }
     }
-    carry = cont;
+    emit(seq, j0, j0 + int(pend - u) - 1, len);
+    u = pend;
   }
 }
 
-// Merge the pieces of each sequence that more than one workgroup worked on
-// (balanced mode), and write zeros for empty sequences.  One wave per
-// (sequence, query head); pieces carry log2-unit maxima.
+struct MergeArgs {
+  const float* piece_out;
+  const float* piece_max;
+  const float* piece_sum;
+  const int32_t* info;
+  void* out;
+  int32_t num_heads;
+  int32_t out_f32;
+};
+
+// Merge the pieces of sequences split between workgroups (balanced mode) and
+// write zeros for empty sequences.  One wave per (sequence, query head).  The
+// work is three memory round trips: the split, the pieces' maxima and sums
+// (lane p reads piece p), and the pieces' output rows (read back to back).
 template <int D>
 __global__ void __launch_bounds__(64) merge_kernel(MergeArgs a) {
   using namespace dev;
@@ -516,33 +624,51 @@ __global__ void __launch_bounds__(64) merge_kernel(MergeArgs a) {
   const int lane = threadIdx.x;
   const int head = blockIdx.x;
   const int seq = blockIdx.y;
-  const int64_t total = a.info[0];
-  const int64_t u0 = a.info[1 + seq];
-  const int64_t u1 = a.info[2 + seq];  // one past the sequence's last unit
+  const int64_t groups = a.info[0];
+  const int64_t total = a.info[1];
+  const int64_t u0 = a.info[2 + seq];
+  const int64_t u1 = a.info[3 + seq];  // one past the sequence's last unit
   const size_t orow = (size_t(seq) * a.num_heads + head) * D;
   float accv[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) accv[e] = 0.f;
   float wsum = 0.f;
   if (u1 > u0) {
-    const int g0 = group_of_unit(u0, total, a.num_groups);
-    const int g1 = group_of_unit(u1 - 1, total, a.num_groups);
+    const int g0 = group_of_unit(u0, total, groups);
+    const int g1 = group_of_unit(u1 - 1, total, groups);
     if (g0 == g1) return;  // one workgroup held the whole sequence and wrote it
+    const int np = g1 - g0 + 1;
     float big = kNegInf;
-    for (int g = g0; g <= g1; ++g) {
-      const size_t row = (size_t(g) + seq) * a.num_heads + head;
-      if (a.piece_sum[row] > 0.f) big = fmaxf(big, a.piece_max[row]);
+    for (int p0 = 0; p0 < np; p0 += 64) {
+      const int p = p0 + lane;
+      if (p < np) {
+        const size_t row = (size_t(g0 + p) + seq) * a.num_heads + head;
+        if (a.piece_sum[row] > 0.f) big = fmaxf(big, a.piece_max[row]);
+      }
     }
-    for (int g = g0; g <= g1; ++g) {
-      const size_t row = (size_t(g) + seq) * a.num_heads + head;
-      const float s = a.piece_sum[row];
-      if (!(s > 0.f)) continue;
-      const float w = s * fast_exp2(a.piece_max[row] - big);
-      wsum += w;
 #pragma unroll
-      for (int e = 0; e < PER; ++e)
-        accv[e] = fmaf(w, a.piece_out[row * D + e * 64 + lane], accv[e]);
+    for (int off = 1; off < 64; off <<= 1) big = fmaxf(big, __shfl_xor(big, off));
+    for (int p0 = 0; p0 < np; p0 += 64) {
+      const int p = p0 + lane;
+      float w = 0.f;
+      if (p < np) {
+        const size_t row = (size_t(g0 + p) + seq) * a.num_heads + head;
+        const float s = a.piece_sum[row];
+        w = s > 0.f ? s * fast_exp2(a.piece_max[row] - big) : 0.f;
+      }
+      wsum += w;
+      const int cnt = np - p0 < 64 ? np - p0 : 64;
+      const float* rows = a.piece_out + ((size_t(g0 + p0) + seq) * a.num_heads + head) * D + lane;
+      const size_t stride = size_t(a.num_heads) * D;  // next workgroup's row of this head
+#pragma unroll 8
+      for (int j = 0; j < cnt; ++j) {
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+#pragma unroll
+        for (int e = 0; e < PER; ++e) accv[e] = fmaf(wj, rows[j * stride + e * 64], accv[e]);
+      }
     }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) wsum += __shfl_xor(wsum, off);
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
@@ -555,6 +681,17 @@ __global__ void __launch_bounds__(64) merge_kernel(MergeArgs a) {
   }
 }
 
+// Tuning knobs (compile-time): ring depth per group width, widest workgroup.
+#ifndef PA_PREFETCH_NARROW
+#define PA_PREFETCH_NARROW 1  // tiles in flight ahead of the current one, G <= 4
+#endif
+#ifndef PA_PREFETCH_WIDE
+#define PA_PREFETCH_WIDE 1    // G = 8
+#endif
+#ifndef PA_MAX_WAVES
+#define PA_MAX_WAVES 8        // KV heads (waves) per workgroup at most
+#endif
+
 // Launches decode_kernel for a runtime (D, BS, G) on a grid of `waves`-wave
 // workgroups with `lds` bytes of dynamic LDS; false when no instantiation matches.
 bool launch_decode_f32(int d, int bs, int g, const DecodeArgs& a, dim3 grid, int waves,
@@ -562,14 +699,21 @@ bool launch_decode_f32(int d, int bs, int g, const DecodeArgs& a, dim3 grid, int
 bool launch_decode_bf16(int d, int bs, int g, const DecodeArgs& a, dim3 grid, int waves,
                         size_t lds, hipStream_t s);
 
+// Workgroups of `waves` waves one CU holds at once for the decode kernel of
+// (D, BS, G), or 0 when no instantiation matches.
+int decode_groups_per_cu_f32(int d, int bs, int g, int waves, size_t lds);
+int decode_groups_per_cu_bf16(int d, int bs, int g, int waves, size_t lds);
+
 // Instantiation table: D in {64, 128}, block size in {16, 32}, G in {1, 2, 4, 8}.
 template <bool BF16>
 bool launch_decode_impl(int d, int bs, int g, const DecodeArgs& a, dim3 grid, int waves,
                         size_t lds, hipStream_t s) {
 #define PA_DECODE_CASE(D_, BS_, G_)                                                       \
   if (d == D_ && bs == BS_ && g == G_) {                                                 \
-    hipLaunchKernelGGL((decode_kernel<BF16, D_, BS_, G_, (G_ <= 4 ? 2 : 1), true>), grid, \
-                       dim3(waves * 64), lds, s, a);                                     \
+    hipLaunchKernelGGL(                                                                  \
+        (decode_kernel<BF16, D_, BS_, G_, (G_ <= 4 ? PA_PREFETCH_NARROW : PA_PREFETCH_WIDE), \
+                       true>),                                                            \
+        grid, dim3(waves * 64), lds, s, a);                                              \
     return true;                                                                         \
   }
 #define PA_DECODE_G(D_, BS_) \
@@ -581,6 +725,33 @@ bool launch_decode_impl(int d, int bs, int g, const DecodeArgs& a, dim3 grid, in
 #undef PA_DECODE_G
 #undef PA_DECODE_CASE
   return false;
+}
+
+}  // namespace pa
+
+namespace pa {
+
+template <bool BF16>
+int decode_groups_per_cu_impl(int d, int bs, int g, int waves, size_t lds) {
+  int n = 0;
+#define PA_OCC_CASE(D_, BS_, G_)                                                             \
+  if (d == D_ && bs == BS_ && g == G_) {                                                    \
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(                                       \
+            &n,                                                                             \
+            decode_kernel<BF16, D_, BS_, G_, (G_ <= 4 ? PA_PREFETCH_NARROW : PA_PREFETCH_WIDE), \
+                          true>,                                                            \
+            waves * 64, lds) != hipSuccess)                                                 \
+      n = 0;                                                                                \
+    return n;                                                                               \
+  }
+#define PA_OCC_G(D_, BS_) PA_OCC_CASE(D_, BS_, 1) PA_OCC_CASE(D_, BS_, 2) PA_OCC_CASE(D_, BS_, 4) PA_OCC_CASE(D_, BS_, 8)
+  PA_OCC_G(64, 16)
+  PA_OCC_G(64, 32)
+  PA_OCC_G(128, 16)
+  PA_OCC_G(128, 32)
+#undef PA_OCC_G
+#undef PA_OCC_CASE
+  return 0;
 }
 
 }  // namespace pa

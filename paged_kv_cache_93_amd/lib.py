@@ -154,6 +154,13 @@ def decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int) -> int:
     return load().pa_decode_workspace_bytes(num_seqs, num_heads, head_dim)
 
 
+def decode_workspace(num_seqs: int, num_heads: int, head_dim: int,
+                     device="cuda") -> torch.Tensor:
+    """A workspace for pa_decode (allocated through torch; contents irrelevant)."""
+    return torch.empty(decode_workspace_bytes(num_seqs, num_heads, head_dim),
+                       dtype=torch.uint8, device=device)
+
+
 def _decode_common(k_pool, v_pool, q, block_tables, context_lens):
     cache = make_cache(k_pool, v_pool)
     _require(q.dim() == 3 and q.is_contiguous() and q.dtype == k_pool.dtype and
@@ -171,9 +178,8 @@ def pa_decode(k_pool, v_pool, q, block_tables, context_lens, scale: float, out, 
               stream=None) -> None:
     """Decode attention into out [num_seqs][num_heads][head_dim].
 
-    ``workspace`` (a uint8 device tensor of at least decode_workspace_bytes())
-    enables the balanced split of the batch; None walks each sequence in one
-    workgroup.
+    ``workspace`` (from decode_workspace()) enables the balanced split of the
+    batch; None walks each sequence in one workgroup.
     """
     cache = _decode_common(k_pool, v_pool, q, block_tables, context_lens)
     num_seqs, num_heads = q.shape[0], q.shape[1]

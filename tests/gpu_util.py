@@ -73,8 +73,7 @@ def run_decode(t: dict, w: W.Workload, mode="balanced", out_f32: bool = False,
     if mode in ("balanced", "single"):
         ws = None
         if mode == "balanced":
-            nbytes = lib.decode_workspace_bytes(w.num_seqs, w.num_heads, w.head_dim)
-            ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")  # garbage is fine
+            ws = lib.decode_workspace(w.num_seqs, w.num_heads, w.head_dim)
         lib.pa_decode(t["k_pool"], t["v_pool"], t["q"], t["block_tables"], t["context_lens"],
                       scale, out, workspace=ws)
     else:

@@ -255,8 +255,7 @@ def test_block_size_16_and_32_agree():
         if mode == "single":
             lib.pa_decode(tk, tv, q, tt, lens_t, scale, out)
         elif mode == "balanced":
-            ws = torch.empty(lib.decode_workspace_bytes(8, 32, 128), dtype=torch.uint8,
-                             device="cuda")
+            ws = lib.decode_workspace(8, 32, 128)
             lib.pa_decode(tk, tv, q, tt, lens_t, scale, out, workspace=ws)
         else:
             mp = max_parts_for(w16, mode)
@@ -290,3 +289,23 @@ def test_ranges_longer_than_64_blocks():
         out, _ = run_decode(t, w, mode, out_f32=True)
         torch.cuda.synchronize()
         assert max_abs_err(out, ref) <= 1e-5, mode
+
+
+def test_workspace_is_reusable_scratch():
+    """One workspace serves call after call and batches of different sizes;
+    whatever it holds beforehand does not matter."""
+    ws = lib.decode_workspace(256, 32, 128)
+    for k, n in ((2, 16), (3, 48), (2, 16)):
+        w = W.make_config(k, num_seqs=n, dtype="f32")
+        ref = oracle.decode(w.q, *oracle.kv_append(w.k_pool, w.v_pool, w.k_new, w.v_new,
+                                                   w.slot_mapping),
+                            w.block_tables, w.context_lens, 1 / math.sqrt(128), "f32")
+        t = upload(w)
+        run_writes(t)
+        for fill in (0x00, 0xFF, 0x7F):
+            ws.fill_(fill)
+            out = torch.empty((n, 32, 128), dtype=torch.float32, device="cuda")
+            lib.pa_decode(t["k_pool"], t["v_pool"], t["q"], t["block_tables"],
+                          t["context_lens"], 1 / math.sqrt(128), out, workspace=ws)
+            torch.cuda.synchronize()
+            assert max_abs_err(out, ref) <= 1e-5, (k, n, fill)
