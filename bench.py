@@ -2,16 +2,20 @@
 
 A step is the whole hot path over one batch: copy-on-write block copies (when
 the workload has any), the append of every sequence's new K/V through the slot
-mapping, decode attention (split-KV), and the log-sum-exp merge.  The default
-workload is the Llama-3.1-8B-class batch (32 query / 8 KV heads, head_dim 128,
-bf16, 16-token blocks, 64 sequences with context lengths uniform in
-[128, 4096]).
+mapping, decode attention, and the log-sum-exp merge of split sequences.  The
+default workload is the Llama-3.1-8B-class batch (32 query / 8 KV heads,
+head_dim 128, bf16, 16-token blocks, 64 sequences with context lengths uniform
+in [128, 4096]).
 
 Inputs are resident in HBM before timing starts.  The step cycles through
 ``--rotate`` independent copies of the KV pools, so each step reads a cache
 that at least (rotate-1) other caches' worth of traffic has passed since it was
 last touched - more than the 256 MB Infinity Cache and the L2s hold - the way a
 model's layers each read their own cache once per step.
+
+Two timed regions, each bracketed by HIP events on the launch stream with no
+event inside: ``--steps`` whole steps (``value``, ``ms_per_step``), then
+``--steps`` decode launches back to back (``decode_us`` and the roofline).
 
 Prints one JSON line.  ``value`` is the KV bytes the step's decode must read
 divided by the step time (GB/s).
@@ -88,6 +92,120 @@ def cpu_baseline(w: W.Workload, budget_s: float) -> dict:
             "seqs_per_s": round(done / dt, 3)}
 
 
+KERNEL_SOURCES = ("pa_decode_kernel.h", "pa_decode.hip", "pa_decode_bf16.hip", "pa_decode_f32.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+CAL_BLOCKS = 4096  # calibration copy: blocks [0, 2048) -> [2048, 4096) of a scratch pool pair
+
+
+def kernel_digest() -> str:
+    """Digest of the decode kernels' sources: traffic figures taken from
+    counters apply only while it is unchanged."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_93_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(workload: str, mode: str) -> str:
+    return os.path.join(PROFILES, f"traffic_decode_{workload}_{mode}.md")
+
+
+def read_traffic(workload: str, mode: str):
+    """HBM bytes per decode launch from the counter summary, or None when
+    there is none or the kernels changed since it was taken."""
+    path = traffic_path(workload, mode)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_digest") != kernel_digest():
+        return None
+    return int(fields["hbm_bytes_per_launch"])
+
+
+def pmc_summary(fetch_dir: str, write_dir: str, workload: str, block_bytes: int, mode: str,
+                command: str) -> str:
+    """Summarise two rocprofv3 --pmc runs of ``--pmc-pass`` (FETCH_SIZE, then
+    WRITE_SIZE) into profiles/traffic_decode_<workload>_<mode>.md.
+
+    The calibration copy moves a known number of bytes each way; the ratio of
+    those bytes to the counter's reading for it scales the decode kernels'
+    readings to bytes."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def per_kernel(d, counter):
+        vals = defaultdict(list)
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for row in csv.DictReader(open(f)):
+                if row["Counter_Name"] != counter:
+                    continue
+                name = row["Kernel_Name"]
+                key = next((k for k in ("decode_kernel", "merge_kernel", "reduce_kernel",
+                                        "copy_kernel") if k in name), None)
+                if key:
+                    vals[key].append(float(row["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    cal_bytes = 2 * (CAL_BLOCKS // 2) * block_bytes
+    mean = lambda v: sum(v) / len(v)
+    f_factor = cal_bytes / (mean(fetch["copy_kernel"]) * 1024)
+    w_factor = cal_bytes / (mean(write["copy_kernel"]) * 1024)
+    kernels = [k for k in ("decode_kernel", "merge_kernel", "reduce_kernel") if k in fetch]
+    rows, total = [], 0.0
+    for k in kernels:
+        fb = mean(fetch[k]) * 1024 * f_factor
+        wb = mean(write[k]) * 1024 * w_factor
+        total += fb + wb
+        rows.append(f"| {k} | {len(fetch[k])} | {mean(fetch[k]):.1f} | {fb / 1e6:.2f} | "
+                    f"{mean(write[k]):.1f} | {wb / 1e6:.2f} |")
+    text = "\n".join([
+        f"# HBM traffic of one decode launch: {workload}, mode {mode}",
+        "",
+        "Two rocprofv3 counter runs of the same program (`bench.py --pmc-pass`), one per counter:",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        f"Calibration: the copy kernel moves {cal_bytes} bytes each way "
+        f"({CAL_BLOCKS // 2} blocks, K and V pools); it read FETCH_SIZE "
+        f"{mean(fetch['copy_kernel']):.1f} KiB and WRITE_SIZE {mean(write['copy_kernel']):.1f} KiB "
+        f"per dispatch, so FETCH_SIZE is scaled by {f_factor:.4f} and WRITE_SIZE by {w_factor:.4f}.",
+        "",
+        "| kernel | dispatches | FETCH_SIZE KiB | read MB (scaled) | WRITE_SIZE KiB | written MB (scaled) |",
+        "|---|---|---|---|---|---|",
+        *rows,
+        "",
+        f"- hbm_bytes_per_launch: {int(round(total))}",
+        f"- fetch_factor: {f_factor:.4f}",
+        f"- write_factor: {w_factor:.4f}",
+        f"- kernel_digest: `{kernel_digest()}`",
+        "",
+    ])
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(traffic_path(workload, mode), "w") as f:
+        f.write(text)
+    return text
+
+
+def workload_shape(k: int, block_size=None):
+    """(name, bytes of one block of one pool) of workload k, as make_config names it."""
+    c = W.CONFIGS[k]
+    bs = int(block_size or c["block_size"])
+    name = c["name"] + ("" if bs == c["block_size"] else f"_bs{bs}")
+    return name, c["num_kv_heads"] * bs * c["head_dim"] * W.element_bytes(c["dtype"])
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,7 +218,18 @@ def main() -> int:
     ap.add_argument("--rotate", type=int, default=3, help="independent copies of the KV pools")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for cpu_baseline (0 = skip)")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="run the calibration copy, then --steps decode launches, and exit "
+                         "(the program to run under rocprofv3 --pmc)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic summary from two --pmc-pass counter runs")
+    ap.add_argument("--pmc-command", default="", help="command line recorded in the summary")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        name, block_bytes = workload_shape(args.workload, args.block_size)
+        print(pmc_summary(*args.pmc_summary, name, block_bytes, args.mode, args.pmc_command))
+        return 0
 
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; "
@@ -138,44 +267,66 @@ def main() -> int:
     if mode == "balanced":
         ws = lib.decode_workspace(w.num_seqs, w.num_heads, w.head_dim)
 
-    def step(r, ev=None):
+    def decode(r):
         kp, vp = pools[r]
-        if shared["pairs"].numel():
-            lib.pa_copy_blocks(kp, vp, shared["pairs"])
-        lib.pa_kv_append(kp, vp, shared["k_new"], shared["v_new"], shared["slots"])
-        if ev is not None:
-            ev[0].record()
         if psize:
             lib.pa_decode_partitions(kp, vp, shared["q"], shared["tables"], shared["lens"],
                                      scale, psize, po, pm, ps)
-            if ev is not None:
-                ev[1].record()
             lib.pa_splitkv_reduce(po, pm, ps, shared["lens"], psize, out)
         else:
             lib.pa_decode(kp, vp, shared["q"], shared["tables"], shared["lens"], scale, out,
                           workspace=ws)
-            if ev is not None:
-                ev[1].record()
+
+    def step(r):
+        kp, vp = pools[r]
+        if shared["pairs"].numel():
+            lib.pa_copy_blocks(kp, vp, shared["pairs"])
+        lib.pa_kv_append(kp, vp, shared["k_new"], shared["v_new"], shared["slots"])
+        decode(r)
+
+    def timed(fn, n):
+        """Mean milliseconds per call of fn over n back-to-back calls, from HIP
+        events recorded on the stream the kernels are launched on (torch's
+        current stream) before the first and after the last call."""
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(n):
+            fn(i % args.rotate)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / n
+
+    if args.pmc_pass:
+        # a plain copy of known size, then the decode launches being measured
+        blk = tuple(k0.shape[1:])
+        ck = torch.zeros((CAL_BLOCKS, *blk), dtype=k0.dtype, device="cuda")
+        cv = torch.zeros_like(ck)
+        half = CAL_BLOCKS // 2
+        cal_pairs = torch.stack([torch.arange(half), torch.arange(half) + half], 1).cuda()
+        for i in range(args.warmup):
+            decode(i % args.rotate)
+        lib.pa_copy_blocks(ck, cv, cal_pairs)
+        for i in range(args.steps):
+            decode(i % args.rotate)
+        torch.cuda.synchronize()
+        print(f"# pmc pass done: 1 calibration copy, {args.warmup + args.steps} decode launches",
+              file=sys.stderr, flush=True)
+        return 0
 
     for i in range(args.warmup):
         step(i % args.rotate)
-    torch.cuda.synchronize()
+    # timed region 1: whole steps (value, ms_per_step)
+    ms_step = timed(step, args.steps)
+    # timed region 2: the decode launches alone, back to back (roofline)
+    for i in range(args.warmup):
+        decode(i % args.rotate)
+    dec_avg = timed(decode, args.steps)
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(args.steps):
-        step(i % args.rotate, evs[i])
-    stop.record()
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / args.steps
-    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    dec_avg = float(dec_ms.mean())
-
+    kernels = ("decode_kernel + merge_kernel" if mode == "balanced" else
+               "decode_kernel" if mode == "single" else "decode_kernel + reduce_kernel")
     kv_gbps_step = nbytes["kv"] / (ms_step * 1e-3) / 1e9
-    decode_bytes = nbytes["kv"] + nbytes["q"] + nbytes["tables"] + nbytes["lens"]
+    decode_bytes = nbytes["kv"] + nbytes["q"] + nbytes["out"] + nbytes["tables"] + nbytes["lens"]
     achieved = decode_bytes / (dec_avg * 1e-3) / 1e9
     result = {
         "metric": "paged decode attention KV GB/s (% of HBM peak) + seqs/s, 8B-class batch 64",
@@ -199,13 +350,12 @@ def main() -> int:
         "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "hbm_peak_frac_step": round(kv_gbps_step / HBM_PEAK_GBPS, 4),
         "kv_bytes": nbytes["kv"],
-        "decode_us": {"mean": round(dec_avg * 1e3, 2),
-                      "p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
-                      "p50": round(float(np.percentile(dec_ms, 50)) * 1e3, 2),
-                      "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2)},
-        "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": round(achieved, 1),
+        "decode_us": round(dec_avg * 1e3, 2),
+        "kv_gbps_decode": round(nbytes["kv"] / (dec_avg * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "kernel": kernels, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": read_traffic(w.name, str(mode)),
                      "algorithmic_bytes_per_launch": decode_bytes},
     }
     if args.cpu_budget > 0:

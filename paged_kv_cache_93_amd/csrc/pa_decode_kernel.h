@@ -12,7 +12,9 @@
 // * A workgroup has one wave per KV head of a head group (up to 8).  All its
 //   waves walk the same blocks, so the rows of all heads of a block - one
 //   contiguous run in each pool - are read at about the same time.  The waves
-//   never synchronise after the preamble; each owns its head end to end.
+//   meet at no barrier after the preamble; each owns its head end to end and
+//   only publishes its progress, so that the two waves sharing a SIMD keep
+//   pace (the one behind runs at raised issue priority).
 // * Work unit = one (sequence, block).  Three ways to hand units out:
 //   single pass (a workgroup per sequence), fixed partitions (a workgroup per
 //   (sequence, partition), writing split-KV partials), and balanced (a fixed
@@ -20,20 +22,23 @@
 //   workgroup's range holds whole sequences and pieces of sequences; whole
 //   ones write the output, pieces write partials merged by merge_kernel).
 // * Rows are loaded in 16-byte chunks with non-temporal loads (the cache is
-//   streamed once): lane = r*LPR + c holds chunk c of rows r, r+RPI, ..., so
-//   one load instruction covers RPI whole rows (1 KiB contiguous).
-// * q.k: each lane dots its chunk against the same chunk of each query head
-//   (bf16 pairs through v_dot2 with f32 accumulation), then the LPR lanes of a
-//   row add up their partial sums with DPP row rotations; every lane of the
-//   row ends with the identical score.
-// * Running softmax per row group (lanes with equal r see rows r, r+RPI, ...):
-//   no cross-row traffic inside the loop; row groups are merged once per
-//   piece with the log-sum-exp rule.  Scores are kept in log2 units
-//   (s*scale*log2 e), so weights are exp2(s - m) and the maximum gets exactly 1.
-// * Block-table entries of up to 64 units are fetched with one vector load
-//   (one per lane) and handed out with v_readlane, so each is read once.
-// * K/V tiles sit in a ring of PF+1 register buffers: the loads of the next
-//   PF tiles are in flight while the current tile is scored and accumulated.
+//   streamed once); one load instruction covers 1 KiB of contiguous rows.
+// * q.k, bf16 with 128-dim heads: a 16-row K tile goes through LDS into the
+//   MFMA A layout and four v_mfma_f32_16x16x32_bf16 score it against the G
+//   query heads (the B operand; columns past G are ignored).  Other cases:
+//   each lane dots its 16-byte chunk against the same chunk of each query
+//   head (v_dot2 for bf16 pairs, f32 accumulation) and the lanes of a row add
+//   up their partial sums with DPP row rotations.
+// * Running softmax in log2 units (s*scale*log2 e), so weights are exp2(s - m)
+//   and the maximum gets exactly 1; the V rows are accumulated on the VALU in
+//   f32.  Row groups (lanes that see the same rows) keep their own running
+//   state and are merged once per piece with the log-sum-exp rule.
+// * The workgroup's units are walked as one stream: a ring of PF+1 register
+//   tiles keeps the next PF tiles in flight while the current one is scored,
+//   across piece boundaries too.  Block-table entries, context lengths and
+//   block indices of 64 units at a time are fetched with one vector load per
+//   lane (one window ahead) and handed out with v_readlane, so each table
+//   entry is read once.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -207,6 +212,8 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   // Units are (sequence, block) pairs.  In single and partition modes they
   // all belong to one sequence `fixed_seq` and unit index = block index.
   extern __shared__ int32_t s_prefix[];
+  __shared__ int32_t s_prog[8];  // tiles done by each wave (issue pacing)
+  if (threadIdx.x < 8) s_prog[threadIdx.x] = 0;
   int fixed_seq = -1;
   int64_t ubeg, uend;
   int64_t total_units = 0, num_groups = 0;
@@ -248,6 +255,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     ubeg = blockIdx.x < num_groups ? int64_t(blockIdx.x) * total_units / num_groups : 0;
     uend = blockIdx.x < num_groups ? int64_t(blockIdx.x + 1) * total_units / num_groups : 0;
   } else {
+    __syncthreads();  // s_prog
     fixed_seq = a.mode == kModeSingle ? blockIdx.x : blockIdx.z;
     int len = a.context_lens[fixed_seq];
     len = len < 0 ? 0 : (len > max_tokens ? max_tokens : len);
@@ -300,10 +308,11 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   float m[G], l[G], acc[G][VEC];
   float mf_m = kNegInf, mf_l = 0.f;
   u32x4 qc[MF ? 1 : G];  // VALU path: chunk c of each head's query
-  u32x4 qf[MF ? 4 : 1];  // MFMA path: B operands (Q^T slices of 32 dims)
+  u32x4 qf[1];           // placeholder for load_q's unused MFMA operand
 
-  // Emit the finished piece (blocks j_first..j_last) of sequence `seq`.
-  auto emit = [&](int seq, int j_first, int j_last, int len) {
+  // Emit the finished piece of sequence `seq`: the final output when the piece
+  // is the whole sequence, else a partial row.
+  auto emit = [&](int seq, bool whole) {
     if constexpr (MF) {
       // hand each row group's (m, l) of every head to all lanes of the group
       if ((lane & 15) < G) {
@@ -339,9 +348,6 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
       l[h] = lw;
     }
     if (r != 0) return;
-    const int nblk = (len + BS - 1) / BS;
-    const bool whole = a.mode == kModeSingle ||
-                       (a.mode == kModeBalanced && j_first == 0 && j_last == nblk - 1);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float inv = l[h] > 0.f ? 1.f / l[h] : 0.f;
@@ -378,228 +384,329 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     }
   };
 
-  // ---- pieces: maximal runs of the range's units that share a sequence -------
-  // The steady-state tile loop issues the same loads every iteration (no
-  // load sits behind a branch), so the compiler's wait before scoring a tile
-  // leaves the later tiles' loads in flight.  Prefetches past the end of a
-  // chunk, and tiles whose table entry is out of range, read block 0 instead
-  // (their data is never used).
-  for (int64_t u = ubeg; u < uend;) {
-    int seq, j0;
-    int64_t pend;
+  // ---- the walk: one ring of tiles over the whole unit range -----------------
+  // Units are taken in order; a piece is a maximal run of them that shares a
+  // sequence.  The ring of register tiles runs across piece boundaries: the
+  // next piece's first tiles, its query and the next 64 block-table entries
+  // are in flight before the current piece ends.  The steady-state loop issues
+  // the same loads every iteration (no tile load sits behind a branch), so the
+  // compiler's wait before scoring a tile leaves the later tiles' loads in
+  // flight; prefetches past the range, and tiles whose table entry is out of
+  // range, read block 0 instead (their data is never used).
+  if (ubeg >= uend) return;  // balanced mode: workgroups past the unit count
+  const int ntiles = int(uend - ubeg) * TPB;
+
+  // Sequence holding unit uu (balanced mode): s_prefix[seq] <= uu < s_prefix[seq + 1].
+  auto seq_of = [&](int64_t uu) {
+    int lo = 0, hi = a.num_seqs;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_prefix[mid] <= uu) lo = mid; else hi = mid;
+    }
+    return lo;
+  };
+
+  // A window describes 64 consecutive units; lane k holds, for unit
+  // cbase + k, its sequence (sk), its block index in the sequence (jk), the
+  // raw table entry (ek) and the sequence's raw context length (lk).  Lanes
+  // past the range repeat the range's last unit, so every lane loads and the
+  // loads write the window's registers directly; entries and lengths are
+  // checked where they are used.
+  struct Window {
+    int ek, lk, jk, sk;
+  };
+  auto fetch_window = [&](int64_t cbase) {
+    const int64_t uu = min(cbase + lane, uend - 1);
+    Window w;
+    if (fixed_seq >= 0) {
+      w.sk = fixed_seq;
+      w.jk = int(uu);
+    } else {
+      w.sk = seq_of(uu);
+      w.jk = int(uu - s_prefix[w.sk]);
+    }
+    w.ek = a.block_tables[size_t(w.sk) * a.max_blocks + w.jk];
+    w.lk = a.context_lens[w.sk];
+    return w;
+  };
+
+  // Query registers of sequence sq (MFMA path: lane 16g + h holds head h's
+  // dims [32mm + 8g, 32mm + 8g + 8) of MFMA mm, lanes with h >= G a copy of a
+  // real head whose score column is never used; VALU path: chunk c of each
+  // head).  Every lane loads, so the registers are written by the loads alone.
+  auto load_q = [&](int sq, u32x4(&dqc)[MF ? 1 : G], u32x4(&dqf)[MF ? 4 : 1]) {
+    const u32x4* qrow =
+        reinterpret_cast<const u32x4*>(a.q + (size_t(sq) * a.num_heads + head0) * D * EB);
+    if constexpr (MF) {
+      const int h = (lane & 15) % G;
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) dqf[mm] = qrow[h * LPR + 4 * mm + (lane >> 4)];
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h) dqc[h] = qrow[h * LPR + c];
+    }
+  };
+
+  auto reset_state = [&]() {
+    mf_m = kNegInf;
+    mf_l = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = kNegInf;
+      l[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[h][e] = 0.f;
+    }
+  };
+
+  // current piece: units [pstart, pend) of sequence seq; `whole` when it is
+  // all of the sequence (balanced mode)
+  int seq;
+  int64_t pstart, pend;
+  bool whole;
+  auto start_piece = [&](int64_t uu) {
     if (fixed_seq >= 0) {
       seq = fixed_seq;
-      j0 = int(u);
       pend = uend;
+      whole = a.mode == kModeSingle;
     } else {
-      int lo = 0, hi = a.num_seqs;  // s_prefix[lo] <= u < s_prefix[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_prefix[mid] <= u) lo = mid; else hi = mid;
-      }
-      seq = __builtin_amdgcn_readfirstlane(lo);
-      j0 = int(u - s_prefix[seq]);
-      pend = min(uend, int64_t(s_prefix[seq + 1]));
+      seq = __builtin_amdgcn_readfirstlane(seq_of(uu));
+      const int64_t first = s_prefix[seq], last = s_prefix[seq + 1];
+      pend = min(uend, last);
+      whole = uu == first && pend == last;
     }
-    int len = a.context_lens[seq];
-    len = len < 0 ? 0 : (len > max_tokens ? max_tokens : len);
-    const int32_t* trow = a.block_tables + size_t(seq) * a.max_blocks;
+    pstart = uu;
+  };
 
-    {
-      const u32x4* qrow = reinterpret_cast<const u32x4*>(
-          a.q + (size_t(seq) * a.num_heads + head0) * D * EB);
-      if constexpr (MF) {
-        // lane 16g + h: head h's dims [32mm + 8g, 32mm + 8g + 8) of MFMA mm
-        const int h = lane & 15;
-#pragma unroll
-        for (int mm = 0; mm < 4; ++mm)
-          qf[mm] = h < G ? qrow[h * LPR + 4 * mm + (lane >> 4)] : u32x4{0, 0, 0, 0};
-        mf_m = kNegInf;
-        mf_l = 0.f;
+  // Windows of units [cbase, +64) and [+64, +128); tiles at most PF ahead of
+  // the current one fall in one of them.
+  int64_t cbase = ubeg;
+  Window w0 = fetch_window(cbase);
+  Window w1 = fetch_window(cbase + 64);
+  start_piece(ubeg);
+  // VALU path: the current piece's query and the next piece's, swapped at a
+  // piece boundary.  (The MFMA path carries the query in the tile ring.)
+  u32x4 qc_next[MF ? 1 : G];
+  if constexpr (!MF) {
+    load_q(seq, qc, qf);
+    load_q(pend < uend ? __builtin_amdgcn_readfirstlane(seq_of(pend)) : seq, qc_next, qf);
+  }
+  reset_state();
+
+  // Loads tile t into (kr, vr) and, on the MFMA path, the query of its
+  // sequence into qr, so a tile always arrives with the query it is scored
+  // against and a piece boundary needs no query load.
+  auto load_tile = [&](u32x4(&kr)[NI], u32x4(&vr)[NI], u32x4(&qr)[MF ? 4 : 1], int t) {
+    int phys = -1, sq = 0;
+    size_t off = 0;
+    if (t < ntiles) {
+      const int idx = int(ubeg + t / TPB - cbase);  // < 128: at most PF tiles ahead
+      if (idx < 64) {
+        phys = __builtin_amdgcn_readlane(w0.ek, idx);
+        sq = __builtin_amdgcn_readlane(w0.sk, idx);
       } else {
+        phys = __builtin_amdgcn_readlane(w1.ek, idx - 64);
+        sq = __builtin_amdgcn_readlane(w1.sk, idx - 64);
+      }
+      off = size_t(t % TPB) * (TR * D * EB);
+    }
+    if constexpr (MF) {
+      u32x4 unused[1];
+      load_q(sq, unused, qr);
+    }
+    if (phys < 0 || int64_t(phys) >= a.num_blocks) {
+      phys = 0;
+      off = 0;
+    }
+    off += size_t(phys) * block_bytes;
+    // VALU path: instruction i holds rows i*RPI + r.  MFMA path: rows 4r + i,
+    // so each row group sees 4 consecutive rows, as the MFMA result rows.
+    const int lo = MF ? r * 64 + c : lane;
+    constexpr int step = MF ? 16 : 64;
+    const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + off) + lo;
+    const u32x4* vp = reinterpret_cast<const u32x4*>(vbase + off) + lo;
 #pragma unroll
-        for (int h = 0; h < G; ++h) qc[h] = qrow[h * LPR + c];
+    for (int i = 0; i < NI; ++i) {
+      kr[i] = load16<NT>(kp + i * step);
+      vr[i] = load16<NT>(vp + i * step);
+    }
+  };
+
+  auto process_tile = [&](const u32x4(&kr)[NI], const u32x4(&vr)[NI],
+                          const u32x4(&qr)[MF ? 4 : 1], int t) {
+    const int idx = int(ubeg + t / TPB - cbase);
+    const int phys = __builtin_amdgcn_readlane(w0.ek, idx);
+    int len = __builtin_amdgcn_readlane(w0.lk, idx);
+    len = len < 0 ? 0 : (len > max_tokens ? max_tokens : len);
+    const int tok0 = __builtin_amdgcn_readlane(w0.jk, idx) * BS + (t % TPB) * TR;
+    const int nvalid = (phys < 0 || int64_t(phys) >= a.num_blocks) ? 0 : min(TR, len - tok0);
+    if (nvalid <= 0) return;
+    const bool partial = nvalid < TR;
+    if constexpr (MF) {
+      // K tile -> LDS, then read back transposed: lane 16g + t gets row t's
+      // dims [32mm + 8g, 32mm + 8g + 8) as the A operand of MFMA mm.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lds_k[(4 * r + i) * 17 + c] = kr[i];
+      __builtin_amdgcn_wave_barrier();
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) {
+        const u32x4 kf = lds_k[(lane & 15) * 17 + 4 * mm + (lane >> 4)];
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf),
+                                                     __builtin_bit_cast(bf16x8, qr[mm]),
+                                                     sc, 0, 0, 0);
+      }
+      // lane 16g + h: scores of rows 4g + v (v = 0..3), head h
+      const int g4 = 4 * (lane >> 4);
+      float sv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        sv[v] = sc[v] * cl2;
+        if (partial && g4 + v >= nvalid) sv[v] = kNegInf;
+      }
+      const float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      const float mnew = fmaxf(mf_m, mx);
+      const float base = (mnew == kNegInf) ? 0.f : mnew;
+      const float alpha = fast_exp2(mf_m - base);
+      float pv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) pv[v] = fast_exp2(sv[v] - base);
+      mf_l = fmaf(mf_l, alpha, (pv[0] + pv[1]) + (pv[2] + pv[3]));
+      mf_m = mnew;
+      const bool live = (lane & 15) < G;
+      if (live) {
+        float* dst = lds_p + ((lane >> 4) * G + (lane & 15)) * 4;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dst[v] = pv[v];
+        lds_a[(lane >> 4) * G + (lane & 15)] = alpha;
+      }
+      const bool rescale = __ballot(live && alpha != 1.f) != 0;
+      __builtin_amdgcn_wave_barrier();
+      // row group r reads its weights: rows 4r + i, every head
+      if (rescale) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          m[h] = kNegInf;
-          l[h] = 0.f;
+          const float al = lds_a[r * G + h];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[h][e] *= al;
         }
       }
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+      for (int i = 0; i < 4; ++i) {
+        float v[VEC];
+        unpack16<BF16>(vr[i], v);
+        if (partial && 4 * r + i >= nvalid) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[h][e] = 0.f;
-    }
-
-    for (int64_t c0 = u; c0 < pend; c0 += 64) {
-      const int n = int(min(int64_t(64), pend - c0));
-      const int jc = j0 + int(c0 - u);  // block index of the chunk's first unit
-      int pk = -1;                      // lane k: physical block of unit c0 + k
-      if (lane < n) {
-        const int e = trow[jc + lane];
-        pk = (e >= 0 && int64_t(e) < a.num_blocks) ? e : -1;
+          for (int e = 0; e < VEC; ++e) v[e] = 0.f;  // masked rows may hold NaN
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float ph = lds_p[(r * G + h) * 4 + i];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(ph, v[e], acc[h][e]);
+        }
       }
-      const int ntiles = n * TPB;
-
-      auto load_tile = [&](u32x4(&kr)[NI], u32x4(&vr)[NI], int t) {
-        const int tt = t < ntiles ? t : ntiles - 1;
-        int phys = __builtin_amdgcn_readlane(pk, tt / TPB);
-        size_t off = size_t(tt % TPB) * (TR * D * EB);
-        if (t >= ntiles || phys < 0) {
-          phys = 0;
-          off = 0;
-        }
-        off += size_t(phys) * block_bytes;
-        // VALU path: instruction i holds rows i*RPI + r.  MFMA path: rows 4r + i,
-        // so each row group sees 4 consecutive rows, as the MFMA result rows.
-        const int lo = MF ? r * 64 + c : lane;
-        constexpr int step = MF ? 16 : 64;
-        const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + off) + lo;
-        const u32x4* vp = reinterpret_cast<const u32x4*>(vbase + off) + lo;
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      float s[NI][G];
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          kr[i] = load16<NT>(kp + i * step);
-          vr[i] = load16<NT>(vp + i * step);
-        }
-      };
-
-      auto process_tile = [&](const u32x4(&kr)[NI], const u32x4(&vr)[NI], int t) {
-        const int ut = t / TPB;
-        const int sub = t % TPB;
-        const int phys = __builtin_amdgcn_readlane(pk, ut);
-        const int tok0 = (jc + ut) * BS + sub * TR;
-        const int nvalid = phys < 0 ? 0 : min(TR, len - tok0);
-        if (nvalid <= 0) return;
-        const bool partial = nvalid < TR;
-        if constexpr (MF) {
-          // K tile -> LDS, then read back transposed: lane 16g + t gets row t's
-          // dims [32mm + 8g, 32mm + 8g + 8) as the A operand of MFMA mm.
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) lds_k[(4 * r + i) * 17 + c] = kr[i];
-          __builtin_amdgcn_wave_barrier();
-          f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int mm = 0; mm < 4; ++mm) {
-            const u32x4 kf = lds_k[(lane & 15) * 17 + 4 * mm + (lane >> 4)];
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf),
-                                                         __builtin_bit_cast(bf16x8, qf[mm]),
-                                                         sc, 0, 0, 0);
-          }
-          // lane 16g + h: scores of rows 4g + v (v = 0..3), head h
-          const int g4 = 4 * (lane >> 4);
-          float sv[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            sv[v] = sc[v] * cl2;
-            if (partial && g4 + v >= nvalid) sv[v] = kNegInf;
-          }
-          const float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-          const float mnew = fmaxf(mf_m, mx);
-          const float base = (mnew == kNegInf) ? 0.f : mnew;
-          const float alpha = fast_exp2(mf_m - base);
-          float pv[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) pv[v] = fast_exp2(sv[v] - base);
-          mf_l = fmaf(mf_l, alpha, (pv[0] + pv[1]) + (pv[2] + pv[3]));
-          mf_m = mnew;
-          const bool live = (lane & 15) < G;
-          if (live) {
-            float* dst = lds_p + ((lane >> 4) * G + (lane & 15)) * 4;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) dst[v] = pv[v];
-            lds_a[(lane >> 4) * G + (lane & 15)] = alpha;
-          }
-          const bool rescale = __ballot(live && alpha != 1.f) != 0;
-          __builtin_amdgcn_wave_barrier();
-          // row group r reads its weights: rows 4r + i, every head
-          if (rescale) {
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-              const float al = lds_a[r * G + h];
-#pragma unroll
-              for (int e = 0; e < VEC; ++e) acc[h][e] *= al;
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float v[VEC];
-            unpack16<BF16>(vr[i], v);
-            if (partial && 4 * r + i >= nvalid) {
-#pragma unroll
-              for (int e = 0; e < VEC; ++e) v[e] = 0.f;  // masked rows may hold NaN
-            }
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-              const float ph = lds_p[(r * G + h) * 4 + i];
-#pragma unroll
-              for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(ph, v[e], acc[h][e]);
-            }
-          }
-          __builtin_amdgcn_wave_barrier();
-        } else {
-        float s[NI][G];
+        for (int h = 0; h < G; ++h)
+          s[i][h] = group_sum<LPR>(dot16<BF16>(0.f, qc[h], kr[i])) * cl2;
+      if (partial) {
 #pragma unroll
         for (int i = 0; i < NI; ++i)
+          if (i * RPI + r >= nvalid)
 #pragma unroll
-          for (int h = 0; h < G; ++h)
-            s[i][h] = group_sum<LPR>(dot16<BF16>(0.f, qc[h], kr[i])) * cl2;
-        if (partial) {
+            for (int h = 0; h < G; ++h) s[i][h] = kNegInf;
+      }
+      float p[NI][G];
 #pragma unroll
-          for (int i = 0; i < NI; ++i)
-            if (i * RPI + r >= nvalid)
+      for (int h = 0; h < G; ++h) {
+        float mx = s[0][h];
 #pragma unroll
-              for (int h = 0; h < G; ++h) s[i][h] = kNegInf;
-        }
-        float p[NI][G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float mx = s[0][h];
-#pragma unroll
-          for (int i = 1; i < NI; ++i) mx = fmaxf(mx, s[i][h]);
-          const float mnew = fmaxf(m[h], mx);
-          const float base = (mnew == kNegInf) ? 0.f : mnew;
-          const float alpha = fast_exp2(m[h] - base);
-          float ps = 0.f;
-#pragma unroll
-          for (int i = 0; i < NI; ++i) {
-            p[i][h] = fast_exp2(s[i][h] - base);
-            ps += p[i][h];
-          }
-          l[h] = fmaf(l[h], alpha, ps);
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[h][e] *= alpha;
-          m[h] = mnew;
-        }
+        for (int i = 1; i < NI; ++i) mx = fmaxf(mx, s[i][h]);
+        const float mnew = fmaxf(m[h], mx);
+        const float base = (mnew == kNegInf) ? 0.f : mnew;
+        const float alpha = fast_exp2(m[h] - base);
+        float ps = 0.f;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-          float v[VEC];
-          unpack16<BF16>(vr[i], v);
-          if (partial && i * RPI + r >= nvalid) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) v[e] = 0.f;  // masked rows may hold NaN
-          }
-#pragma unroll
-          for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(p[i][h], v[e], acc[h][e]);
+          p[i][h] = fast_exp2(s[i][h] - base);
+          ps += p[i][h];
         }
-        }
-      };
-
-      u32x4 kb[NB][NI], vb[NB][NI];
+        l[h] = fmaf(l[h], alpha, ps);
 #pragma unroll
-      for (int i = 0; i < PF; ++i) load_tile(kb[i], vb[i], i);
-      for (int t0 = 0; t0 < ntiles; t0 += NB) {
+        for (int e = 0; e < VEC; ++e) acc[h][e] *= alpha;
+        m[h] = mnew;
+      }
 #pragma unroll
-        for (int k = 0; k < NB; ++k) {
-          const int t = t0 + k;
-          load_tile(kb[(k + PF) % NB], vb[(k + PF) % NB], t + PF);
-          if (t < ntiles) process_tile(kb[k], vb[k], t);
+      for (int i = 0; i < NI; ++i) {
+        float v[VEC];
+        unpack16<BF16>(vr[i], v);
+        if (partial && i * RPI + r >= nvalid) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) v[e] = 0.f;  // masked rows may hold NaN
         }
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(p[i][h], v[e], acc[h][e]);
       }
     }
-    emit(seq, j0, j0 + int(pend - u) - 1, len);
-    u = pend;
+  };
+
+  // After the last tile of a unit: close the piece if the unit ended it, and
+  // move the table-entry window when the next unit starts a new chunk.
+  auto unit_done = [&](int64_t next) {
+    if (next == pend) {
+      emit(seq, whole);
+      if (next < uend) {
+        start_piece(next);
+        if constexpr (!MF) {
+#pragma unroll
+          for (int h = 0; h < G; ++h) qc[h] = qc_next[h];
+          load_q(pend < uend ? __builtin_amdgcn_readfirstlane(seq_of(pend)) : seq, qc_next, qf);
+        }
+        reset_state();
+      }
+    }
+    if (next == cbase + 64) {
+      cbase = next;
+      w0 = w1;
+      w1 = fetch_window(cbase + 64);
+    }
+  };
+
+  // Issue priority.  An 8-wave workgroup puts waves w and w^4 on one SIMD,
+  // where the older wave wins arbitration and would finish its (equal) share
+  // well before the younger one, leaving the workgroup waiting on the latter.
+  // After each tile a wave publishes its progress and runs at raised priority
+  // while it is not ahead of its partner.
+  auto pace = [&](int t) {
+    if (nwave != 8) return;
+    s_prog[wave] = t;
+    if (t > s_prog[wave ^ 4])
+      __builtin_amdgcn_s_setprio(0);
+    else
+      __builtin_amdgcn_s_setprio(2);
+  };
+
+  u32x4 kb[NB][NI], vb[NB][NI], qb[NB][MF ? 4 : 1];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) load_tile(kb[i], vb[i], qb[i], i);
+  for (int t0 = 0; t0 < ntiles; t0 += NB) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int t = t0 + k;
+      load_tile(kb[(k + PF) % NB], vb[(k + PF) % NB], qb[(k + PF) % NB], t + PF);
+      if (t < ntiles) {
+        process_tile(kb[k], vb[k], qb[k], t);
+        pace(t);
+        if (t % TPB == TPB - 1) unit_done(ubeg + t / TPB + 1);
+      }
+    }
   }
 }
 
@@ -614,70 +721,104 @@ struct MergeArgs {
 };
 
 // Merge the pieces of sequences split between workgroups (balanced mode) and
-// write zeros for empty sequences.  One wave per (sequence, query head).  The
-// work is three memory round trips: the split, the pieces' maxima and sums
-// (lane p reads piece p), and the pieces' output rows (read back to back).
+// write zeros for empty sequences.  One wave per (sequence, query head).
+// After one read of the split description, the pieces' maxima and sums (lane p
+// holds piece p) and their output rows (16-byte loads; LR lanes cover a row,
+// so one load instruction brings 64/LR pieces) are all in flight at once.
+// Pieces are taken 64 at a time with the running log-sum-exp rescale, and
+// their rows in batches of NBATCH load instructions.
 template <int D>
 __global__ void __launch_bounds__(64) merge_kernel(MergeArgs a) {
   using namespace dev;
-  constexpr int PER = D / 64;
+  constexpr int LR = D / 4;          // lanes per row
+  constexpr int PPI = 64 / LR;       // pieces per load instruction
+  constexpr int NBATCH = 8;          // load instructions per batch
+  constexpr int PB = PPI * NBATCH;   // pieces per batch
+  static_assert(64 % LR == 0 && 64 % PB == 0, "merge tiling");
   const int lane = threadIdx.x;
   const int head = blockIdx.x;
   const int seq = blockIdx.y;
+  const int sub = lane / LR;         // which piece of an instruction this lane reads
+  const int col = (lane % LR) * 4;   // its 4 dims
   const int64_t groups = a.info[0];
   const int64_t total = a.info[1];
   const int64_t u0 = a.info[2 + seq];
   const int64_t u1 = a.info[3 + seq];  // one past the sequence's last unit
-  const size_t orow = (size_t(seq) * a.num_heads + head) * D;
-  float accv[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) accv[e] = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (u1 > u0) {
     const int g0 = group_of_unit(u0, total, groups);
     const int g1 = group_of_unit(u1 - 1, total, groups);
     if (g0 == g1) return;  // one workgroup held the whole sequence and wrote it
     const int np = g1 - g0 + 1;
+    const size_t stride = size_t(a.num_heads) * D;  // next workgroup's row of this head
+    const float* rows = a.piece_out + ((size_t(g0) + seq) * a.num_heads + head) * D + col;
+    const size_t mrow0 = (size_t(g0) + seq) * a.num_heads + head;
     float big = kNegInf;
     for (int p0 = 0; p0 < np; p0 += 64) {
-      const int p = p0 + lane;
-      if (p < np) {
-        const size_t row = (size_t(g0 + p) + seq) * a.num_heads + head;
-        if (a.piece_sum[row] > 0.f) big = fmaxf(big, a.piece_max[row]);
+      const int cnt = min(64, np - p0);
+      float pm = kNegInf, ps = 0.f;
+      if (lane < cnt) {
+        const size_t row = mrow0 + size_t(p0 + lane) * a.num_heads;
+        ps = a.piece_sum[row];
+        pm = a.piece_max[row];
+      }
+      f32x4 v[NBATCH];
+#pragma unroll
+      for (int i = 0; i < NBATCH; ++i) {
+        const int p = i * PPI + sub;
+        v[i] = p < cnt ? *reinterpret_cast<const f32x4*>(rows + size_t(p0 + p) * stride)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      float cmax = ps > 0.f ? pm : kNegInf;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, off));
+      const float nb = fmaxf(big, cmax);
+      if (nb != big) {
+        const float f = big == kNegInf ? 0.f : fast_exp2(big - nb);
+        acc *= f;
+        wsum *= f;
+        big = nb;
+      }
+      const float w = ps > 0.f ? ps * fast_exp2(pm - big) : 0.f;
+      float ws = w;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) ws += __shfl_xor(ws, off);
+      wsum += ws;
+      for (int b0 = 0; b0 < cnt; b0 += PB) {
+        if (b0 > 0) {
+#pragma unroll
+          for (int i = 0; i < NBATCH; ++i) {
+            const int p = b0 + i * PPI + sub;
+            v[i] = p < cnt ? *reinterpret_cast<const f32x4*>(rows + size_t(p0 + p) * stride)
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NBATCH; ++i) {
+          const int p = b0 + i * PPI + sub;  // < 64; lanes past cnt hold w = 0
+          const float wp = __shfl(w, p);
+          acc += wp * v[i];
+        }
       }
     }
+    // add up the PPI pieces of each load instruction's lane groups
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) big = fmaxf(big, __shfl_xor(big, off));
-    for (int p0 = 0; p0 < np; p0 += 64) {
-      const int p = p0 + lane;
-      float w = 0.f;
-      if (p < np) {
-        const size_t row = (size_t(g0 + p) + seq) * a.num_heads + head;
-        const float s = a.piece_sum[row];
-        w = s > 0.f ? s * fast_exp2(a.piece_max[row] - big) : 0.f;
-      }
-      wsum += w;
-      const int cnt = np - p0 < 64 ? np - p0 : 64;
-      const float* rows = a.piece_out + ((size_t(g0 + p0) + seq) * a.num_heads + head) * D + lane;
-      const size_t stride = size_t(a.num_heads) * D;  // next workgroup's row of this head
-#pragma unroll 8
-      for (int j = 0; j < cnt; ++j) {
-        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+    for (int off = LR; off < 64; off <<= 1) {
 #pragma unroll
-        for (int e = 0; e < PER; ++e) accv[e] = fmaf(wj, rows[j * stride + e * 64], accv[e]);
-      }
+      for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], off);
     }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) wsum += __shfl_xor(wsum, off);
   }
+  if (lane >= LR) return;
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const float val = accv[e] * inv;
-    if (a.out_f32)
-      static_cast<float*>(a.out)[orow + e * 64 + lane] = val;
-    else
-      static_cast<uint16_t*>(a.out)[orow + e * 64 + lane] = uint16_t(to_bf16(val));
+  const size_t o = (size_t(seq) * a.num_heads + head) * D + col;
+  if (a.out_f32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = acc * inv;
+  } else {
+    uint16_t* dst = static_cast<uint16_t*>(a.out) + o;
+    const uint32_t lo = to_bf16(acc[0] * inv) | (to_bf16(acc[1] * inv) << 16);
+    const uint32_t hi = to_bf16(acc[2] * inv) | (to_bf16(acc[3] * inv) << 16);
+    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
   }
 }
 
