@@ -167,8 +167,12 @@ __device__ __forceinline__ int group_of_unit(int64_t u, int64_t total, int64_t g
 
 }  // namespace dev
 
+#ifndef PA_MFMA_SCORES
+#define PA_MFMA_SCORES 1  // 0: score every case on the VALU (for comparison)
+#endif
+
 // Scores on the matrix cores: bf16 caches with 128-dim heads.
-constexpr bool decode_uses_mfma(bool bf16, int d) { return bf16 && d == 128; }
+constexpr bool decode_uses_mfma(bool bf16, int d) { return PA_MFMA_SCORES && bf16 && d == 128; }
 
 // LDS bytes each wave of the MFMA path uses: a 16-row K tile padded to 17
 // chunks per row (conflict-free transposed reads), then the softmax weights
