@@ -10,10 +10,15 @@ passages each function follows.
 """
 
 from .paged_attention import (  # noqa: F401
+    E4M3_MAX,
     blocks_needed,
     copy_blocks,
     decode,
     decode_partitions,
+    e4m3_value,
+    fp8_encode,
+    fp8_quantize,
+    fp8_to_f64,
     gather_rows,
     kv_append,
     last_block_waste,

@@ -33,6 +33,9 @@ Storage conventions (shared with the caller only as array shapes):
   K and V live in two separate pools of that shape.
 * Values of dtype ``"f32"`` are ``numpy.float32`` arrays; values of dtype
   ``"bf16"`` are ``numpy.uint16`` arrays holding bfloat16 bit patterns.
+* An 8-bit cache (dtype ``"fp8"``) holds ``numpy.uint8`` E4M3 codes; stored
+  code c stands for e4m3(c) * scale, with one scale for the K pool and one for
+  the V pool.  Its queries and new tokens are bfloat16 bit patterns.
 * ``block_tables`` is ``[num_seqs][max_blocks]`` of int32; only the first
   ceil(L_i / block_size) entries of row i are ever read.
 * ``context_lens[i]`` = L_i counts every token sequence i attends to, including
@@ -65,6 +68,109 @@ def to_f64(values, dtype: str) -> np.ndarray:
         bits = np.asarray(values, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return bits.view(np.float32).astype(np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# ---------------------------------------------------------------------------
+# 8-bit E4M3 values (the fp8 KV cache)
+# ---------------------------------------------------------------------------
+#
+# The pages name an 8-bit KV cache only as a lever on top of paging: it halves
+# the bytes of every block ("PagedAttention" glossary page, section "What
+# paging costs") and relieves a full block pool ("How Paged Attention and
+# Continuous Batching Actually Work", section "What this means when you serve
+# a model").  They fix no format or scaling.  The format taken here is OCP
+# E4M3 ("FN": no infinities): 1 sign bit, 4 exponent
+# bits with bias 7, 3 mantissa bits; exponent field 0 holds the subnormals
+# m/8 * 2^-6; the all-ones pattern S.1111.111 is NaN; the largest finite
+# magnitude is 1.75 * 2^8 = 448.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code: int) -> float:
+    """Exact value of one E4M3 byte (NaN for S.1111.111)."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    exponent = (code >> 3) & 0xF
+    mantissa = code & 0x7
+    if exponent == 0xF and mantissa == 0x7:
+        return math.nan
+    if exponent == 0:
+        return sign * math.ldexp(mantissa, -9)  # (m/8) * 2^-6
+    return sign * math.ldexp(8 + mantissa, exponent - 10)  # (1 + m/8) * 2^(e-7)
+
+
+_E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def fp8_to_f64(codes) -> np.ndarray:
+    """Widen E4M3 codes to float64 (exact: every E4M3 value is a float64)."""
+    return _E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+# The 127 non-negative finite values, in code order 0x00..0x7E (increasing).
+_E4M3_MAGNITUDES = _E4M3_TABLE[:0x7F]
+
+
+def fp8_encode(values) -> np.ndarray:
+    """E4M3 codes of the given values: round to nearest, ties to the even code.
+
+    Magnitudes above 448 saturate to 448 (the format has no infinity; this
+    library clamps instead of producing NaN), NaN becomes S.1111.111, and the
+    sign bit follows the sign of the value (so -0.0 and negative values that
+    round to zero give 0x80).  Nearest is found by direct search over the 127
+    finite magnitudes; of two equally near neighbours the one whose code is
+    even (mantissa bit 0 clear) wins.
+    """
+    y = np.asarray(values, dtype=np.float64)
+    flat = y.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    for n, v in enumerate(flat):
+        sign = 0x80 if math.copysign(1.0, v) < 0 else 0
+        if math.isnan(v):
+            out[n] = sign | 0x7F
+            continue
+        a = abs(v)
+        if a >= E4M3_MAX:
+            out[n] = sign | 0x7E
+            continue
+        hi = int(np.searchsorted(_E4M3_MAGNITUDES, a, side="left"))  # first magnitude >= a
+        if _E4M3_MAGNITUDES[hi] == a:
+            code = hi
+        else:
+            lo = hi - 1
+            below, above = a - _E4M3_MAGNITUDES[lo], _E4M3_MAGNITUDES[hi] - a
+            if below < above:
+                code = lo
+            elif above < below:
+                code = hi
+            else:
+                code = lo if lo % 2 == 0 else hi
+        out[n] = sign | code
+    return out.reshape(y.shape)
+
+
+def fp8_quantize(bf16_bits, scale: float) -> np.ndarray:
+    """E4M3 codes stored for bfloat16 inputs with dequantisation scale ``scale``.
+
+    Each input x is widened exactly to binary32, divided by the scale in
+    binary32 (IEEE division, rounded to nearest), and the quotient is encoded
+    with :func:`fp8_encode`.
+    """
+    x32 = to_f64(bf16_bits, "bf16").astype(np.float32)
+    y32 = x32 / np.float32(scale)
+    return fp8_encode(y32.astype(np.float64))
+
+
+def _kv_f64(rows, dtype: str, scale: float) -> np.ndarray:
+    """Exact float64 values of stored K or V rows (E4M3 codes times the pool's scale)."""
+    if dtype == "fp8":
+        return fp8_to_f64(rows) * float(scale)
+    return to_f64(rows, dtype)
+
+
+def _q_dtype(dtype: str) -> str:
+    return "bf16" if dtype == "fp8" else dtype
 
 
 # ---------------------------------------------------------------------------
@@ -161,7 +267,7 @@ def _softmax_weighted_sum(scores: np.ndarray, values: np.ndarray):
 
 
 def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float,
-           dtype: str) -> np.ndarray:
+           dtype: str, k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """Decode attention of one query token per sequence over a paged KV cache.
 
     For sequence i and query head h (KV head g = h // G):
@@ -172,22 +278,26 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float,
     Executes Paged Attention"; the attended range K_{0:t} is that of
     "PagedAttention and continuous batching", section "Attention kernel
     modification".  A sequence with L_i = 0 gets an all-zero output (the pages
-    never produce one; decode always has the new token).
+    never produce one; decode always has the new token).  For an 8-bit cache
+    (``dtype="fp8"``) k_t and v_t are the stored codes' values times
+    ``k_scale`` / ``v_scale`` and q holds bfloat16 bit patterns.
 
     Returns float64 ``[num_seqs][num_heads][head_dim]``.
     """
     num_seqs, num_heads, head_dim, num_kv_heads, block_size = _check_shapes(
         q, k_pool, v_pool, block_tables, context_lens)
     group = num_heads // num_kv_heads
-    q64 = to_f64(q, dtype)
+    q64 = to_f64(q, _q_dtype(dtype))
     out = np.zeros((num_seqs, num_heads, head_dim), dtype=np.float64)
     for i in range(num_seqs):
         length = int(context_lens[i])
         if length == 0:
             continue
         for g in range(num_kv_heads):
-            keys = to_f64(gather_rows(k_pool, block_tables[i], length, block_size, g), dtype)
-            values = to_f64(gather_rows(v_pool, block_tables[i], length, block_size, g), dtype)
+            keys = _kv_f64(gather_rows(k_pool, block_tables[i], length, block_size, g),
+                           dtype, k_scale)
+            values = _kv_f64(gather_rows(v_pool, block_tables[i], length, block_size, g),
+                             dtype, v_scale)
             for h in range(g * group, (g + 1) * group):
                 scores = scale * (keys @ q64[i, h])
                 out[i, h], _, _ = _softmax_weighted_sum(scores, values)
@@ -195,7 +305,8 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float,
 
 
 def decode_partitions(q, k_pool, v_pool, block_tables, context_lens, scale: float,
-                      dtype: str, partition_size: int, max_parts: int | None = None):
+                      dtype: str, partition_size: int, max_parts: int | None = None,
+                      k_scale: float = 1.0, v_scale: float = 1.0):
     """Per-partition attention results for split-KV decode.
 
     The pages never split a sequence's context; this follows the split-KV
@@ -217,7 +328,7 @@ def decode_partitions(q, k_pool, v_pool, block_tables, context_lens, scale: floa
     group = num_heads // num_kv_heads
     if max_parts is None:
         max_parts = max([blocks_needed(int(n), partition_size) for n in context_lens] + [1])
-    q64 = to_f64(q, dtype)
+    q64 = to_f64(q, _q_dtype(dtype))
     part_out = np.zeros((num_seqs, num_heads, max_parts, head_dim), dtype=np.float64)
     part_max = np.full((num_seqs, num_heads, max_parts), -np.inf, dtype=np.float64)
     part_sum = np.zeros((num_seqs, num_heads, max_parts), dtype=np.float64)
@@ -227,8 +338,10 @@ def decode_partitions(q, k_pool, v_pool, block_tables, context_lens, scale: floa
         if nparts > max_parts:
             raise ValueError("max_parts too small for context_lens")
         for g in range(num_kv_heads):
-            keys = to_f64(gather_rows(k_pool, block_tables[i], length, block_size, g), dtype)
-            values = to_f64(gather_rows(v_pool, block_tables[i], length, block_size, g), dtype)
+            keys = _kv_f64(gather_rows(k_pool, block_tables[i], length, block_size, g),
+                           dtype, k_scale)
+            values = _kv_f64(gather_rows(v_pool, block_tables[i], length, block_size, g),
+                             dtype, v_scale)
             for h in range(g * group, (g + 1) * group):
                 scores = scale * (keys @ q64[i, h])
                 for p in range(nparts):
@@ -279,7 +392,7 @@ def splitkv_merge(part_out, part_max, part_sum, context_lens, partition_size: in
 # KV writes (byte-exact)
 # ---------------------------------------------------------------------------
 
-def kv_append(k_pool, v_pool, k_new, v_new, slot_mapping):
+def kv_append(k_pool, v_pool, k_new, v_new, slot_mapping, fp8_scales=None):
     """Pools after writing each new token's K/V rows at its slot.
 
     "How Paged Attention and Continuous Batching Actually Work", section "One
@@ -290,9 +403,16 @@ def kv_append(k_pool, v_pool, k_new, v_new, slot_mapping):
     ``k_new[n]`` / ``v_new[n]`` (all KV heads), bit for bit; a negative slot
     means "no write".  Every other byte stays as it was.  Two tokens with the
     same slot are a caller error.
+
+    With ``fp8_scales = (k_scale, v_scale)`` the pools are an 8-bit cache and
+    k_new / v_new hold bfloat16 bit patterns: each row is stored as
+    :func:`fp8_quantize` of it with the pool's scale instead of a bit copy.
     """
     k_out = np.array(k_pool, copy=True)
     v_out = np.array(v_pool, copy=True)
+    if fp8_scales is not None:
+        k_new = fp8_quantize(k_new, fp8_scales[0])
+        v_new = fp8_quantize(v_new, fp8_scales[1])
     block_size = k_pool.shape[2]
     slots = [int(s) for s in slot_mapping]
     live = [s for s in slots if s >= 0]

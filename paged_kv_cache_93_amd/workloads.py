@@ -17,7 +17,10 @@ and Continuous Batching Actually Work", section "One step, end to end".
 
 Storage layout of every pool: ``[num_blocks][num_kv_heads][block_size][head_dim]``;
 bf16 values are carried as ``numpy.uint16`` bit patterns, f32 values as
-``numpy.float32``.  Slots a sequence does not own (unallocated blocks, the
+``numpy.float32``.  An 8-bit (``"fp8"``) workload stores E4M3 codes
+(``numpy.uint8``) with dequantisation scale ``FP8_SCALE`` for both pools; its
+queries and new tokens are bf16.  The codes come from PyTorch's float8_e4m3fn
+cast of the scaled draws (a library conversion, not this library's).  Slots a sequence does not own (unallocated blocks, the
 unfilled tail of a last block, and this step's new-token slots before the
 append) hold NaN, so any read outside the attended range shows up in results.
 
@@ -34,6 +37,10 @@ import numpy as np
 
 NAN_F32_BITS = np.uint32(0x7FC00000)
 NAN_BF16_BITS = np.uint16(0x7FC0)
+NAN_FP8_BITS = np.uint8(0x7F)  # E4M3 NaN
+# Dequantisation scale of both pools of the 8-bit workloads: stored codes hold
+# N(0,1) draws times 64, well inside E4M3's +-448.
+FP8_SCALE = 2.0 ** -6
 
 # Named workloads (the shapes the pages' examples use: Llama-3.1-8B-class and
 # Llama-3-70B-class attention head layouts, 16-token blocks).
@@ -98,15 +105,33 @@ def draw_values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
 
 
 def nan_bits(dtype: str):
-    return NAN_F32_BITS if dtype == "f32" else NAN_BF16_BITS
+    return {"f32": NAN_F32_BITS, "bf16": NAN_BF16_BITS, "fp8": NAN_FP8_BITS}[dtype]
 
 
 def storage_dtype(dtype: str):
-    return np.float32 if dtype == "f32" else np.uint16
+    return {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[dtype]
+
+
+def bits_dtype(dtype: str):
+    """Unsigned integer type with the storage's width (for writing bit patterns)."""
+    return {"f32": np.uint32, "bf16": np.uint16, "fp8": np.uint8}[dtype]
 
 
 def element_bytes(dtype: str) -> int:
-    return 4 if dtype == "f32" else 2
+    return {"f32": 4, "bf16": 2, "fp8": 1}[dtype]
+
+
+def query_dtype(dtype: str) -> str:
+    """Dtype of q and of the new tokens: bf16 for an 8-bit cache, else the cache's."""
+    return "bf16" if dtype == "fp8" else dtype
+
+
+def fp8_codes(x: np.ndarray, scale: float) -> np.ndarray:
+    """E4M3 codes of float32 draws divided by ``scale`` (PyTorch's cast; |x/scale| <= 448)."""
+    import torch
+
+    y = np.clip(np.asarray(x, dtype=np.float32) / np.float32(scale), -448.0, 448.0)
+    return torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
 # ---------------------------------------------------------------------------
@@ -201,6 +226,8 @@ class Workload:
     copy_pairs: np.ndarray
     refcount: np.ndarray
     info: dict
+    k_scale: float = 1.0  # dequantisation scales of an 8-bit cache
+    v_scale: float = 1.0
 
     @property
     def num_seqs(self) -> int:
@@ -261,7 +288,10 @@ def _fill_pools(seed_seq, num_blocks, hkv, bs, d, dtype, chunk_blocks=1024):
         b1 = min(num_blocks, b0 + chunk_blocks)
         rng = np.random.default_rng(children[job])
         x = rng.standard_normal(size=(b1 - b0, hkv, bs, d), dtype=np.float32)
-        pools[p][b0:b1] = x if dtype == "f32" else _round_bf16_inplace(x)
+        if dtype == "fp8":
+            pools[p][b0:b1] = fp8_codes(x, FP8_SCALE)
+        else:
+            pools[p][b0:b1] = x if dtype == "f32" else _round_bf16_inplace(x)
 
     with ThreadPoolExecutor(max_workers=8) as ex:
         list(ex.map(work, range(2 * len(starts))))
@@ -310,11 +340,12 @@ def _assemble(name, seed, cfg, dtype, streams, num_blocks, seq_blocks, lens,
         dead[dst, :] = True
     bidx, ridx = np.nonzero(dead)
     for pool in (k_pool, v_pool):
-        pool.view(np.uint32 if dtype == "f32" else np.uint16)[bidx, :, ridx, :] = poison
+        pool.view(bits_dtype(dtype))[bidx, :, ridx, :] = poison
 
-    q = draw_values(streams["q"], (num_seqs, hq, d), dtype)
-    k_new = draw_values(streams["new"], (len(writes), hkv, d), dtype)
-    v_new = draw_values(streams["new"], (len(writes), hkv, d), dtype)
+    qdt = query_dtype(dtype)
+    q = draw_values(streams["q"], (num_seqs, hq, d), qdt)
+    k_new = draw_values(streams["new"], (len(writes), hkv, d), qdt)
+    v_new = draw_values(streams["new"], (len(writes), hkv, d), qdt)
 
     # Table rows past a sequence's last block point at a poisoned block when one
     # exists, so reading them would show up as NaN in the output.
@@ -324,8 +355,10 @@ def _assemble(name, seed, cfg, dtype, streams, num_blocks, seq_blocks, lens,
     for i, blocks in enumerate(seq_blocks):
         tables[i, : len(blocks)] = blocks
 
+    scale = FP8_SCALE if dtype == "fp8" else 1.0
     return Workload(
-        name=name, seed=seed, dtype=dtype, num_heads=hq, num_kv_heads=hkv,
+        name=name, seed=seed, dtype=dtype, k_scale=scale, v_scale=scale,
+        num_heads=hq, num_kv_heads=hkv,
         head_dim=d, block_size=bs, q=q, k_pool=k_pool, v_pool=v_pool,
         block_tables=tables, context_lens=np.asarray(lens, dtype=np.int32),
         k_new=k_new, v_new=v_new, slot_mapping=slot_mapping,

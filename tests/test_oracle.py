@@ -421,6 +421,139 @@ def test_copy_on_write_semantics():
 
 
 # ---------------------------------------------------------------------------
+# the 8-bit (E4M3) cache
+# ---------------------------------------------------------------------------
+
+def _torch_e4m3(values_f32):
+    """PyTorch's float32 -> float8_e4m3fn cast (round to nearest even; NaN past 464)."""
+    t = torch.from_numpy(np.ascontiguousarray(values_f32, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_decode_table_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = oracle.fp8_to_f64(codes)
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    keep = ~np.isnan(ref)
+    assert np.array_equal(ref[keep], got[keep])
+    assert np.array_equal(np.signbit(ref[keep]), np.signbit(got[keep]))
+
+
+def test_e4m3_closed_forms():
+    v = oracle.e4m3_value
+    assert v(0x00) == 0.0 and math.copysign(1.0, v(0x80)) < 0
+    assert v(0x01) == 2.0 ** -9 and v(0x07) == 7 * 2.0 ** -9   # subnormals m/8 * 2^-6
+    assert v(0x08) == 2.0 ** -6                                 # smallest normal
+    assert v(0x30) == 0.5 and v(0x38) == 1.0 and v(0x40) == 2.0 and v(0xB8) == -1.0
+    assert v(0x7E) == 448.0 == oracle.E4M3_MAX and v(0xFE) == -448.0
+    assert math.isnan(v(0x7F)) and math.isnan(v(0xFF))
+    assert v(0x78) == 256.0 and v(0x3F) == 1.875
+
+
+def test_e4m3_encode_matches_torch_in_range():
+    rng = np.random.default_rng(7)
+    finite = oracle.fp8_to_f64(np.arange(0x7F))  # 0 .. 448, increasing
+    mids = (finite[:-1] + finite[1:]) / 2          # every tie between neighbours
+    mags = np.exp(rng.uniform(math.log(2.0 ** -12), math.log(460.0), 30000))
+    vals = np.concatenate([finite, mids, mags, [464.0]])
+    vals = np.concatenate([vals, -vals]).astype(np.float32)
+    assert np.array_equal(oracle.fp8_encode(vals.astype(np.float64)), _torch_e4m3(vals))
+
+
+def test_e4m3_encode_saturates_and_keeps_nan():
+    enc = lambda x: int(oracle.fp8_encode(np.array([x]))[0])
+    for x in (448.0, 448.5, 464.0, 465.0, 1.0e30, math.inf):
+        assert enc(x) == 0x7E and enc(-x) == 0xFE
+    assert enc(math.nan) == 0x7F
+    assert enc(-0.0) == 0x80 and enc(-1e-10) == 0x80 and enc(1e-10) == 0x00
+    # the library clamps where PyTorch's cast gives NaN
+    assert math.isnan(torch.tensor(465.0).to(torch.float8_e4m3fn).float().item())
+
+
+def test_e4m3_round_trip_of_every_finite_code():
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    assert np.array_equal(oracle.fp8_encode(oracle.fp8_to_f64(codes)), codes)
+
+
+@pytest.mark.parametrize("scale", [2.0 ** -6, 0.0123, 3.0])
+def test_fp8_quantize_divides_in_binary32(scale):
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(4000).astype(np.float32)
+    bits = ((x.view(np.uint32) + np.uint32(0x8000)) >> np.uint32(16)).astype(np.uint16)
+    x32 = torch.from_numpy((bits.astype(np.uint32) << np.uint32(16)).view(np.float32))
+    quot = (x32 / torch.tensor(scale, dtype=torch.float32)).numpy()
+    quot = np.clip(quot, -448.0, 448.0)
+    assert np.array_equal(oracle.fp8_quantize(bits, scale), _torch_e4m3(quot))
+
+
+def _fp8_case(rng, bs=4, d=8, hkv=2, group=2, lens=(1, 5, 9, 13)):
+    nb = sum(-(-n // bs) for n in lens) + 2
+    k_codes = rng.integers(0, 256, size=(nb, hkv, bs, d), dtype=np.uint8)
+    v_codes = rng.integers(0, 256, size=(nb, hkv, bs, d), dtype=np.uint8)
+    for pool in (k_codes, v_codes):  # no NaN codes where rows are read
+        pool[(pool & 0x7F) == 0x7F] = 0x38
+    perm = rng.permutation(nb)
+    tables = np.zeros((len(lens), 8), dtype=np.int32)
+    cursor = 0
+    for i, n in enumerate(lens):
+        for j in range(-(-n // bs)):
+            tables[i, j] = perm[cursor]
+            cursor += 1
+    qf = rng.standard_normal((len(lens), hkv * group, d)).astype(np.float32)
+    q_bits = ((qf.view(np.uint32) + np.uint32(0x8000)) >> np.uint32(16)).astype(np.uint16)
+    return q_bits, k_codes, v_codes, tables, np.array(lens, dtype=np.int32)
+
+
+def test_fp8_decode_is_decode_of_the_dequantised_values():
+    rng = np.random.default_rng(5)
+    q_bits, k_codes, v_codes, tables, lens = _fp8_case(rng)
+    ks, vs = 2.0 ** -5, 2.0 ** 3  # powers of two: the dequantised values are float32
+    got = oracle.decode(q_bits, k_codes, v_codes, tables, lens, 0.25, "fp8", k_scale=ks, v_scale=vs)
+    k32 = (oracle.fp8_to_f64(k_codes) * ks).astype(np.float32)
+    v32 = (oracle.fp8_to_f64(v_codes) * vs).astype(np.float32)
+    q32 = oracle.to_f64(q_bits, "bf16").astype(np.float32)
+    ref = oracle.decode(q32, k32, v32, tables, lens, 0.25, "f32")
+    assert np.array_equal(got, ref)
+    # and the scales act where they should: scores see k_scale, outputs scale with v_scale
+    swapped = oracle.decode(q_bits, k_codes, v_codes, tables, lens, 0.25, "fp8", k_scale=vs, v_scale=ks)
+    assert not np.allclose(swapped, got)
+    doubled = oracle.decode(q_bits, k_codes, v_codes, tables, lens, 0.25, "fp8", k_scale=ks, v_scale=2 * vs)
+    assert np.array_equal(doubled, 2 * got)
+    po, pm, ps = oracle.decode_partitions(q_bits, k_codes, v_codes, tables, lens, 0.25, "fp8", 4,
+                                          k_scale=ks, v_scale=vs)
+    merged, _ = oracle.splitkv_merge(po, pm, ps, lens, 4)
+    np.testing.assert_allclose(merged, got, rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_append_writes_quantised_rows():
+    rng = np.random.default_rng(9)
+    bs, d, hkv = 4, 16, 2
+    k_pool = rng.integers(0, 256, size=(5, hkv, bs, d), dtype=np.uint8)
+    v_pool = rng.integers(0, 256, size=(5, hkv, bs, d), dtype=np.uint8)
+    xk = rng.standard_normal((3, hkv, d)).astype(np.float32) * 8
+    xv = rng.standard_normal((3, hkv, d)).astype(np.float32) * 8
+    to_bits = lambda x: ((x.view(np.uint32) + np.uint32(0x8000)) >> np.uint32(16)).astype(np.uint16)
+    kb, vb = to_bits(xk), to_bits(xv)
+    slots = [6, -1, 17]
+    ks, vs = 0.05, 2.0 ** -4
+    k2, v2 = oracle.kv_append(k_pool, v_pool, kb, vb, slots, fp8_scales=(ks, vs))
+    for n, s in enumerate(slots):
+        if s < 0:
+            continue
+        kq = (torch.from_numpy(oracle.to_f64(kb[n], "bf16").astype(np.float32)) /
+              torch.tensor(ks, dtype=torch.float32)).numpy()
+        vq = (torch.from_numpy(oracle.to_f64(vb[n], "bf16").astype(np.float32)) /
+              torch.tensor(vs, dtype=torch.float32)).numpy()
+        # saturation at 448 (PyTorch's cast would give NaN past 464)
+        assert np.array_equal(k2[s // bs, :, s % bs], _torch_e4m3(np.clip(kq, -448, 448)))
+        assert np.array_equal(v2[s // bs, :, s % bs], _torch_e4m3(np.clip(vq, -448, 448)))
+        k2[s // bs, :, s % bs] = k_pool[s // bs, :, s % bs]
+        v2[s // bs, :, s % bs] = v_pool[s // bs, :, s % bs]
+    assert np.array_equal(k2, k_pool) and np.array_equal(v2, v_pool)  # nothing else moved
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes are caught by the pins above
 # ---------------------------------------------------------------------------
 
@@ -472,4 +605,58 @@ def test_planted_mistakes_are_caught(monkeypatch, name, target, mutant):
         test_worked_example_attention_is_contiguous_attention()
     except AssertionError:
         failures += 1
+    assert failures > 0, f"planted mistake '{name}' went unnoticed"
+
+
+def _e4m3_table_bias8():
+    out = []
+    for c in range(256):
+        e, m = (c >> 3) & 0xF, c & 7
+        sign = -1.0 if c & 0x80 else 1.0
+        out.append(sign * (math.ldexp(m, -10) if e == 0 else math.ldexp(8 + m, e - 11)))
+    return np.array(out)
+
+
+def _encode_ties_toward_zero(values):
+    y = np.asarray(values, dtype=np.float64)
+    mags = pa._E4M3_MAGNITUDES
+    out = []
+    for v in y.reshape(-1):
+        a = min(abs(v), 448.0)
+        idx = int(np.argmin(np.abs(mags - a)))  # the first of two equally near: the smaller
+        out.append((0x80 if math.copysign(1, v) < 0 else 0) | idx)
+    return np.array(out, dtype=np.uint8).reshape(y.shape)
+
+
+def _quantize_multiplies(bf16_bits, scale):
+    x32 = pa.to_f64(bf16_bits, "bf16").astype(np.float32)
+    return pa.fp8_encode((x32 * np.float32(scale)).astype(np.float64))
+
+
+def _kv_f64_swapped(rows, dtype, scale):
+    return pa.fp8_to_f64(rows) / float(scale) if dtype == "fp8" else pa.to_f64(rows, dtype)
+
+
+@pytest.mark.parametrize("name,target,mutant,checks", [
+    ("E4M3 bias 8", "_E4M3_TABLE", _e4m3_table_bias8(),
+     ["test_e4m3_decode_table_matches_torch"]),
+    ("ties toward zero", "fp8_encode", _encode_ties_toward_zero,
+     ["test_e4m3_encode_matches_torch_in_range"]),
+    ("scale multiplies", "fp8_quantize", _quantize_multiplies,
+     ["test_fp8_append_writes_quantised_rows"]),
+    ("scale divides on read", "_kv_f64", _kv_f64_swapped,
+     ["test_fp8_decode_is_decode_of_the_dequantised_values"]),
+])
+def test_planted_fp8_mistakes_are_caught(monkeypatch, name, target, mutant, checks):
+    monkeypatch.setattr(pa, target, mutant)
+    if target == "fp8_encode":
+        monkeypatch.setattr(oracle, "fp8_encode", mutant)
+    if target == "fp8_quantize":
+        monkeypatch.setattr(oracle, "fp8_quantize", mutant)
+    failures = 0
+    for check in checks:
+        try:
+            globals()[check]()
+        except AssertionError:
+            failures += 1
     assert failures > 0, f"planted mistake '{name}' went unnoticed"

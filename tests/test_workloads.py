@@ -132,3 +132,24 @@ def test_random_partials_poison_unused_partitions():
     out, mx, sm = W.random_partials(3, 2, 4, 8, 5, [100, 20], 32)
     assert np.isfinite(out[0, :, :4]).all() and np.isnan(out[0, :, 4:]).all()
     assert np.isfinite(sm[1, :, :1]).all() and np.isnan(sm[1, :, 1:]).all()
+
+
+def test_fp8_workloads():
+    """8-bit copies of the shapes: E4M3 codes from PyTorch's cast, bf16 queries and
+    new tokens, NaN codes exactly on the unowned rows, the generator's slots."""
+    w = W.make_config(4, dtype="fp8", num_seqs=6)
+    assert w.name.endswith("_fp8") and w.k_pool.dtype == np.uint8 and w.v_pool.dtype == np.uint8
+    assert w.q.dtype == np.uint16 and w.k_new.dtype == np.uint16
+    assert w.k_scale == w.v_scale == W.FP8_SCALE
+    b = W.make_config(4, num_seqs=6)  # same seed: same draws, stored in bf16
+    assert np.array_equal(w.q, b.q) and np.array_equal(w.block_tables, b.block_tables)
+    assert np.array_equal(w.slot_mapping, b.slot_mapping)
+    nan_fp8 = ((w.k_pool & 0x7F) == 0x7F).all(axis=(1, 3))
+    assert np.array_equal(nan_fp8, _nan_rows(b))  # poisoned exactly where the bf16 copy is
+    live = ~nan_fp8[:, None, :, None] & np.ones_like(w.k_pool, dtype=bool)
+    vals = torch.from_numpy(w.k_pool).view(torch.float8_e4m3fn).double().numpy()
+    assert np.isfinite(vals[live]).all() and np.abs(vals[live]).max() <= 448
+    # the codes are the scaled bf16-rounded draws' near neighbours (same stream, finer grid)
+    ref = W.bf16_bits_to_f32(b.k_pool)[live] / W.FP8_SCALE
+    assert np.max(np.abs(vals[live] - ref) / np.maximum(np.abs(ref), 2.0 ** -6)) < 2.0 ** -3
+    assert w.kv_bytes() * 2 == b.kv_bytes()
