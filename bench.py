@@ -44,6 +44,7 @@ HBM_PEAK_GBPS = 8000.0
 
 
 def to_device(arr, dtype):
+    """Device copy of stored values: bf16 bit patterns, f32, or uint8 E4M3 codes."""
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
     return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
@@ -51,15 +52,16 @@ def to_device(arr, dtype):
 
 def algorithmic_bytes(w: W.Workload) -> dict:
     """Bytes the decode step must move, per component."""
-    e = W.element_bytes(w.dtype)
+    e = W.element_bytes(w.dtype)                    # cache element
+    eq = W.element_bytes(W.query_dtype(w.dtype))    # q, new tokens and output
     table_entries = sum(W.blocks_for(int(n), w.block_size) for n in w.context_lens)
     return dict(
         kv=w.kv_bytes(),
-        q=w.num_seqs * w.num_heads * w.head_dim * e,
-        out=w.num_seqs * w.num_heads * w.head_dim * e,
+        q=w.num_seqs * w.num_heads * w.head_dim * eq,
+        out=w.num_seqs * w.num_heads * w.head_dim * eq,
         tables=4 * table_entries,
         lens=4 * w.num_seqs,
-        append=2 * 2 * len(w.slot_mapping) * w.num_kv_heads * w.head_dim * e,
+        append=2 * len(w.slot_mapping) * w.num_kv_heads * w.head_dim * (eq + e),
     )
 
 
@@ -73,14 +75,16 @@ def cpu_baseline(w: W.Workload, budget_s: float) -> dict:
     except Exception:  # pragma: no cover - reporting only
         threads = 1
     kp, vp = oracle.copy_blocks(w.k_pool, w.v_pool, w.copy_pairs)
-    kp, vp = oracle.kv_append(kp, vp, w.k_new, w.v_new, w.slot_mapping)
+    kp, vp = oracle.kv_append(kp, vp, w.k_new, w.v_new, w.slot_mapping,
+                              fp8_scales=(w.k_scale, w.v_scale) if w.dtype == "fp8" else None)
     scale = 1.0 / math.sqrt(w.head_dim)
     done = 0
     kv = 0
     t0 = time.perf_counter()
     while done < w.num_seqs and time.perf_counter() - t0 < budget_s:
         sl = slice(done, done + 1)
-        oracle.decode(w.q[sl], kp, vp, w.block_tables[sl], w.context_lens[sl], scale, w.dtype)
+        oracle.decode(w.q[sl], kp, vp, w.block_tables[sl], w.context_lens[sl], scale, w.dtype,
+                      k_scale=w.k_scale, v_scale=w.v_scale)
         kv += int(w.context_lens[done]) * w.num_kv_heads * w.head_dim * 2 * W.element_bytes(w.dtype)
         done += 1
     dt = time.perf_counter() - t0
@@ -198,12 +202,14 @@ def pmc_summary(fetch_dir: str, write_dir: str, workload: str, block_bytes: int,
     return text
 
 
-def workload_shape(k: int, block_size=None):
+def workload_shape(k: int, block_size=None, dtype=None):
     """(name, bytes of one block of one pool) of workload k, as make_config names it."""
     c = W.CONFIGS[k]
     bs = int(block_size or c["block_size"])
-    name = c["name"] + ("" if bs == c["block_size"] else f"_bs{bs}")
-    return name, c["num_kv_heads"] * bs * c["head_dim"] * W.element_bytes(c["dtype"])
+    dt = dtype or c["dtype"]
+    name = (c["name"] + ("" if dt == c["dtype"] else f"_{dt}") +
+            ("" if bs == c["block_size"] else f"_bs{bs}"))
+    return name, c["num_kv_heads"] * bs * c["head_dim"] * W.element_bytes(dt)
 
 
 def main() -> int:
@@ -213,6 +219,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--block-size", type=int, default=None)
+    ap.add_argument("--dtype", default=None, choices=["f32", "bf16", "fp8"],
+                    help="cache element type (default: the workload's; fp8 = E4M3 codes)")
     ap.add_argument("--mode", default="balanced",
                     help="balanced | single | <partition size in tokens> (split-KV + merge)")
     ap.add_argument("--rotate", type=int, default=3, help="independent copies of the KV pools")
@@ -227,7 +235,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.pmc_summary:
-        name, block_bytes = workload_shape(args.workload, args.block_size)
+        name, block_bytes = workload_shape(args.workload, args.block_size, args.dtype)
         print(pmc_summary(*args.pmc_summary, name, block_bytes, args.mode, args.pmc_command))
         return 0
 
@@ -240,24 +248,27 @@ def main() -> int:
         return 2
     lib.load()
 
-    w = W.make_config(args.workload, block_size=args.block_size)
+    w = W.make_config(args.workload, dtype=args.dtype, block_size=args.block_size)
+    qdt = W.query_dtype(w.dtype)
+    sc = dict(k_scale=w.k_scale, v_scale=w.v_scale)
     mode = args.mode if args.mode in ("balanced", "single") else int(args.mode)
     scale = 1.0 / math.sqrt(w.head_dim)
     nbytes = algorithmic_bytes(w)
     print(f"# workload {w.name}: {w.num_seqs} seqs, KV {nbytes['kv'] / 1e6:.1f} MB, "
           f"pool {w.num_blocks} blocks, mode {mode}", file=sys.stderr, flush=True)
 
-    shared = dict(q=to_device(w.q, w.dtype),
+    shared = dict(q=to_device(w.q, qdt),
                   tables=torch.from_numpy(w.block_tables).cuda(),
                   lens=torch.from_numpy(w.context_lens).cuda(),
                   slots=torch.from_numpy(w.slot_mapping).cuda(),
                   pairs=torch.from_numpy(w.copy_pairs).cuda(),
-                  k_new=to_device(w.k_new, w.dtype), v_new=to_device(w.v_new, w.dtype))
+                  k_new=to_device(w.k_new, qdt), v_new=to_device(w.v_new, qdt))
     pools = []
     k0, v0 = to_device(w.k_pool, w.dtype), to_device(w.v_pool, w.dtype)
     for r in range(args.rotate):
         pools.append((k0, v0) if r == 0 else (k0.clone(), v0.clone()))
-    out = torch.empty((w.num_seqs, w.num_heads, w.head_dim), dtype=k0.dtype, device="cuda")
+    out = torch.empty((w.num_seqs, w.num_heads, w.head_dim), device="cuda",
+                      dtype=torch.float32 if w.dtype == "f32" else torch.bfloat16)
     psize = mode if isinstance(mode, int) else 0
     mp = max(1, max(math.ceil(int(n) / psize) for n in w.context_lens)) if psize else 1
     po = torch.empty((w.num_seqs, w.num_heads, mp, w.head_dim), device="cuda")
@@ -271,17 +282,17 @@ def main() -> int:
         kp, vp = pools[r]
         if psize:
             lib.pa_decode_partitions(kp, vp, shared["q"], shared["tables"], shared["lens"],
-                                     scale, psize, po, pm, ps)
+                                     scale, psize, po, pm, ps, **sc)
             lib.pa_splitkv_reduce(po, pm, ps, shared["lens"], psize, out)
         else:
             lib.pa_decode(kp, vp, shared["q"], shared["tables"], shared["lens"], scale, out,
-                          workspace=ws)
+                          workspace=ws, **sc)
 
     def step(r):
         kp, vp = pools[r]
         if shared["pairs"].numel():
             lib.pa_copy_blocks(kp, vp, shared["pairs"])
-        lib.pa_kv_append(kp, vp, shared["k_new"], shared["v_new"], shared["slots"])
+        lib.pa_kv_append(kp, vp, shared["k_new"], shared["v_new"], shared["slots"], **sc)
         decode(r)
 
     def timed(fn, n):

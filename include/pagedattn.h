@@ -25,8 +25,16 @@
  *   [num_blocks][num_kv_heads][block_size][head_dim] row-major, so the rows of
  *   one (block, KV head) pair are one contiguous run.  Token slot s of the
  *   cache is row (s / block_size, :, s % block_size, :).
- * - Element types: PA_F32 (IEEE binary32) or PA_BF16 (bfloat16).  Decode
- *   accumulates in binary32 and rounds a bf16 output to nearest-even.
+ * - Element types: PA_F32 (IEEE binary32), PA_BF16 (bfloat16), or
+ *   PA_FP8_E4M3 for an 8-bit cache.  Decode accumulates in binary32 and rounds
+ *   a bf16 output to nearest-even.
+ * - An 8-bit cache halves the bytes of every block (the lever the
+ *   "PagedAttention" glossary page, section "What paging costs", names on top
+ *   of paging).  Its codes are OCP E4M3 (1 sign, 4 exponent bits with bias 7,
+ *   3 mantissa bits; exponent field 0 = subnormals m/8 * 2^-6; S.1111.111 =
+ *   NaN; largest magnitude 448).  Code c of the K pool stands for
+ *   e4m3(c) * k_scale, of the V pool for e4m3(c) * v_scale.  Queries and new
+ *   tokens of an 8-bit cache are bfloat16.
  * - Device-side contents are not validated beyond what keeps every access in
  *   bounds: a block id outside [0, num_blocks) in a table or pair, or a slot
  *   outside [0, num_blocks*block_size), is skipped (its rows take no part);
@@ -42,7 +50,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -53,7 +61,7 @@ typedef enum pa_status {
   PA_ERR_LAUNCH = 5       /* the HIP runtime refused a launch */
 } pa_status;
 
-typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
 
 /* Description of the two KV pools (a HOST struct holding DEVICE pointers). */
 typedef struct pa_cache {
@@ -64,6 +72,8 @@ typedef struct pa_cache {
   int32_t block_size;    /* tokens per block: 16 or 32 */
   int32_t head_dim;      /* 64 or 128 */
   int32_t dtype;         /* pa_dtype of both pools */
+  float k_scale;         /* PA_FP8_E4M3: dequantisation scales of the pools, positive */
+  float v_scale;         /*   and finite; ignored for the other types */
 } pa_cache;
 
 /* Version of this header the library was built from (PA_ABI_VERSION). */
@@ -87,10 +97,14 @@ const char *pa_last_error(void);
  * KV head h gets
  *     K[s / B][h][s % B][:] = k_new[n][h][:],   V likewise from v_new,
  * copied bit for bit (no conversion).  A negative slot means "no write".
- * No other byte of either pool changes.
+ * No other byte of either pool changes.  An 8-bit cache stores instead, for
+ * each bf16 input x, the E4M3 code nearest to x / scale (x widened to
+ * binary32, the division done in binary32 and rounded to nearest), ties to
+ * the even code, magnitudes past 448 clamped to 448, NaN kept as NaN.
  *
  *   cache         HOST   pool description
  *   k_new, v_new  DEVICE [num_tokens][num_kv_heads][head_dim], cache->dtype
+ *                        (bfloat16 for an 8-bit cache)
  *   slot_mapping  DEVICE int64 [num_tokens]; live slots must be distinct
  *   num_tokens    >= 0 (0 enqueues nothing)
  * Requires head_dim * element size to be a multiple of 16 bytes and every
@@ -137,14 +151,15 @@ int pa_copy_blocks(const pa_cache *cache, const int64_t *block_pairs, int32_t nu
  * the log-sum-exp rule by a second kernel enqueued on the same stream.
  * Without one (workspace = NULL), one workgroup walks each sequence.
  *
- *   q             DEVICE [num_seqs][num_heads][head_dim], cache->dtype
+ *   q             DEVICE [num_seqs][num_heads][head_dim], cache->dtype (bfloat16
+ *                 for an 8-bit cache, whose K/V values are codes times scales)
  *   block_tables  DEVICE int32 [num_seqs][max_blocks_per_seq]; entries past
  *                 ceil(L_i / block_size) are not read
  *   context_lens  DEVICE int32 [num_seqs], 0 <= L_i <= max_blocks_per_seq*block_size
  *   num_heads     multiple of num_kv_heads; ratio 1, 2, 4 or 8
  *   scale         > 0 and finite (normally 1/sqrt(head_dim))
  *   out           DEVICE [num_seqs][num_heads][head_dim] of out_dtype, 16-byte aligned
- *   out_dtype     PA_F32, or cache->dtype
+ *   out_dtype     PA_F32, or PA_BF16 for a bf16 or 8-bit cache
  *   workspace     DEVICE scratch of workspace_bytes >= pa_decode_workspace_bytes(),
  *                 256-byte aligned, or NULL; its contents need no initialising
  *                 and are meaningless afterwards.  Calls in flight at the same

@@ -66,7 +66,8 @@ def to_f64(values, dtype: str) -> np.ndarray:
         return np.asarray(values, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":
         bits = np.asarray(values, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
-        return bits.view(np.float32).astype(np.float64)
+        with np.errstate(invalid="ignore"):  # NaN patterns widen to NaN
+            return bits.view(np.float32).astype(np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -158,7 +159,8 @@ def fp8_quantize(bf16_bits, scale: float) -> np.ndarray:
     with :func:`fp8_encode`.
     """
     x32 = to_f64(bf16_bits, "bf16").astype(np.float32)
-    y32 = x32 / np.float32(scale)
+    with np.errstate(over="ignore", invalid="ignore"):  # IEEE: overflow gives +-inf
+        y32 = x32 / np.float32(scale)
     return fp8_encode(y32.astype(np.float64))
 
 

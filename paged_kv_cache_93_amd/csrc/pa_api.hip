@@ -1,9 +1,16 @@
 // Library-wide entry points of libpagedattn: version queries, the per-thread
 // error message, and the pool checks every cache entry point shares.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 
 #include "pa_internal.h"
+
+#include <cstddef>
+
+static_assert(sizeof(pa_cache) == 48 && offsetof(pa_cache, dtype) == 36 &&
+                  offsetof(pa_cache, k_scale) == 40 && offsetof(pa_cache, v_scale) == 44,
+              "pa_cache layout is part of the ABI");
 
 namespace pa {
 
@@ -44,6 +51,10 @@ int check_cache(const pa_cache* cache, const char* fn) {
   if (total > 9.0e18) return fail(PA_ERR_SHAPE, "%s: pool too large", fn);
   if (!aligned16(cache->k_pool) || !aligned16(cache->v_pool))
     return fail(PA_ERR_SHAPE, "%s: pools must be 16-byte aligned", fn);
+  if (cache->dtype == PA_FP8_E4M3 &&
+      !(cache->k_scale > 0.f && cache->v_scale > 0.f && std::isfinite(cache->k_scale) &&
+        std::isfinite(cache->v_scale)))
+    return fail(PA_ERR_SHAPE, "%s: an 8-bit cache needs positive finite k_scale and v_scale", fn);
   return PA_OK;
 }
 

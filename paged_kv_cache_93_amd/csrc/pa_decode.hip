@@ -8,6 +8,10 @@
 namespace pa {
 namespace {
 
+int elem_type(int32_t dtype) {
+  return dtype == PA_BF16 ? kBF16 : dtype == PA_FP8_E4M3 ? kFP8 : kF32;
+}
+
 // Largest workgroup (in waves) made of whole KV heads, at most PA_MAX_WAVES.
 int waves_per_group(int num_kv_heads) {
   for (int w : {8, 4, 2, 1})
@@ -29,9 +33,10 @@ constexpr int kMaxGroupsPerCu = 32;
 
 // Workgroups the balanced split uses: as many as the device holds at once.
 int balanced_groups(const pa_cache* cache, int group, int waves, size_t lds) {
-  int per_cu = cache->dtype == PA_BF16
-                   ? decode_groups_per_cu_bf16(cache->head_dim, cache->block_size, group, waves, lds)
-                   : decode_groups_per_cu_f32(cache->head_dim, cache->block_size, group, waves, lds);
+  const int d = cache->head_dim, bs = cache->block_size;
+  int per_cu = cache->dtype == PA_BF16       ? decode_groups_per_cu_bf16(d, bs, group, waves, lds)
+               : cache->dtype == PA_FP8_E4M3 ? decode_groups_per_cu_fp8(d, bs, group, waves, lds)
+                                             : decode_groups_per_cu_f32(d, bs, group, waves, lds);
   if (per_cu < 1) per_cu = 1;
   if (per_cu > kMaxGroupsPerCu) per_cu = kMaxGroupsPerCu;
   return device_cus() * per_cu;
@@ -102,16 +107,20 @@ int prepare(const char* fn, const pa_cache* cache, const void* q, const int32_t*
   a->num_heads = num_heads;
   a->max_blocks = max_blocks_per_seq;
   a->out_f32 = 1;
-  a->scale_log2 = scale * 1.4426950408889634f;
+  // an 8-bit cache's K scale multiplies every score, its V scale every output
+  const bool fp8 = cache->dtype == PA_FP8_E4M3;
+  a->scale_log2 = scale * 1.4426950408889634f * (fp8 ? cache->k_scale : 1.f);
+  a->v_scale = fp8 ? cache->v_scale : 1.f;
   return PA_OK;
 }
 
 int launch(const char* fn, const pa_cache* cache, int group, const DecodeArgs& a, dim3 grid,
            int waves, size_t lds, hipStream_t s) {
+  const int d = cache->head_dim, bs = cache->block_size;
   const bool ok =
-      cache->dtype == PA_BF16
-          ? launch_decode_bf16(cache->head_dim, cache->block_size, group, a, grid, waves, lds, s)
-          : launch_decode_f32(cache->head_dim, cache->block_size, group, a, grid, waves, lds, s);
+      cache->dtype == PA_BF16       ? launch_decode_bf16(d, bs, group, a, grid, waves, lds, s)
+      : cache->dtype == PA_FP8_E4M3 ? launch_decode_fp8(d, bs, group, a, grid, waves, lds, s)
+                                    : launch_decode_f32(d, bs, group, a, grid, waves, lds, s);
   if (!ok) return fail(PA_ERR_UNSUPPORTED, "%s: no kernel for this shape", fn);
   return launch_result(fn);
 }
@@ -139,8 +148,9 @@ PA_API int pa_decode(const pa_cache* cache, const void* q, const int32_t* block_
                        max_blocks_per_seq, scale, &a, &group))
     return st;
   if (!out) return fail(PA_ERR_NULL, "%s: out is NULL", fn);
-  if (out_dtype != PA_F32 && out_dtype != cache->dtype)
-    return fail(PA_ERR_UNSUPPORTED, "%s: out_dtype must be PA_F32 or the cache dtype", fn);
+  if (out_dtype != PA_F32 && !(out_dtype == PA_BF16 && cache->dtype != PA_F32))
+    return fail(PA_ERR_UNSUPPORTED,
+                "%s: out_dtype must be PA_F32, or PA_BF16 for a bf16 or 8-bit cache", fn);
   if (!aligned16(out)) return fail(PA_ERR_SHAPE, "%s: out must be 16-byte aligned", fn);
   if (num_seqs == 0) return PA_OK;
   a.out = out;
@@ -150,7 +160,7 @@ PA_API int pa_decode(const pa_cache* cache, const void* q, const int32_t* block_
   const hipStream_t s = static_cast<hipStream_t>(stream);
 
   const size_t wave_lds =
-      size_t(waves) * decode_wave_lds_bytes(cache->dtype == PA_BF16, cache->head_dim, group);
+      size_t(waves) * decode_wave_lds_bytes(elem_type(cache->dtype), cache->head_dim, group);
   if (workspace == nullptr || num_seqs > kMaxBalancedSeqs) {
     a.mode = kModeSingle;
     return launch(fn, cache, group, a, dim3(unsigned(num_seqs), head_groups), waves, wave_lds, s);
@@ -217,6 +227,6 @@ PA_API int pa_decode_partitions(const pa_cache* cache, const void* q, const int3
   const int waves = waves_per_group(cache->num_kv_heads);
   const dim3 grid(unsigned(max_parts), unsigned(cache->num_kv_heads / waves), unsigned(num_seqs));
   const size_t lds =
-      size_t(waves) * decode_wave_lds_bytes(cache->dtype == PA_BF16, cache->head_dim, group);
+      size_t(waves) * decode_wave_lds_bytes(elem_type(cache->dtype), cache->head_dim, group);
   return launch(fn, cache, group, a, grid, waves, lds, static_cast<hipStream_t>(stream));
 }

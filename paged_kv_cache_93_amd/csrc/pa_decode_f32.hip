@@ -4,9 +4,9 @@
 namespace pa {
 bool launch_decode_f32(int d, int bs, int g, const DecodeArgs& a, dim3 grid, int waves,
                         size_t lds, hipStream_t s) {
-  return launch_decode_impl<false>(d, bs, g, a, grid, waves, lds, s);
+  return launch_decode_impl<kF32>(d, bs, g, a, grid, waves, lds, s);
 }
 int decode_groups_per_cu_f32(int d, int bs, int g, int waves, size_t lds) {
-  return decode_groups_per_cu_impl<false>(d, bs, g, waves, lds);
+  return decode_groups_per_cu_impl<kF32>(d, bs, g, waves, lds);
 }
 }  // namespace pa

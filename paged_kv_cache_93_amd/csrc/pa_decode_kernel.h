@@ -49,6 +49,9 @@ namespace pa {
 
 enum DecodeMode : int32_t { kModeSingle = 0, kModePartition = 1, kModeBalanced = 2 };
 
+// Element type of the K/V pools (the template parameter ET of decode_kernel).
+enum ElemType : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
 struct DecodeArgs {
   const uint8_t* q;
   const uint8_t* k_pool;
@@ -69,14 +72,21 @@ struct DecodeArgs {
   int32_t partition_blocks;  // partition mode: blocks per partition
   int32_t max_parts;         // partition mode: partitions per (sequence, head) row
   int32_t num_groups;        // balanced mode: workgroups in the grid (those past the unit count idle)
-  int32_t out_f32;           // 1: binary32 output; 0: bf16 output (bf16 cache only)
-  float scale_log2;          // score scale * log2(e)
+  int32_t out_f32;           // 1: binary32 output; 0: bf16 output (bf16 or 8-bit cache)
+  float scale_log2;          // score scale * log2(e), times the K pool's scale (8-bit cache)
+  float v_scale;             // the V pool's scale (8-bit cache), else 1
 };
 
 namespace dev {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// What one lane loads of a row: 16 bytes, or 8 bytes (eight E4M3 codes).
+template <int LB> struct LaneChunk { typedef u32x4 type; };
+template <> struct LaneChunk<8> { typedef u32x2 type; };
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994531f;
@@ -107,8 +117,8 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <bool NT>
-__device__ __forceinline__ u32x4 load16(const u32x4* p) {
+template <bool NT, class T>
+__device__ __forceinline__ T load_chunk(const T* p) {
   if constexpr (NT)
     return __builtin_nontemporal_load(p);
   else
@@ -133,10 +143,21 @@ __device__ __forceinline__ float dot16(float acc, const u32x4& q, const u32x4& k
   return acc;
 }
 
-// 16-byte chunk -> 8 (bf16) or 4 (f32) floats, exactly.
-template <bool BF16>
-__device__ __forceinline__ void unpack16(const u32x4& c, float* v) {
-  if constexpr (BF16) {
+// A lane's chunk of a V row -> 8 (bf16, E4M3) or 4 (f32) floats, exactly.
+template <int ET, class T>
+__device__ __forceinline__ void unpack_chunk(const T& c, float* v) {
+  if constexpr (ET == kFP8) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const unsigned int word = c[w];  // codes of 4 consecutive elements, lowest byte first
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+      v[4 * w] = lo[0];
+      v[4 * w + 1] = lo[1];
+      v[4 * w + 2] = hi[0];
+      v[4 * w + 3] = hi[1];
+    }
+  } else if constexpr (ET == kBF16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[2 * i] = __uint_as_float(c[i] << 16);
@@ -145,6 +166,28 @@ __device__ __forceinline__ void unpack16(const u32x4& c, float* v) {
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(c[i]);
+  }
+}
+
+// A lane's chunk of a K row in the form it is scored in: bf16 pairs for bf16
+// and E4M3 caches (every E4M3 value is a bf16 value; gfx950 converts a pair of
+// codes to a bf16 pair in one instruction, exactly with scale 1), f32 for f32
+// caches.
+template <int ET, class T>
+__device__ __forceinline__ u32x4 score_chunk(const T& c) {
+  if constexpr (ET == kFP8) {
+    u32x4 r;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const unsigned int word = c[w];
+      r[2 * w] = __builtin_bit_cast(unsigned int,
+                                    __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false));
+      r[2 * w + 1] = __builtin_bit_cast(unsigned int,
+                                        __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true));
+    }
+    return r;
+  } else {
+    return c;
   }
 }
 
@@ -171,14 +214,14 @@ __device__ __forceinline__ int group_of_unit(int64_t u, int64_t total, int64_t g
 #define PA_MFMA_SCORES 1  // 0: score every case on the VALU (for comparison)
 #endif
 
-// Scores on the matrix cores: bf16 caches with 128-dim heads.
-constexpr bool decode_uses_mfma(bool bf16, int d) { return PA_MFMA_SCORES && bf16 && d == 128; }
+// Scores on the matrix cores: bf16 and 8-bit caches with 128-dim heads.
+constexpr bool decode_uses_mfma(int et, int d) { return PA_MFMA_SCORES && et != kF32 && d == 128; }
 
 // LDS bytes each wave of the MFMA path uses: a 16-row K tile padded to 17
 // chunks per row (conflict-free transposed reads), then the softmax weights
 // [4 row groups][G heads][4 rows] and the rescale factors [4][G].
-constexpr int decode_wave_lds_bytes(bool bf16, int d, int g) {
-  return decode_uses_mfma(bf16, d) ? 16 * 17 * 16 + 64 * g + 16 * g : 0;
+constexpr int decode_wave_lds_bytes(int et, int d, int g) {
+  return decode_uses_mfma(et, d) ? 16 * 17 * 16 + 64 * g + 16 * g : 0;
 }
 
 // Byte offset of the per-wave LDS areas behind the unit prefix (balanced mode).
@@ -186,21 +229,26 @@ constexpr size_t decode_prefix_lds_bytes(int num_seqs, bool balanced) {
   return balanced ? (size_t(num_seqs + 1) * 4 + 15) / 16 * 16 : 0;
 }
 
-template <bool BF16, int D, int BS, int G, int PF, bool NT>
+template <int ET, int D, int BS, int G, int PF, bool NT>
 __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   using namespace dev;
-  constexpr int EB = BF16 ? 2 : 4;                   // element bytes
-  constexpr int VEC = 16 / EB;                       // elements per 16-byte chunk
+  constexpr bool BF16 = ET != kF32;                  // q, and K as scored, in bf16
+  constexpr int EB = ET == kF32 ? 4 : ET == kBF16 ? 2 : 1;  // K/V element bytes
+  constexpr int QEB = BF16 ? 2 : 4;                  // q element bytes
+  constexpr int LB = ET == kFP8 ? 8 : 16;            // bytes a lane loads per row chunk
+  using Raw = typename LaneChunk<LB>::type;
+  constexpr int VEC = LB / EB;                       // elements per lane chunk
   constexpr int LPR = D / VEC;                       // lanes per row
   constexpr int RPI = 64 / LPR;                      // rows per load instruction
-  constexpr bool MF = decode_uses_mfma(BF16, D);     // q.k on MFMA (16-row tiles)
+  constexpr bool MF = decode_uses_mfma(ET, D);       // q.k on MFMA (16-row tiles)
   constexpr int TRW = MF ? 16 : (G >= 8 ? 2 : 4) * RPI;  // wide groups keep smaller tiles
   constexpr int TR = BS < TRW ? BS : TRW;            // rows per register tile
   constexpr int NI = TR / RPI;                       // load instructions per tile
   constexpr int TPB = BS / TR;                       // tiles per block
   constexpr int NB = PF + 1;                         // ring buffers
   static_assert(D % VEC == 0 && 64 % LPR == 0 && TR % RPI == 0 && BS % TR == 0, "tiling");
-  static_assert(RPI * D * EB == 1024, "one load instruction covers 1 KiB");
+  static_assert(RPI * D * EB == 64 * LB, "one load instruction covers whole rows");
+  static_assert(!BF16 || VEC == 8, "bf16 query chunks hold 8 elements");
   static_assert(!MF || (RPI == 4 && NI == 4 && TR == 16), "MFMA tiles are 16 rows of 4 groups");
 
   const int lane = threadIdx.x & 63;
@@ -276,7 +324,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   // Per-wave LDS of the MFMA path, behind the unit prefix.
   uint8_t* wave_lds = reinterpret_cast<uint8_t*>(s_prefix) +
                       decode_prefix_lds_bytes(a.num_seqs, a.mode == kModeBalanced) +
-                      size_t(wave) * decode_wave_lds_bytes(BF16, D, G);
+                      size_t(wave) * decode_wave_lds_bytes(ET, D, G);
   u32x4* lds_k = reinterpret_cast<u32x4*>(wave_lds);              // [16 rows][17 chunks]
   float* lds_p = reinterpret_cast<float*>(wave_lds + 16 * 17 * 16);  // [4][G][4]
   float* lds_a = lds_p + 16 * G;                                   // [4][G]
@@ -354,7 +402,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     if (r != 0) return;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float inv = l[h] > 0.f ? 1.f / l[h] : 0.f;
+      const float inv = l[h] > 0.f ? a.v_scale / l[h] : 0.f;
       const int head = head0 + h;
       if (whole) {
         const size_t idx = (size_t(seq) * a.num_heads + head) * D + c * VEC;
@@ -440,7 +488,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   // head).  Every lane loads, so the registers are written by the loads alone.
   auto load_q = [&](int sq, u32x4(&dqc)[MF ? 1 : G], u32x4(&dqf)[MF ? 4 : 1]) {
     const u32x4* qrow =
-        reinterpret_cast<const u32x4*>(a.q + (size_t(sq) * a.num_heads + head0) * D * EB);
+        reinterpret_cast<const u32x4*>(a.q + (size_t(sq) * a.num_heads + head0) * D * QEB);
     if constexpr (MF) {
       const int h = (lane & 15) % G;
 #pragma unroll
@@ -500,7 +548,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   // Loads tile t into (kr, vr) and, on the MFMA path, the query of its
   // sequence into qr, so a tile always arrives with the query it is scored
   // against and a piece boundary needs no query load.
-  auto load_tile = [&](u32x4(&kr)[NI], u32x4(&vr)[NI], u32x4(&qr)[MF ? 4 : 1], int t) {
+  auto load_tile = [&](Raw(&kr)[NI], Raw(&vr)[NI], u32x4(&qr)[MF ? 4 : 1], int t) {
     int phys = -1, sq = 0;
     size_t off = 0;
     if (t < ntiles) {
@@ -527,16 +575,16 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     // so each row group sees 4 consecutive rows, as the MFMA result rows.
     const int lo = MF ? r * 64 + c : lane;
     constexpr int step = MF ? 16 : 64;
-    const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + off) + lo;
-    const u32x4* vp = reinterpret_cast<const u32x4*>(vbase + off) + lo;
+    const Raw* kp = reinterpret_cast<const Raw*>(kbase + off) + lo;
+    const Raw* vp = reinterpret_cast<const Raw*>(vbase + off) + lo;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      kr[i] = load16<NT>(kp + i * step);
-      vr[i] = load16<NT>(vp + i * step);
+      kr[i] = load_chunk<NT>(kp + i * step);
+      vr[i] = load_chunk<NT>(vp + i * step);
     }
   };
 
-  auto process_tile = [&](const u32x4(&kr)[NI], const u32x4(&vr)[NI],
+  auto process_tile = [&](const Raw(&kr)[NI], const Raw(&vr)[NI],
                           const u32x4(&qr)[MF ? 4 : 1], int t) {
     const int idx = int(ubeg + t / TPB - cbase);
     const int phys = __builtin_amdgcn_readlane(w0.ek, idx);
@@ -550,7 +598,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
       // K tile -> LDS, then read back transposed: lane 16g + t gets row t's
       // dims [32mm + 8g, 32mm + 8g + 8) as the A operand of MFMA mm.
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lds_k[(4 * r + i) * 17 + c] = kr[i];
+      for (int i = 0; i < 4; ++i) lds_k[(4 * r + i) * 17 + c] = score_chunk<ET>(kr[i]);
       __builtin_amdgcn_wave_barrier();
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -595,19 +643,23 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
           for (int e = 0; e < VEC; ++e) acc[h][e] *= al;
         }
       }
+      float v[4][VEC];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) unpack_chunk<ET>(vr[i], v[i]);
+      if (__builtin_expect(partial, 0)) {  // the last block of a sequence only
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * r + i >= nvalid)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) v[i][e] = 0.f;  // masked rows may hold NaN
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float v[VEC];
-        unpack16<BF16>(vr[i], v);
-        if (partial && 4 * r + i >= nvalid) {
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) v[e] = 0.f;  // masked rows may hold NaN
-        }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           const float ph = lds_p[(r * G + h) * 4 + i];
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(ph, v[e], acc[h][e]);
+          for (int e = 0; e < VEC; ++e) acc[h][e] = fmaf(ph, v[i][e], acc[h][e]);
         }
       }
       __builtin_amdgcn_wave_barrier();
@@ -617,7 +669,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
       for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int h = 0; h < G; ++h)
-          s[i][h] = group_sum<LPR>(dot16<BF16>(0.f, qc[h], kr[i])) * cl2;
+          s[i][h] = group_sum<LPR>(dot16<BF16>(0.f, qc[h], score_chunk<ET>(kr[i]))) * cl2;
       if (partial) {
 #pragma unroll
         for (int i = 0; i < NI; ++i)
@@ -648,7 +700,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         float v[VEC];
-        unpack16<BF16>(vr[i], v);
+        unpack_chunk<ET>(vr[i], v);
         if (partial && i * RPI + r >= nvalid) {
 #pragma unroll
           for (int e = 0; e < VEC; ++e) v[e] = 0.f;  // masked rows may hold NaN
@@ -697,7 +749,8 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
       __builtin_amdgcn_s_setprio(2);
   };
 
-  u32x4 kb[NB][NI], vb[NB][NI], qb[NB][MF ? 4 : 1];
+  Raw kb[NB][NI], vb[NB][NI];
+  u32x4 qb[NB][MF ? 4 : 1];
 #pragma unroll
   for (int i = 0; i < PF; ++i) load_tile(kb[i], vb[i], qb[i], i);
   for (int t0 = 0; t0 < ntiles; t0 += NB) {
@@ -833,9 +886,17 @@ __global__ void __launch_bounds__(64) merge_kernel(MergeArgs a) {
 #ifndef PA_PREFETCH_WIDE
 #define PA_PREFETCH_WIDE 1    // G = 8
 #endif
+#ifndef PA_PREFETCH_FP8
+#define PA_PREFETCH_FP8 1     // 8-bit caches (tiles of half the bytes)
+#endif
 #ifndef PA_MAX_WAVES
 #define PA_MAX_WAVES 8        // KV heads (waves) per workgroup at most
 #endif
+
+// Tiles in flight ahead of the current one.
+constexpr int decode_prefetch(int et, int g) {
+  return et == kFP8 ? PA_PREFETCH_FP8 : g <= 4 ? PA_PREFETCH_NARROW : PA_PREFETCH_WIDE;
+}
 
 // Launches decode_kernel for a runtime (D, BS, G) on a grid of `waves`-wave
 // workgroups with `lds` bytes of dynamic LDS; false when no instantiation matches.
@@ -843,21 +904,23 @@ bool launch_decode_f32(int d, int bs, int g, const DecodeArgs& a, dim3 grid, int
                        size_t lds, hipStream_t s);
 bool launch_decode_bf16(int d, int bs, int g, const DecodeArgs& a, dim3 grid, int waves,
                         size_t lds, hipStream_t s);
+bool launch_decode_fp8(int d, int bs, int g, const DecodeArgs& a, dim3 grid, int waves,
+                       size_t lds, hipStream_t s);
 
 // Workgroups of `waves` waves one CU holds at once for the decode kernel of
 // (D, BS, G), or 0 when no instantiation matches.
 int decode_groups_per_cu_f32(int d, int bs, int g, int waves, size_t lds);
 int decode_groups_per_cu_bf16(int d, int bs, int g, int waves, size_t lds);
+int decode_groups_per_cu_fp8(int d, int bs, int g, int waves, size_t lds);
 
 // Instantiation table: D in {64, 128}, block size in {16, 32}, G in {1, 2, 4, 8}.
-template <bool BF16>
+template <int ET>
 bool launch_decode_impl(int d, int bs, int g, const DecodeArgs& a, dim3 grid, int waves,
                         size_t lds, hipStream_t s) {
 #define PA_DECODE_CASE(D_, BS_, G_)                                                       \
   if (d == D_ && bs == BS_ && g == G_) {                                                 \
     hipLaunchKernelGGL(                                                                  \
-        (decode_kernel<BF16, D_, BS_, G_, (G_ <= 4 ? PA_PREFETCH_NARROW : PA_PREFETCH_WIDE), \
-                       true>),                                                            \
+        (decode_kernel<ET, D_, BS_, G_, decode_prefetch(ET, G_), true>),                 \
         grid, dim3(waves * 64), lds, s, a);                                              \
     return true;                                                                         \
   }
@@ -876,15 +939,14 @@ bool launch_decode_impl(int d, int bs, int g, const DecodeArgs& a, dim3 grid, in
 
 namespace pa {
 
-template <bool BF16>
+template <int ET>
 int decode_groups_per_cu_impl(int d, int bs, int g, int waves, size_t lds) {
   int n = 0;
 #define PA_OCC_CASE(D_, BS_, G_)                                                             \
   if (d == D_ && bs == BS_ && g == G_) {                                                    \
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(                                       \
             &n,                                                                             \
-            decode_kernel<BF16, D_, BS_, G_, (G_ <= 4 ? PA_PREFETCH_NARROW : PA_PREFETCH_WIDE), \
-                          true>,                                                            \
+            decode_kernel<ET, D_, BS_, G_, decode_prefetch(ET, G_), true>,                 \
             waves * 64, lds) != hipSuccess)                                                 \
       n = 0;                                                                                \
     return n;                                                                               \

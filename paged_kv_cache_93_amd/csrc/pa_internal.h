@@ -19,7 +19,9 @@ int launch_result(const char* what);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-inline int element_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_BF16 ? 2 : 0); }
+inline int element_bytes(int32_t dtype) {
+  return dtype == PA_F32 ? 4 : dtype == PA_BF16 ? 2 : dtype == PA_FP8_E4M3 ? 1 : 0;
+}
 
 // Validates the pool description shared by every cache entry point.
 int check_cache(const pa_cache* cache, const char* fn);

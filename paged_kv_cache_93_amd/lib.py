@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedatt
 PA_OK = 0
 PA_F32 = 0
 PA_BF16 = 1
+PA_FP8_E4M3 = 2
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
                 4: "PA_ERR_WORKSPACE", 5: "PA_ERR_LAUNCH"}
 
@@ -38,7 +39,8 @@ class PaCache(ctypes.Structure):
     _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
                 ("num_blocks", ctypes.c_int64), ("num_kv_heads", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float)]
 
 
 _lib = None
@@ -82,11 +84,19 @@ def _check(status: int):
 
 
 def _dtype_code(t: torch.Tensor) -> int:
+    """pa_dtype of a tensor; E4M3 codes come as float8_e4m3fn or uint8 tensors."""
     if t.dtype == torch.float32:
         return PA_F32
     if t.dtype == torch.bfloat16:
         return PA_BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return PA_FP8_E4M3
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _token_dtype(cache) -> torch.dtype:
+    """dtype of q and of new tokens for a cache: bf16 for an 8-bit cache."""
+    return {PA_F32: torch.float32, PA_BF16: torch.bfloat16, PA_FP8_E4M3: torch.bfloat16}[cache.dtype]
 
 
 def _ptr(t):
@@ -104,13 +114,19 @@ def _require(cond: bool, msg: str):
         raise ValueError(msg)
 
 
-def make_cache(k_pool: torch.Tensor, v_pool: torch.Tensor) -> PaCache:
-    """pa_cache for two [num_blocks][num_kv_heads][block_size][head_dim] pools."""
+def make_cache(k_pool: torch.Tensor, v_pool: torch.Tensor, k_scale: float = 1.0,
+               v_scale: float = 1.0) -> PaCache:
+    """pa_cache for two [num_blocks][num_kv_heads][block_size][head_dim] pools.
+
+    The scales are the dequantisation scales of an 8-bit (E4M3) cache; the
+    other element types ignore them.
+    """
     _require(k_pool.dim() == 4 and k_pool.shape == v_pool.shape and k_pool.dtype == v_pool.dtype,
              "k_pool and v_pool must be equal-shaped 4-D tensors")
     _require(k_pool.is_contiguous() and v_pool.is_contiguous(), "pools must be contiguous")
     nb, hkv, bs, d = k_pool.shape
-    return PaCache(k_pool.data_ptr(), v_pool.data_ptr(), nb, hkv, bs, d, _dtype_code(k_pool))
+    return PaCache(k_pool.data_ptr(), v_pool.data_ptr(), nb, hkv, bs, d, _dtype_code(k_pool),
+                   float(k_scale), float(v_scale))
 
 
 def abi_version() -> int:
@@ -125,23 +141,29 @@ def partials_bytes(num_seqs: int, num_heads: int, head_dim: int, max_parts: int)
     return load().pa_partials_bytes(num_seqs, num_heads, head_dim, max_parts)
 
 
-def pa_kv_append(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None) -> None:
-    """Write k_new/v_new [n][Hkv][D] into the pools at slot_mapping (int64 [n])."""
-    cache = make_cache(k_pool, v_pool)
+def pa_kv_append(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None, k_scale=1.0,
+                 v_scale=1.0) -> None:
+    """Write k_new/v_new [n][Hkv][D] into the pools at slot_mapping (int64 [n]).
+
+    For an 8-bit cache k_new/v_new are bf16 and are stored quantised with the
+    pools' scales.
+    """
+    cache = make_cache(k_pool, v_pool, k_scale, v_scale)
     _require(slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous(),
              "slot_mapping must be contiguous int64")
     n = slot_mapping.numel()
     for t in (k_new, v_new):
-        _require(t.dtype == k_pool.dtype and t.is_contiguous() and
+        _require(t.dtype == _token_dtype(cache) and t.is_contiguous() and
                  tuple(t.shape) == (n, cache.num_kv_heads, cache.head_dim),
-                 "k_new/v_new must be contiguous [n][num_kv_heads][head_dim] of the pool dtype")
+                 "k_new/v_new must be contiguous [n][num_kv_heads][head_dim] of the pool dtype "
+                 "(bf16 for an 8-bit cache)")
     _check(load().pa_kv_append(ctypes.byref(cache), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
                                n, _stream(stream)))
 
 
 def pa_copy_blocks(k_pool, v_pool, block_pairs, stream=None) -> None:
     """Copy block src -> dst in both pools for each row of block_pairs (int64 [n][2])."""
-    cache = make_cache(k_pool, v_pool)
+    cache = make_cache(k_pool, v_pool, 1.0, 1.0)
     _require(block_pairs.dtype == torch.int64 and block_pairs.is_contiguous() and
              (block_pairs.numel() == 0 or block_pairs.shape[-1] == 2),
              "block_pairs must be contiguous int64 [n][2]")
@@ -161,10 +183,12 @@ def decode_workspace(num_seqs: int, num_heads: int, head_dim: int,
                        dtype=torch.uint8, device=device)
 
 
-def _decode_common(k_pool, v_pool, q, block_tables, context_lens):
-    cache = make_cache(k_pool, v_pool)
-    _require(q.dim() == 3 and q.is_contiguous() and q.dtype == k_pool.dtype and
-             q.shape[2] == cache.head_dim, "q must be contiguous [num_seqs][num_heads][head_dim]")
+def _decode_common(k_pool, v_pool, q, block_tables, context_lens, k_scale, v_scale):
+    cache = make_cache(k_pool, v_pool, k_scale, v_scale)
+    _require(q.dim() == 3 and q.is_contiguous() and q.dtype == _token_dtype(cache) and
+             q.shape[2] == cache.head_dim,
+             "q must be contiguous [num_seqs][num_heads][head_dim] of the pool dtype "
+             "(bf16 for an 8-bit cache)")
     num_seqs = q.shape[0]
     _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
              block_tables.is_contiguous() and block_tables.shape[0] == num_seqs,
@@ -175,13 +199,14 @@ def _decode_common(k_pool, v_pool, q, block_tables, context_lens):
 
 
 def pa_decode(k_pool, v_pool, q, block_tables, context_lens, scale: float, out, workspace=None,
-              stream=None) -> None:
+              stream=None, k_scale=1.0, v_scale=1.0) -> None:
     """Decode attention into out [num_seqs][num_heads][head_dim].
 
     ``workspace`` (from decode_workspace()) enables the balanced split of the
-    batch; None walks each sequence in one workgroup.
+    batch; None walks each sequence in one workgroup.  ``k_scale``/``v_scale``
+    are an 8-bit cache's dequantisation scales.
     """
-    cache = _decode_common(k_pool, v_pool, q, block_tables, context_lens)
+    cache = _decode_common(k_pool, v_pool, q, block_tables, context_lens, k_scale, v_scale)
     num_seqs, num_heads = q.shape[0], q.shape[1]
     _require(out is not None and out.is_contiguous() and
              tuple(out.shape) == (num_seqs, num_heads, cache.head_dim),
@@ -196,9 +221,10 @@ def pa_decode(k_pool, v_pool, q, block_tables, context_lens, scale: float, out, 
 
 
 def pa_decode_partitions(k_pool, v_pool, q, block_tables, context_lens, scale: float,
-                         partition_size: int, part_out, part_max, part_sum, stream=None) -> None:
+                         partition_size: int, part_out, part_max, part_sum, stream=None,
+                         k_scale=1.0, v_scale=1.0) -> None:
     """Split-KV decode partials; see include/pagedattn.h."""
-    cache = _decode_common(k_pool, v_pool, q, block_tables, context_lens)
+    cache = _decode_common(k_pool, v_pool, q, block_tables, context_lens, k_scale, v_scale)
     num_seqs, num_heads = q.shape[0], q.shape[1]
     _require(part_out is not None and part_out.dim() == 4 and part_out.is_contiguous() and
              part_out.dtype == torch.float32 and

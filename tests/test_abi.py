@@ -50,10 +50,17 @@ def test_partials_bytes():
 
 def _cache(**kw):
     c = dict(k_pool=16, v_pool=32, num_blocks=4, num_kv_heads=2, block_size=16, head_dim=128,
-             dtype=lib.PA_BF16)
+             dtype=lib.PA_BF16, k_scale=1.0, v_scale=1.0)
     c.update(kw)
     return lib.PaCache(c["k_pool"], c["v_pool"], c["num_blocks"], c["num_kv_heads"],
-                       c["block_size"], c["head_dim"], c["dtype"])
+                       c["block_size"], c["head_dim"], c["dtype"], c["k_scale"], c["v_scale"])
+
+
+def test_cache_struct_layout():
+    # the C side asserts the same size and offsets (pa_api.hip)
+    assert ctypes.sizeof(lib.PaCache) == 48
+    assert lib.PaCache.dtype.offset == 36 and lib.PaCache.k_scale.offset == 40
+    assert lib.PaCache.v_scale.offset == 44
 
 
 def _decode(cache, **kw):
@@ -95,6 +102,11 @@ def _partitions(cache, **kw):
     ({}, dict(q=0), 1),
     ({}, dict(q=8), 2),                            # misaligned q
     ({}, dict(ws=256, ws_bytes=64), 4),            # workspace too small
+    (dict(dtype=lib.PA_FP8_E4M3, k_scale=0.0), {}, 2),            # 8-bit cache needs scales
+    (dict(dtype=lib.PA_FP8_E4M3, v_scale=float("nan")), {}, 2),
+    (dict(dtype=lib.PA_FP8_E4M3, k_scale=float("inf")), {}, 2),
+    (dict(dtype=lib.PA_FP8_E4M3), dict(out_dtype=lib.PA_FP8_E4M3), 3),  # no 8-bit output
+    (dict(dtype=lib.PA_F32), dict(out_dtype=lib.PA_BF16), 3),          # f32 cache: f32 out
 ])
 def test_decode_rejects_bad_arguments(cache_kw, call_kw, status):
     cache = None if cache_kw is None else _cache(**cache_kw)
@@ -138,6 +150,11 @@ def test_append_and_copy_reject_bad_arguments():
     assert call("pa_kv_append", ctypes.byref(c), 16, 16, 12, 1, None) == 2
     odd = _cache(head_dim=4, dtype=lib.PA_BF16)  # 8-byte rows cannot move in 16-byte chunks
     assert call("pa_kv_append", ctypes.byref(odd), 16, 16, 16, 1, None) == 3
+    odd8 = _cache(head_dim=8, dtype=lib.PA_FP8_E4M3)  # 8-byte rows of codes
+    assert call("pa_kv_append", ctypes.byref(odd8), 16, 16, 16, 1, None) == 3
+    noscale = _cache(dtype=lib.PA_FP8_E4M3, v_scale=-1.0)
+    assert call("pa_kv_append", ctypes.byref(noscale), 16, 16, 16, 1, None) == 2
+    assert call("pa_copy_blocks", ctypes.byref(noscale), 16, 1, None) == 2
     assert call("pa_copy_blocks", ctypes.byref(c), None, 1, None) == 1
     assert call("pa_copy_blocks", ctypes.byref(c), 16, -2, None) == 2
     assert call("pa_copy_blocks", ctypes.byref(c), 16, 0, None) == 0

@@ -1,9 +1,11 @@
 """pa_decode and pa_splitkv_reduce on the GPU against the float64 oracle.
 
 Tolerances: max abs error <= 1e-5 for float32 caches (float32 output) and
-<= 2e-2 for bfloat16 caches with a bfloat16 output.  Every named workload runs
-a whole step (copy-on-write copy, append, decode, and merge when split) at its
-full size and is compared on every output element.
+<= 2e-2 for bfloat16 caches with a bfloat16 output; the same for 8-bit (E4M3)
+caches, whose stored values are as exact in float32 as bfloat16 ones (a
+float32 output from a bf16 or 8-bit cache is held to 1e-5).  Every named
+workload runs a whole step (copy-on-write copy, append, decode, and merge when
+split) at its full size and is compared on every output element.
 """
 
 import math
@@ -41,6 +43,32 @@ def test_named_workload_step(k):
         assert err <= TOL[w.dtype], mode
 
 
+@pytest.mark.parametrize("k", [2, 3, 4, 5])
+def test_named_workload_step_fp8(k):
+    """The 8-bit copies of the named workloads: the append quantises the new
+    tokens, decode reads codes times scales; bf16 and f32 outputs."""
+    w, _, ref = named(k, "fp8")
+    t = upload(w)
+    run_writes(t)
+    for mode in MODES[k]:
+        for out_f32 in (False, True):
+            out, _ = run_decode(t, w, mode, out_f32=out_f32)
+            torch.cuda.synchronize()
+            err = max_abs_err(out, ref)
+            print(f"{w.name} mode={mode} f32={out_f32}: max abs err {err:.3g}")
+            assert err <= (1e-5 if out_f32 else TOL["fp8"]), (mode, out_f32)
+
+
+def test_long_context_block_size_32_fp8():
+    w, _, ref = named(5, "fp8", block_size=32)
+    t = upload(w)
+    run_writes(t)
+    for mode in ("balanced", "single", 512):
+        out, _ = run_decode(t, w, mode)
+        torch.cuda.synchronize()
+        assert max_abs_err(out, ref) <= TOL["fp8"], mode
+
+
 def test_long_context_block_size_32():
     w, _, ref = named(5, block_size=32)
     t = upload(w)
@@ -69,7 +97,7 @@ def test_float32_shadow_of_named_shapes(k, num_seqs):
 RAGGED = [1, 2, 15, 16, 17, 31, 32, 33, 64, 100, 257, 515]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
@@ -77,16 +105,20 @@ def test_ragged_shapes(dtype, d, bs, group):
     w = W.small_random(7 + d + bs + group, dtype=dtype, num_seqs=len(RAGGED),
                        num_heads=2 * group, num_kv_heads=2, head_dim=d, block_size=bs,
                        lens=RAGGED)
+    if dtype == "fp8":  # scales that are not powers of two
+        w.k_scale, w.v_scale = 0.0137, 0.0291
+    scales = (w.k_scale, w.v_scale) if dtype == "fp8" else None
     ref = oracle.decode(w.q, *oracle.kv_append(w.k_pool, w.v_pool, w.k_new, w.v_new,
-                                               w.slot_mapping),
-                        w.block_tables, w.context_lens, 1 / math.sqrt(d), dtype)
+                                               w.slot_mapping, fp8_scales=scales),
+                        w.block_tables, w.context_lens, 1 / math.sqrt(d), dtype,
+                        k_scale=w.k_scale, v_scale=w.v_scale)
     t = upload(w)
     run_writes(t)
     for mode in ("balanced", "single", bs, 64, 128):
-        for out_f32 in ((False, True) if dtype == "bf16" else (False,)):
+        for out_f32 in ((False, True) if dtype != "f32" else (False,)):
             out, _ = run_decode(t, w, mode, out_f32=out_f32)
             torch.cuda.synchronize()
-            tol = TOL["bf16"] if (dtype == "bf16" and not out_f32) else 1e-5
+            tol = TOL[dtype] if (dtype != "f32" and not out_f32) else 1e-5
             assert max_abs_err(out, ref) <= tol, (mode, out_f32)
 
 

@@ -12,9 +12,10 @@ from paged_kv_cache_93_amd import lib
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
-def test_step_writes_bit_exact(k):
-    w, pools, _ = named(k)
+@pytest.mark.parametrize("k,dtype", [(k, None) for k in (1, 2, 3, 4, 5)] +
+                         [(k, "fp8") for k in (2, 3, 4, 5)])
+def test_step_writes_bit_exact(k, dtype):
+    w, pools, _ = named(k, dtype)
     t = upload(w)
     run_writes(t)
     torch.cuda.synchronize()
@@ -62,11 +63,11 @@ def test_append_skips_out_of_range_slots():
     assert np.array_equal(to_host_bits(tk), ek) and np.array_equal(to_host_bits(tv), ev)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
 def test_copy_blocks_bit_exact(dtype):
     rng = np.random.default_rng(11)
     nb, hkv, bs, d = 64, 8, 16, 128
-    store = np.uint32 if dtype == "f32" else np.uint16
+    store = {"f32": np.uint32, "bf16": np.uint16, "fp8": np.uint8}[dtype]
     kp = rng.integers(0, np.iinfo(store).max, size=(nb, hkv, bs, d), dtype=store)
     vp = rng.integers(0, np.iinfo(store).max, size=(nb, hkv, bs, d), dtype=store)
     perm = rng.permutation(nb)
@@ -90,3 +91,26 @@ def test_empty_calls_change_nothing():
                                                               device="cuda"))
     torch.cuda.synchronize()
     assert np.array_equal(to_host_bits(t["k_pool"]), before)
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [(1.0, 2.0 ** -6), (0.37, 1e-4), (1e4, 3.0)])
+def test_append_fp8_quantises_every_bf16_input(k_scale, v_scale):
+    """All 65,536 bf16 bit patterns (NaN, infinities, subnormals, ties, values
+    past 448 after scaling) go through the 8-bit append; the codes written equal
+    the oracle's bit for bit, and nothing else in the pools changes."""
+    hkv, bs, d, n = 2, 16, 128, 256  # n * hkv * d = 65,536 inputs per pool
+    every = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    kn = every.reshape(n, hkv, d)
+    vn = every[::-1].copy().reshape(n, hkv, d)
+    rng = np.random.default_rng(3)
+    nb = 40
+    kp = rng.integers(0, 256, size=(nb, hkv, bs, d), dtype=np.uint8)
+    vp = rng.integers(0, 256, size=(nb, hkv, bs, d), dtype=np.uint8)
+    slots = rng.permutation(nb * bs)[:n].astype(np.int64)
+    ek, ev = oracle.kv_append(kp, vp, kn, vn, slots, fp8_scales=(k_scale, v_scale))
+    tk, tv = to_device(kp, "fp8"), to_device(vp, "fp8")
+    lib.pa_kv_append(tk, tv, to_device(kn, "bf16"), to_device(vn, "bf16"),
+                     torch.from_numpy(slots).cuda(), k_scale=k_scale, v_scale=v_scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(tk), ek)
+    assert np.array_equal(to_host_bits(tv), ev)
