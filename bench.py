@@ -96,7 +96,8 @@ def cpu_baseline(w: W.Workload, budget_s: float) -> dict:
             "seqs_per_s": round(done / dt, 3)}
 
 
-KERNEL_SOURCES = ("pa_decode_kernel.h", "pa_decode.hip", "pa_decode_bf16.hip", "pa_decode_f32.hip")
+KERNEL_SOURCES = ("pa_decode_kernel.h", "pa_decode.hip", "pa_decode_bf16.hip", "pa_decode_f32.hip",
+                  "pa_decode_fp8.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 CAL_BLOCKS = 4096  # calibration copy: blocks [0, 2048) -> [2048, 4096) of a scratch pool pair
 
