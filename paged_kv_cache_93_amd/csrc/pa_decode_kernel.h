@@ -210,6 +210,10 @@ __device__ __forceinline__ int group_of_unit(int64_t u, int64_t total, int64_t g
 
 }  // namespace dev
 
+#ifndef PA_PACE
+#define PA_PACE 1  // 0: no issue-priority pacing between the waves of a SIMD
+#endif
+
 #ifndef PA_MFMA_SCORES
 #define PA_MFMA_SCORES 1  // 0: score every case on the VALU (for comparison)
 #endif
@@ -218,10 +222,11 @@ __device__ __forceinline__ int group_of_unit(int64_t u, int64_t total, int64_t g
 constexpr bool decode_uses_mfma(int et, int d) { return PA_MFMA_SCORES && et != kF32 && d == 128; }
 
 // LDS bytes each wave of the MFMA path uses: a 16-row K tile padded to 17
-// chunks per row (conflict-free transposed reads), then the softmax weights
-// [4 row groups][G heads][4 rows] and the rescale factors [4][G].
+// chunks per row (conflict-free transposed reads), the softmax weights
+// [4 row groups][G heads][4 rows], the rescale factors [4][G], and the G
+// query rows of the sequence being scored (16 chunks of 16 bytes each).
 constexpr int decode_wave_lds_bytes(int et, int d, int g) {
-  return decode_uses_mfma(et, d) ? 16 * 17 * 16 + 64 * g + 16 * g : 0;
+  return decode_uses_mfma(et, d) ? 16 * 17 * 16 + 64 * g + 16 * g + 256 * g : 0;
 }
 
 // Byte offset of the per-wave LDS areas behind the unit prefix (balanced mode).
@@ -241,6 +246,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   constexpr int LPR = D / VEC;                       // lanes per row
   constexpr int RPI = 64 / LPR;                      // rows per load instruction
   constexpr bool MF = decode_uses_mfma(ET, D);       // q.k on MFMA (16-row tiles)
+  constexpr int QC = MF ? (16 * G + 63) / 64 : 1;    // query chunks a lane loads per tile
   constexpr int TRW = MF ? 16 : (G >= 8 ? 2 : 4) * RPI;  // wide groups keep smaller tiles
   constexpr int TR = BS < TRW ? BS : TRW;            // rows per register tile
   constexpr int NI = TR / RPI;                       // load instructions per tile
@@ -328,6 +334,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   u32x4* lds_k = reinterpret_cast<u32x4*>(wave_lds);              // [16 rows][17 chunks]
   float* lds_p = reinterpret_cast<float*>(wave_lds + 16 * 17 * 16);  // [4][G][4]
   float* lds_a = lds_p + 16 * G;                                   // [4][G]
+  u32x4* lds_q = reinterpret_cast<u32x4*>(lds_a + 4 * G);          // [G][16 chunks]
 
   const size_t head_bytes = size_t(BS) * D * EB;
   const size_t block_bytes = head_bytes * a.num_kv_heads;
@@ -360,7 +367,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   float m[G], l[G], acc[G][VEC];
   float mf_m = kNegInf, mf_l = 0.f;
   u32x4 qc[MF ? 1 : G];  // VALU path: chunk c of each head's query
-  u32x4 qf[1];           // placeholder for load_q's unused MFMA operand
+  u32x4 qf[MF ? 4 : 1];  // MFMA path: the current sequence's query as B operands
 
   // Emit the finished piece of sequence `seq`: the final output when the piece
   // is the whole sequence, else a partial row.
@@ -545,10 +552,14 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   }
   reset_state();
 
-  // Loads tile t into (kr, vr) and, on the MFMA path, the query of its
-  // sequence into qr, so a tile always arrives with the query it is scored
-  // against and a piece boundary needs no query load.
-  auto load_tile = [&](Raw(&kr)[NI], Raw(&vr)[NI], u32x4(&qr)[MF ? 4 : 1], int t) {
+  // Loads tile t into (kr, vr).  On the MFMA path a tile that starts a new
+  // sequence in the walk also brings the G query rows of that sequence in qr
+  // (one 16-byte chunk per lane, QC per lane for G = 8): the query arrives in
+  // the ring with the first tile it is scored against, so a piece boundary
+  // needs no separate query load, and other tiles load no query at all.
+  int q_loaded = -1;     // sequence of the last query loaded into the ring
+  int q_staged = -1;     // sequence whose query rows sit in lds_q
+  auto load_tile = [&](Raw(&kr)[NI], Raw(&vr)[NI], u32x4(&qr)[QC], int t) {
     int phys = -1, sq = 0;
     size_t off = 0;
     if (t < ntiles) {
@@ -563,8 +574,16 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
       off = size_t(t % TPB) * (TR * D * EB);
     }
     if constexpr (MF) {
-      u32x4 unused[1];
-      load_q(sq, unused, qr);
+      if (t < ntiles && sq != q_loaded) {
+        q_loaded = sq;
+        const u32x4* qrow =
+            reinterpret_cast<const u32x4*>(a.q + (size_t(sq) * a.num_heads + head0) * D * QEB);
+#pragma unroll
+        for (int j = 0; j < QC; ++j) {
+          const int ch = lane + 64 * j;
+          qr[j] = qrow[ch < 16 * G ? ch : ch % (16 * G)];  // lanes past the rows repeat one
+        }
+      }
     }
     if (phys < 0 || int64_t(phys) >= a.num_blocks) {
       phys = 0;
@@ -573,6 +592,9 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     off += size_t(phys) * block_bytes;
     // VALU path: instruction i holds rows i*RPI + r.  MFMA path: rows 4r + i,
     // so each row group sees 4 consecutive rows, as the MFMA result rows.
+    // (Every instruction reads 1 KiB of whole rows; loading K straight in
+    // the MFMA operand layout instead - 64-byte pieces of 16 rows - was
+    // measured slower than transposing it through LDS.)
     const int lo = MF ? r * 64 + c : lane;
     constexpr int step = MF ? 16 : 64;
     const Raw* kp = reinterpret_cast<const Raw*>(kbase + off) + lo;
@@ -584,8 +606,8 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     }
   };
 
-  auto process_tile = [&](const Raw(&kr)[NI], const Raw(&vr)[NI],
-                          const u32x4(&qr)[MF ? 4 : 1], int t) {
+  auto process_tile = [&](const Raw(&kr)[NI], const Raw(&vr)[NI], const u32x4(&qr)[QC],
+                          int t) {
     const int idx = int(ubeg + t / TPB - cbase);
     const int phys = __builtin_amdgcn_readlane(w0.ek, idx);
     int len = __builtin_amdgcn_readlane(w0.lk, idx);
@@ -596,18 +618,37 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     const bool partial = nvalid < TR;
     if constexpr (MF) {
       // K tile -> LDS, then read back transposed: lane 16g + t gets row t's
-      // dims [32mm + 8g, 32mm + 8g + 8) as the A operand of MFMA mm.
+      // dims [32mm + 8g, 32mm + 8g + 8) as the A operand of MFMA mm, and lane
+      // 16g + h holds the same dims of query head h as B (h < G; the other
+      // lanes repeat a head whose score column is never used).  The first
+      // tile of a sequence brought its query rows (see load_tile): they go
+      // through LDS into the B layout once, and stay in qf after.
 #pragma unroll
       for (int i = 0; i < 4; ++i) lds_k[(4 * r + i) * 17 + c] = score_chunk<ET>(kr[i]);
-      __builtin_amdgcn_wave_barrier();
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      const int tseq = __builtin_amdgcn_readlane(w0.sk, idx);
+      if (tseq != q_staged) {
+        q_staged = tseq;
 #pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
-        const u32x4 kf = lds_k[(lane & 15) * 17 + 4 * mm + (lane >> 4)];
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf),
-                                                     __builtin_bit_cast(bf16x8, qr[mm]),
-                                                     sc, 0, 0, 0);
+        for (int j = 0; j < QC; ++j)
+          if (lane + 64 * j < 16 * G) lds_q[lane + 64 * j] = qr[j];
+        __builtin_amdgcn_wave_barrier();
+        const int qh = (lane & 15) % G;
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) qf[mm] = lds_q[qh * 16 + 4 * mm + (lane >> 4)];
       }
+      // two independent accumulation chains of two MFMAs each
+      f32x4 sc_even = {0.f, 0.f, 0.f, 0.f}, sc_odd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mm = 0; mm < 4; mm += 2) {
+        const u32x4 ka = lds_k[(lane & 15) * 17 + 4 * mm + (lane >> 4)];
+        const u32x4 kb2 = lds_k[(lane & 15) * 17 + 4 * (mm + 1) + (lane >> 4)];
+        sc_even = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, ka), __builtin_bit_cast(bf16x8, qf[mm]), sc_even, 0, 0, 0);
+        sc_odd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, kb2), __builtin_bit_cast(bf16x8, qf[mm + 1]), sc_odd, 0,
+            0, 0);
+      }
+      const f32x4 sc = sc_even + sc_odd;
       // lane 16g + h: scores of rows 4g + v (v = 0..3), head h
       const int g4 = 4 * (lane >> 4);
       float sv[4];
@@ -741,7 +782,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   // After each tile a wave publishes its progress and runs at raised priority
   // while it is not ahead of its partner.
   auto pace = [&](int t) {
-    if (nwave != 8) return;
+    if (!PA_PACE || nwave != 8) return;
     s_prog[wave] = t;
     if (t > s_prog[wave ^ 4])
       __builtin_amdgcn_s_setprio(0);
@@ -750,7 +791,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   };
 
   Raw kb[NB][NI], vb[NB][NI];
-  u32x4 qb[NB][MF ? 4 : 1];
+  u32x4 qb[NB][QC];
 #pragma unroll
   for (int i = 0; i < PF; ++i) load_tile(kb[i], vb[i], qb[i], i);
   for (int t0 = 0; t0 < ntiles; t0 += NB) {
