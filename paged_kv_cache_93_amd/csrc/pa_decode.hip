@@ -190,11 +190,11 @@ PA_API int pa_decode(const pa_cache* cache, const void* q, const int32_t* block_
   m.out = out;
   m.num_heads = num_heads;
   m.out_f32 = a.out_f32;
-  const dim3 mgrid(static_cast<unsigned>(num_heads), static_cast<unsigned>(num_seqs));
+  const dim3 mgrid(static_cast<unsigned>((num_heads + 3) / 4), static_cast<unsigned>(num_seqs));
   if (cache->head_dim == 64)
-    hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(64), 0, s, m);
+    hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(256), 0, s, m);
   else
-    hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(64), 0, s, m);
+    hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(256), 0, s, m);
   return launch_result(fn);
 }
 

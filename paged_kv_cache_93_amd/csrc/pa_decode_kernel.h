@@ -117,6 +117,19 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Inclusive prefix sum over the 64 lanes: shifted adds inside each row of 16
+// lanes (DPP row_shr), then the running totals of rows 0 and 0..1 carried
+// into the rows after them (DPP row_bcast:15 and row_bcast:31).
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
 template <bool NT, class T>
 __device__ __forceinline__ T load_chunk(const T* p) {
   if constexpr (NT)
@@ -288,14 +301,9 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
       int carry = 0;
       for (int base = 0; base < S; base += 64) {
         const int i = base + lane;
-        int v = i < S ? s_prefix[i + 1] : 0;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const int up = __shfl_up(v, off);
-          if (lane >= off) v += up;
-        }
+        const int v = wave_inclusive_sum(i < S ? s_prefix[i + 1] : 0);
         if (i < S) s_prefix[i + 1] = carry + v;
-        carry += __shfl(v, 63);
+        carry += __builtin_amdgcn_readlane(v, 63);
       }
     }
     __syncthreads();
@@ -819,23 +827,25 @@ struct MergeArgs {
 };
 
 // Merge the pieces of sequences split between workgroups (balanced mode) and
-// write zeros for empty sequences.  One wave per (sequence, query head).
+// write zeros for empty sequences.  One wave per (sequence, query head), four
+// heads per workgroup.
 // After one read of the split description, the pieces' maxima and sums (lane p
 // holds piece p) and their output rows (16-byte loads; LR lanes cover a row,
 // so one load instruction brings 64/LR pieces) are all in flight at once.
 // Pieces are taken 64 at a time with the running log-sum-exp rescale, and
 // their rows in batches of NBATCH load instructions.
 template <int D>
-__global__ void __launch_bounds__(64) merge_kernel(MergeArgs a) {
+__global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
   using namespace dev;
   constexpr int LR = D / 4;          // lanes per row
   constexpr int PPI = 64 / LR;       // pieces per load instruction
   constexpr int NBATCH = 8;          // load instructions per batch
   constexpr int PB = PPI * NBATCH;   // pieces per batch
   static_assert(64 % LR == 0 && 64 % PB == 0, "merge tiling");
-  const int lane = threadIdx.x;
-  const int head = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int head = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int seq = blockIdx.y;
+  if (head >= a.num_heads) return;
   const int sub = lane / LR;         // which piece of an instruction this lane reads
   const int col = (lane % LR) * 4;   // its 4 dims
   const int64_t groups = a.info[0];
