@@ -117,6 +117,51 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The values of lanes l and l ^ OFF, lower lane first, in both lanes.  OFF = 16
+// and 32 use gfx950's lane swaps (v_permlane16/32_swap: plain VALU, no LDS
+// round trip); smaller offsets a shuffle.
+template <int OFF>
+__device__ __forceinline__ void xor_pair(float x, float& lo, float& hi) {
+  const unsigned int u = __float_as_uint(x);
+  if constexpr (OFF == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+  } else if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+  } else {
+    const float o = __shfl_xor(x, OFF);
+    const bool upper = (threadIdx.x & OFF) != 0;
+    lo = upper ? o : x;
+    hi = upper ? x : o;
+  }
+}
+
+// Sum (or max) over lanes that differ only in bits FROM.. of the lane index
+// (FROM a power of two); every lane of a set gets the same bits.
+template <int FROM>
+__device__ __forceinline__ float xor_sum(float x) {
+  if constexpr (FROM >= 64) {
+    return x;
+  } else {
+    float lo, hi;
+    xor_pair<FROM>(x, lo, hi);
+    return xor_sum<FROM * 2>(lo + hi);
+  }
+}
+template <int FROM>
+__device__ __forceinline__ float xor_max(float x) {
+  if constexpr (FROM >= 64) {
+    return x;
+  } else {
+    float lo, hi;
+    xor_pair<FROM>(x, lo, hi);
+    return xor_max<FROM * 2>(fmaxf(lo, hi));
+  }
+}
+
 // Inclusive prefix sum over the 64 lanes: shifted adds inside each row of 16
 // lanes (DPP row_shr), then the running totals of rows 0 and 0..1 carried
 // into the rows after them (DPP row_bcast:15 and row_bcast:31).
@@ -397,20 +442,11 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     // merge the RPI row groups (lanes that differ in r)
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float big = m[h];
-#pragma unroll
-      for (int off = LPR; off < 64; off <<= 1) big = fmaxf(big, __shfl_xor(big, off));
+      const float big = xor_max<LPR>(m[h]);
       const float f = (m[h] == kNegInf) ? 0.f : fast_exp2(m[h] - big);
-      float lw = l[h] * f;
+      const float lw = xor_sum<LPR>(l[h] * f);
 #pragma unroll
-      for (int off = LPR; off < 64; off <<= 1) lw += __shfl_xor(lw, off);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        float x = acc[h][e] * f;
-#pragma unroll
-        for (int off = LPR; off < 64; off <<= 1) x += __shfl_xor(x, off);
-        acc[h][e] = x;
-      }
+      for (int e = 0; e < VEC; ++e) acc[h][e] = xor_sum<LPR>(acc[h][e] * f);
       m[h] = big;
       l[h] = lw;
     }
