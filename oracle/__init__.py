@@ -5,8 +5,9 @@ TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT. Only ``tests/``,
 import or call anything in this package. The HIP library never imports it, and
 nothing here imports the HIP library or its Python binding.
 
-Everything is plain NumPy in float64; see ``paged_attention.py`` for the
-passages each function follows.
+Attention is plain NumPy in float64 (``paged_attention.py``); the block
+manager and its per-step scheduler are plain Python (``block_manager.py``).
+Each module lists the passages it follows.
 """
 
 from .paged_attention import (  # noqa: F401
