@@ -12,8 +12,9 @@
  * ----------------------------------------
  * - Pointers marked DEVICE are HIP device pointers; HOST pointers are read
  *   before the call returns.  The caller allocates and frees every buffer;
- *   the library allocates nothing and keeps no state besides a per-thread
- *   error message.
+ *   the device entry points below allocate nothing and keep no state besides
+ *   a per-thread error message.  (The block manager of pa_block_manager.h
+ *   owns host memory for its own state between its create and destroy calls.)
  * - `stream` is a hipStream_t (NULL = the null stream).  Every call only
  *   enqueues work on it and returns without synchronising; results are
  *   visible after the stream is synchronised.
@@ -50,7 +51,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -58,7 +59,10 @@ typedef enum pa_status {
   PA_ERR_SHAPE = 2,       /* sizes are negative, inconsistent, or misaligned */
   PA_ERR_UNSUPPORTED = 3, /* a valid request this build has no kernel for */
   PA_ERR_WORKSPACE = 4,   /* workspace or split-KV partial buffers missing or too small */
-  PA_ERR_LAUNCH = 5       /* the HIP runtime refused a launch */
+  PA_ERR_LAUNCH = 5,      /* the HIP runtime refused a launch */
+  PA_ERR_ID = 6,          /* unknown request id, or an id already in use (block manager) */
+  PA_ERR_STATE = 7,       /* the request's state does not allow the call (block manager) */
+  PA_ERR_NOMEM = 8        /* host memory for the block manager could not be allocated */
 } pa_status;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
@@ -129,6 +133,34 @@ int pa_kv_append(const pa_cache *cache, const void *k_new, const void *v_new,
  */
 int pa_copy_blocks(const pa_cache *cache, const int64_t *block_pairs, int32_t num_pairs,
                    void *stream);
+
+/*
+ * pa_swap_blocks - whole-block copies between the device pools and pinned host
+ * pools: the data movement of swapping.
+ *
+ * When the block pool runs dry, a preempted request's KV can be copied to
+ * pinned CPU memory and copied back when blocks free up ("LLM paged attention
+ * arch", section "The architecture: every piece explained").  For each pair
+ * (a, b) = (block_pairs[2p], block_pairs[2p+1]):
+ *   PA_SWAP_OUT:  host block b  <- device block a   (K and V pools)
+ *   PA_SWAP_IN:   device block b <- host block a
+ * every KV head and row, bit for bit.  Pairs whose ids fall outside their pool
+ * are skipped.
+ *
+ *   cache            HOST   the device pools
+ *   host_k_pool,     HOST   pinned host memory (hipHostMalloc, or a pinned torch
+ *   host_v_pool             tensor) laid out like the device pools, with
+ *                           host_num_blocks blocks of the same type; 16-byte aligned
+ *   block_pairs      DEVICE int64 [num_pairs][2]; destinations distinct
+ *   direction        PA_SWAP_OUT or PA_SWAP_IN
+ * Host pools the HIP runtime does not know as pinned memory mapped for the
+ * device are refused (PA_ERR_SHAPE) before anything is enqueued.
+ */
+enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 };
+
+int pa_swap_blocks(const pa_cache *cache, void *host_k_pool, void *host_v_pool,
+                   int64_t host_num_blocks, const int64_t *block_pairs, int32_t num_pairs,
+                   int32_t direction, void *stream);
 
 /*
  * pa_decode - attention of one query token per sequence over its paged cache.

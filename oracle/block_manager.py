@@ -142,6 +142,11 @@ class BlockManager:
         self._arrivals = 0
         self._cow_sources = set()   # reading 7, per step
         self._deferred = []
+        # running totals: the telemetry the pages name (block use, preemption
+        # rate, prefix hit rate; "LLM paged attention arch", section "The
+        # architecture: every piece explained")
+        self.totals = dict(preemptions=0, swapped_out_blocks=0, swapped_in_blocks=0,
+                           cow_copies=0, prefix_hit_tokens=0, admitted_tokens=0)
 
     # -- request lifecycle ---------------------------------------------------
 
@@ -242,6 +247,8 @@ class BlockManager:
                 r.blocks = list(hits)
                 r.computed = cached
                 r.state = RUNNING
+                self.totals["prefix_hit_tokens"] += cached
+                self.totals["admitted_tokens"] += len(r.tokens)
                 self._schedule(r, n, plan)
                 budget -= n
 
@@ -305,6 +312,7 @@ class BlockManager:
             r.blocks[j] = new
             plan.cow_pairs.append((old, new))
             self._cow_sources.add(old)
+            self.totals["cow_copies"] += 1
         while len(r.blocks) < self._blocks_for(c + n):
             r.blocks.append(self._pop_gpu())
         if self.prefix_caching:
@@ -333,11 +341,13 @@ class BlockManager:
         return hits
 
     def _preempt(self, r: Request, plan: StepPlan) -> None:
+        self.totals["preemptions"] += 1
         if self.preempt_mode == SWAP and len(self.cpu_free) >= len(r.blocks):
             for b in r.blocks:
                 cb = self.cpu_free.pop(0)
                 r.cpu_blocks.append(cb)
                 plan.swap_out.append((b, cb))
+            self.totals["swapped_out_blocks"] += len(r.blocks)
             self._release(r)
             r.state = SWAPPED
             plan.preempted.append((r.rid, SWAP))
@@ -352,6 +362,7 @@ class BlockManager:
             b = self._pop_gpu()
             r.blocks.append(b)
             plan.swap_in.append((cb, b))
+        self.totals["swapped_in_blocks"] += len(r.cpu_blocks)
         for cb in reversed(r.cpu_blocks):
             self.cpu_free.append(cb)
         r.cpu_blocks = []
@@ -369,9 +380,9 @@ class BlockManager:
 
     def stats(self) -> dict:
         states = [r.state for r in self.requests.values()]
-        return dict(free_gpu=len(self.free), free_cpu=len(self.cpu_free),
+        return dict(free_gpu_blocks=len(self.free), free_cpu_blocks=len(self.cpu_free),
                     cached_blocks=len(self.cache), running=states.count(RUNNING),
-                    waiting=states.count(WAITING), swapped=states.count(SWAPPED))
+                    waiting=states.count(WAITING), swapped=states.count(SWAPPED), **self.totals)
 
 
 def swap_blocks(dst_pool, src_pool, pairs):

@@ -1,7 +1,9 @@
 """Build libpagedattn.so in-tree with hipcc for gfx950.
 
-Every HIP source under ``csrc/`` is compiled to an object in parallel, then
-linked into ``paged_kv_cache_93_amd/libpagedattn.so``.  Run as a module
+Every HIP source under ``csrc/`` is compiled to an object with hipcc, every
+host-only C++ source (``*.cpp``: the block manager) with the host C++
+compiler, all in parallel; the objects are linked into
+``paged_kv_cache_93_amd/libpagedattn.so``.  Run as a module
 (``python -m paged_kv_cache_93_amd.build``) or call :func:`build`.
 """
 
@@ -37,6 +39,18 @@ COMMON_FLAGS = [
 ]
 
 
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wextra",
+              "-Wno-unused-parameter", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def host_cxx() -> str:
+    for name in ("g++", "c++", "clang++"):
+        path = shutil.which(name)
+        if path:
+            return path
+    raise RuntimeError("no host C++ compiler found")
+
+
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -55,7 +69,7 @@ def _run(cmd):
 
 def build(verbose: bool = False, jobs: int | None = None, defines=(), out: str = LIB_PATH,
           build_dir: str = BUILD_DIR) -> str:
-    """Compile every csrc/*.hip and link a shared library; returns its path.
+    """Compile every csrc/*.hip and csrc/*.cpp and link a shared library; returns its path.
 
     ``defines`` are extra ``NAME=VALUE`` preprocessor definitions (tuning
     knobs); ``out`` is the library path (default: the in-tree libpagedattn.so).
@@ -68,6 +82,10 @@ def build(verbose: bool = False, jobs: int | None = None, defines=(), out: str =
     flags = [*COMMON_FLAGS, *(f"-D{d}" for d in defines)]
     objects = [os.path.join(build_dir, os.path.basename(s) + ".o") for s in sources]
     cmds = [[cc, *flags, "-c", src, "-o", obj] for src, obj in zip(sources, objects)]
+    for src in sorted(glob.glob(os.path.join(CSRC, "*.cpp"))):
+        obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+        objects.append(obj)
+        cmds.append([host_cxx(), *HOST_FLAGS, *(f"-D{d}" for d in defines), "-c", src, "-o", obj])
     jobs = jobs or min(len(cmds), os.cpu_count() or 4, 16)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         for log in ex.map(_run, cmds):

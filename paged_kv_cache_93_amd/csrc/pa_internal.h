@@ -5,14 +5,10 @@
 
 #include <cstdint>
 
+#include "pa_status.h"
 #include "pagedattn.h"
 
-#define PA_API extern "C" __attribute__((visibility("default")))
-
 namespace pa {
-
-// Records a formatted message for pa_last_error() and returns `status`.
-int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
 // Checks hipGetLastError() after a launch; PA_OK or PA_ERR_LAUNCH.
 int launch_result(const char* what);

@@ -1,8 +1,10 @@
-// KV writes of a decode step: the new-token append through the slot mapping
-// and the block copy of copy-on-write.  Both are 16-byte data movement: every
-// thread writes one 16-byte chunk, consecutive threads write consecutive
-// chunks of a row, so each wave reads and writes whole contiguous runs.  An
-// 8-bit cache's append reads 32 bytes of bf16 per chunk and quantises them.
+// KV writes of a decode step: the new-token append through the slot mapping,
+// the block copy of copy-on-write, and the block copies of swapping between
+// the device pools and pinned host pools.  All are 16-byte data movement:
+// every thread writes one 16-byte chunk, consecutive threads write
+// consecutive chunks of a block, so each wave reads and writes whole
+// contiguous runs.  An 8-bit cache's append reads 32 bytes of bf16 per chunk
+// and quantises them.
 #include "pa_internal.h"
 
 namespace pa {
@@ -95,16 +97,23 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
 }
 
 struct CopyArgs {
-  uint8_t* k_pool;
-  uint8_t* v_pool;
+  const uint8_t* src_k;
+  const uint8_t* src_v;
+  uint8_t* dst_k;
+  uint8_t* dst_v;
   const int64_t* pairs;
-  int64_t num_blocks;
+  int64_t src_blocks;        // blocks in the source pools
+  int64_t dst_blocks;        // blocks in the destination pools
   int64_t chunks_per_block;  // heads * block_size * head_dim * element bytes / 16
   int64_t total_chunks;      // num_pairs * 2 * chunks_per_block
 };
 
-// "Paged Attention as a Memory Manager", section "Prefix Caching and
-// Copy-on-Write": the fresh block receives a copy of the shared block's content.
+// Whole-block copies, block src of the source pools to block dst of the
+// destination pools.  Copy-on-write copies inside the device pools ("Paged
+// Attention as a Memory Manager", section "Prefix Caching and Copy-on-Write":
+// the fresh block receives a copy of the shared block's content); a swap
+// copies between the device pools and pinned host pools ("LLM paged attention
+// arch", section "The architecture: every piece explained").
 __global__ void __launch_bounds__(kThreads) copy_kernel(CopyArgs a) {
   const int64_t stride = int64_t(gridDim.x) * kThreads;
   for (int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x; idx < a.total_chunks;
@@ -115,9 +124,10 @@ __global__ void __launch_bounds__(kThreads) copy_kernel(CopyArgs a) {
     const int64_t pair = rest >> 1;
     const int64_t src = a.pairs[2 * pair];
     const int64_t dst = a.pairs[2 * pair + 1];
-    if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) continue;
-    uint4* pool = reinterpret_cast<uint4*>(is_v ? a.v_pool : a.k_pool);
-    pool[dst * a.chunks_per_block + chunk] = pool[src * a.chunks_per_block + chunk];
+    if (src < 0 || src >= a.src_blocks || dst < 0 || dst >= a.dst_blocks) continue;
+    const uint4* from = reinterpret_cast<const uint4*>(is_v ? a.src_v : a.src_k);
+    uint4* to = reinterpret_cast<uint4*>(is_v ? a.dst_v : a.dst_k);
+    to[dst * a.chunks_per_block + chunk] = from[src * a.chunks_per_block + chunk];
   }
 }
 
@@ -162,6 +172,38 @@ PA_API int pa_kv_append(const pa_cache* cache, const void* k_new, const void* v_
   return launch_result("pa_kv_append");
 }
 
+namespace pa {
+namespace {
+
+int launch_copy(CopyArgs a, int32_t num_pairs, const pa_cache* cache, hipStream_t stream,
+                const char* fn) {
+  a.chunks_per_block = int64_t(cache->num_kv_heads) * cache->block_size * cache->head_dim *
+                       element_bytes(cache->dtype) / 16;
+  a.total_chunks = int64_t(num_pairs) * 2 * a.chunks_per_block;
+  hipLaunchKernelGGL(copy_kernel, dim3(grid_for(a.total_chunks)), dim3(kThreads), 0, stream, a);
+  return launch_result(fn);
+}
+
+// Device address of pinned host memory, or nullptr if the HIP runtime does not
+// know `host` as pinned memory mapped for the current device.
+void* mapped_host(void* host) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, host) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (attr.type != hipMemoryTypeHost) return nullptr;
+  void* dev = nullptr;
+  if (hipHostGetDevicePointer(&dev, host, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return dev;
+}
+
+}  // namespace
+}  // namespace pa
+
 PA_API int pa_copy_blocks(const pa_cache* cache, const int64_t* block_pairs, int32_t num_pairs,
                           void* stream) {
   using namespace pa;
@@ -172,14 +214,52 @@ PA_API int pa_copy_blocks(const pa_cache* cache, const int64_t* block_pairs, int
   if ((reinterpret_cast<uintptr_t>(block_pairs) & 7u) != 0)
     return fail(PA_ERR_SHAPE, "pa_copy_blocks: block_pairs must be 8-byte aligned");
   CopyArgs a;
-  a.k_pool = static_cast<uint8_t*>(cache->k_pool);
-  a.v_pool = static_cast<uint8_t*>(cache->v_pool);
+  a.src_k = static_cast<const uint8_t*>(cache->k_pool);
+  a.src_v = static_cast<const uint8_t*>(cache->v_pool);
+  a.dst_k = static_cast<uint8_t*>(cache->k_pool);
+  a.dst_v = static_cast<uint8_t*>(cache->v_pool);
   a.pairs = block_pairs;
-  a.num_blocks = cache->num_blocks;
-  a.chunks_per_block = int64_t(cache->num_kv_heads) * cache->block_size * cache->head_dim *
-                       element_bytes(cache->dtype) / 16;
-  a.total_chunks = int64_t(num_pairs) * 2 * a.chunks_per_block;
-  hipLaunchKernelGGL(copy_kernel, dim3(grid_for(a.total_chunks)), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
-  return launch_result("pa_copy_blocks");
+  a.src_blocks = a.dst_blocks = cache->num_blocks;
+  return launch_copy(a, num_pairs, cache, static_cast<hipStream_t>(stream), "pa_copy_blocks");
+}
+
+PA_API int pa_swap_blocks(const pa_cache* cache, void* host_k_pool, void* host_v_pool,
+                          int64_t host_num_blocks, const int64_t* block_pairs, int32_t num_pairs,
+                          int32_t direction, void* stream) {
+  using namespace pa;
+  if (int st = check_cache(cache, "pa_swap_blocks")) return st;
+  if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN)
+    return fail(PA_ERR_SHAPE, "pa_swap_blocks: direction must be PA_SWAP_OUT or PA_SWAP_IN");
+  if (num_pairs < 0 || host_num_blocks < 0)
+    return fail(PA_ERR_SHAPE, "pa_swap_blocks: num_pairs and host_num_blocks must be >= 0");
+  if (num_pairs == 0) return PA_OK;
+  if (!block_pairs || !host_k_pool || !host_v_pool)
+    return fail(PA_ERR_NULL, "pa_swap_blocks: block_pairs or a host pool is NULL");
+  if ((reinterpret_cast<uintptr_t>(block_pairs) & 7u) != 0)
+    return fail(PA_ERR_SHAPE, "pa_swap_blocks: block_pairs must be 8-byte aligned");
+  if (!aligned16(host_k_pool) || !aligned16(host_v_pool))
+    return fail(PA_ERR_SHAPE, "pa_swap_blocks: host pools must be 16-byte aligned");
+  void* hk = mapped_host(host_k_pool);
+  void* hv = mapped_host(host_v_pool);
+  if (!hk || !hv)
+    return fail(PA_ERR_SHAPE, "pa_swap_blocks: host pools must be pinned host memory mapped "
+                              "for the device (hipHostMalloc or a pinned tensor)");
+  CopyArgs a;
+  a.pairs = block_pairs;
+  if (direction == PA_SWAP_OUT) {
+    a.src_k = static_cast<const uint8_t*>(cache->k_pool);
+    a.src_v = static_cast<const uint8_t*>(cache->v_pool);
+    a.dst_k = static_cast<uint8_t*>(hk);
+    a.dst_v = static_cast<uint8_t*>(hv);
+    a.src_blocks = cache->num_blocks;
+    a.dst_blocks = host_num_blocks;
+  } else {
+    a.src_k = static_cast<const uint8_t*>(hk);
+    a.src_v = static_cast<const uint8_t*>(hv);
+    a.dst_k = static_cast<uint8_t*>(cache->k_pool);
+    a.dst_v = static_cast<uint8_t*>(cache->v_pool);
+    a.src_blocks = host_num_blocks;
+    a.dst_blocks = cache->num_blocks;
+  }
+  return launch_copy(a, num_pairs, cache, static_cast<hipStream_t>(stream), "pa_swap_blocks");
 }

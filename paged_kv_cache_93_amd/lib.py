@@ -20,13 +20,19 @@ PA_OK = 0
 PA_F32 = 0
 PA_BF16 = 1
 PA_FP8_E4M3 = 2
+PA_SWAP_OUT = 0
+PA_SWAP_IN = 1
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED",
-                4: "PA_ERR_WORKSPACE", 5: "PA_ERR_LAUNCH"}
+                4: "PA_ERR_WORKSPACE", 5: "PA_ERR_LAUNCH", 6: "PA_ERR_ID", 7: "PA_ERR_STATE",
+                8: "PA_ERR_NOMEM"}
 
-# Every symbol include/pagedattn.h declares.
+# Every symbol include/pagedattn.h and include/pa_block_manager.h declare.
 EXPORTED = ("pa_abi_version", "pa_hip_runtime_version", "pa_last_error", "pa_kv_append",
-            "pa_copy_blocks", "pa_decode", "pa_decode_workspace_bytes", "pa_decode_partitions",
-            "pa_splitkv_reduce", "pa_partials_bytes")
+            "pa_copy_blocks", "pa_swap_blocks", "pa_decode", "pa_decode_workspace_bytes",
+            "pa_decode_partitions", "pa_splitkv_reduce", "pa_partials_bytes",
+            "pa_bm_create", "pa_bm_destroy", "pa_bm_add_request", "pa_bm_append_tokens",
+            "pa_bm_fork", "pa_bm_finish", "pa_bm_schedule", "pa_bm_get_stats",
+            "pa_bm_request_info", "pa_bm_blocks", "pa_bm_refcounts", "pa_bm_free_list")
 
 
 class PagedAttnError(RuntimeError):
@@ -43,6 +49,42 @@ class PaCache(ctypes.Structure):
                 ("v_scale", ctypes.c_float)]
 
 
+class PaBmConfig(ctypes.Structure):
+    _fields_ = [("num_gpu_blocks", ctypes.c_int64), ("num_cpu_blocks", ctypes.c_int64),
+                ("block_size", ctypes.c_int32), ("prefix_caching", ctypes.c_int32),
+                ("preempt_mode", ctypes.c_int32), ("watermark_blocks", ctypes.c_int32)]
+
+
+_P64, _P32 = ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)
+
+
+class PaStepPlan(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_tokens", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32), ("num_cow", ctypes.c_int32),
+                ("num_swap_out", ctypes.c_int32), ("num_swap_in", ctypes.c_int32),
+                ("num_preempted", ctypes.c_int32),
+                ("seq_ids", _P64), ("query_start", _P32), ("context_lens", _P32),
+                ("slot_mapping", _P64), ("block_tables", _P32), ("cow_pairs", _P64),
+                ("swap_out_pairs", _P64), ("swap_in_pairs", _P64), ("preempted_ids", _P64),
+                ("preempted_modes", _P32)]
+
+
+_BM_STATS = ("free_gpu_blocks", "free_cpu_blocks", "cached_blocks", "running", "waiting",
+             "swapped", "preemptions", "swapped_out_blocks", "swapped_in_blocks", "cow_copies",
+             "prefix_hit_tokens", "admitted_tokens")
+
+
+class PaBmStats(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int64) for name in _BM_STATS]
+
+
+class PaRequestInfo(ctypes.Structure):
+    _fields_ = [("state", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("arrival", ctypes.c_int64), ("num_tokens", ctypes.c_int64),
+                ("computed", ctypes.c_int64), ("num_blocks", ctypes.c_int64),
+                ("num_cpu_blocks", ctypes.c_int64)]
+
+
 _lib = None
 _vp, _i32, _i64, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
 _SIGNATURES = {
@@ -51,6 +93,8 @@ _SIGNATURES = {
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_kv_append": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _vp, _vp, _i32, _vp]),
     "pa_copy_blocks": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _i32, _vp]),
+    "pa_swap_blocks": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _vp, _i64, _vp, _i32, _i32,
+                                      _vp]),
     "pa_decode": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _vp, _vp, _i32, _i32, _i32, _f32,
                                  _vp, _i32, _vp, ctypes.c_size_t, _vp]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32]),
@@ -59,6 +103,18 @@ _SIGNATURES = {
     "pa_splitkv_reduce": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp,
                                          _i32, _vp, _vp]),
     "pa_partials_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32]),
+    "pa_bm_create": (ctypes.c_int, [ctypes.POINTER(PaBmConfig), ctypes.POINTER(_vp)]),
+    "pa_bm_destroy": (None, [_vp]),
+    "pa_bm_add_request": (ctypes.c_int, [_vp, _i64, _vp, _i64]),
+    "pa_bm_append_tokens": (ctypes.c_int, [_vp, _i64, _vp, _i64]),
+    "pa_bm_fork": (ctypes.c_int, [_vp, _i64, _i64]),
+    "pa_bm_finish": (ctypes.c_int, [_vp, _i64]),
+    "pa_bm_schedule": (ctypes.c_int, [_vp, _i64, ctypes.POINTER(PaStepPlan)]),
+    "pa_bm_get_stats": (ctypes.c_int, [_vp, ctypes.POINTER(PaBmStats)]),
+    "pa_bm_request_info": (ctypes.c_int, [_vp, _i64, ctypes.POINTER(PaRequestInfo)]),
+    "pa_bm_blocks": (ctypes.c_int, [_vp, _i64, _i32, _vp, _i64, ctypes.POINTER(_i64)]),
+    "pa_bm_refcounts": (ctypes.c_int, [_vp, _vp, _i64]),
+    "pa_bm_free_list": (ctypes.c_int, [_vp, _i32, _vp, _i64, ctypes.POINTER(_i64)]),
 }
 
 
@@ -171,6 +227,32 @@ def pa_copy_blocks(k_pool, v_pool, block_pairs, stream=None) -> None:
                                  _stream(stream)))
 
 
+def pa_swap_blocks(k_pool, v_pool, host_k_pool, host_v_pool, block_pairs, direction: int,
+                   stream=None, k_scale: float = 1.0, v_scale: float = 1.0) -> None:
+    """Whole-block copies between device pools and pinned host pools.
+
+    ``direction`` PA_SWAP_OUT copies device block a to host block b for every
+    row (a, b) of ``block_pairs`` (device int64 [n][2]); PA_SWAP_IN copies host
+    block a to device block b.  The host pools are pinned CPU tensors shaped and
+    typed like the device pools.
+    """
+    cache = make_cache(k_pool, v_pool, k_scale, v_scale)
+    _require(host_k_pool.device.type == "cpu" and host_v_pool.device.type == "cpu" and
+             host_k_pool.is_pinned() and host_v_pool.is_pinned(),
+             "host pools must be pinned CPU tensors")
+    _require(host_k_pool.shape[1:] == k_pool.shape[1:] and host_v_pool.shape == host_k_pool.shape
+             and host_k_pool.dtype == k_pool.dtype and host_v_pool.dtype == k_pool.dtype and
+             host_k_pool.is_contiguous() and host_v_pool.is_contiguous(),
+             "host pools must be contiguous and match the device pools' block shape and type")
+    _require(block_pairs.dtype == torch.int64 and block_pairs.is_contiguous() and
+             block_pairs.device.type != "cpu" and
+             (block_pairs.numel() == 0 or block_pairs.shape[-1] == 2),
+             "block_pairs must be contiguous device int64 [n][2]")
+    _check(load().pa_swap_blocks(ctypes.byref(cache), host_k_pool.data_ptr(),
+                                 host_v_pool.data_ptr(), host_k_pool.shape[0], _ptr(block_pairs),
+                                 block_pairs.numel() // 2, int(direction), _stream(stream)))
+
+
 def decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int) -> int:
     """Bytes of workspace pa_decode needs on the current device."""
     return load().pa_decode_workspace_bytes(num_seqs, num_heads, head_dim)
@@ -264,6 +346,132 @@ def pa_splitkv_reduce(part_out, part_max, part_sum, context_lens, partition_size
                                     _ptr(context_lens), num_seqs, num_heads, head_dim, max_parts,
                                     int(partition_size), _ptr(out), _dtype_code(out), _ptr(lse),
                                     _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# block manager (host only)
+# ---------------------------------------------------------------------------
+
+REQUEST_STATES = {0: "waiting", 1: "running", 2: "swapped"}
+PREEMPT_MODES = {"recompute": 0, "swap": 1}
+
+
+class StepPlan:
+    """One step's plan as numpy arrays (copied out of the manager)."""
+
+    def __init__(self, p: PaStepPlan):
+        import numpy as np
+
+        def arr(ptr, n, dtype):
+            if n == 0:
+                return np.zeros(0, dtype=dtype)
+            return np.ctypeslib.as_array(ptr, shape=(n,)).astype(dtype, copy=True)
+
+        S = p.num_seqs
+        self.seq_ids = arr(p.seq_ids, S, np.int64)
+        self.query_start = arr(p.query_start, S + 1, np.int32)
+        self.context_lens = arr(p.context_lens, S, np.int32)
+        self.slot_mapping = arr(p.slot_mapping, p.num_tokens, np.int64)
+        self.max_blocks = p.max_blocks
+        self.block_tables = arr(p.block_tables, S * p.max_blocks, np.int32).reshape(S, p.max_blocks)
+        self.cow_pairs = arr(p.cow_pairs, 2 * p.num_cow, np.int64).reshape(-1, 2)
+        self.swap_out = arr(p.swap_out_pairs, 2 * p.num_swap_out, np.int64).reshape(-1, 2)
+        self.swap_in = arr(p.swap_in_pairs, 2 * p.num_swap_in, np.int64).reshape(-1, 2)
+        modes = {v: k for k, v in PREEMPT_MODES.items()}
+        self.preempted = list(zip(arr(p.preempted_ids, p.num_preempted, np.int64).tolist(),
+                                  [modes[m] for m in arr(p.preempted_modes, p.num_preempted,
+                                                         np.int32).tolist()]))
+
+
+class BlockManager:
+    """The native block manager (include/pa_block_manager.h) behind a Python object."""
+
+    def __init__(self, num_gpu_blocks: int, num_cpu_blocks: int, block_size: int,
+                 prefix_caching: bool = True, preempt_mode: str = "recompute",
+                 watermark_blocks: int = 0):
+        _require(preempt_mode in PREEMPT_MODES, "preempt_mode is 'recompute' or 'swap'")
+        cfg = PaBmConfig(num_gpu_blocks, num_cpu_blocks, block_size, int(bool(prefix_caching)),
+                         PREEMPT_MODES[preempt_mode], watermark_blocks)
+        handle = _vp()
+        self._h = None
+        _check(load().pa_bm_create(ctypes.byref(cfg), ctypes.byref(handle)))
+        self._h = handle
+        self.B = block_size
+        self.num_gpu_blocks = num_gpu_blocks
+        self.num_cpu_blocks = num_cpu_blocks
+
+    def __del__(self):
+        if getattr(self, "_h", None) is not None and _lib is not None:
+            _lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    @staticmethod
+    def _tokens(tokens):
+        import numpy as np
+
+        a = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+        _require(a.ndim == 1 and (a.size == 0 or (a.min() >= -2**31 and a.max() < 2**31)),
+                 "tokens must be a 1-D sequence of int32 values")
+        return np.ascontiguousarray(a.astype(np.int32))
+
+    def add_request(self, rid: int, tokens) -> None:
+        t = self._tokens(tokens)
+        _check(load().pa_bm_add_request(self._h, int(rid), t.ctypes.data, t.size))
+
+    def append_token(self, rid: int, token: int) -> None:
+        self.append_tokens(rid, [token])
+
+    def append_tokens(self, rid: int, tokens) -> None:
+        t = self._tokens(tokens)
+        _check(load().pa_bm_append_tokens(self._h, int(rid), t.ctypes.data, t.size))
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(load().pa_bm_fork(self._h, int(parent), int(child)))
+
+    def finish(self, rid: int) -> None:
+        _check(load().pa_bm_finish(self._h, int(rid)))
+
+    def schedule(self, token_budget: int) -> StepPlan:
+        p = PaStepPlan()
+        _check(load().pa_bm_schedule(self._h, int(token_budget), ctypes.byref(p)))
+        return StepPlan(p)
+
+    def stats(self) -> dict:
+        st = PaBmStats()
+        _check(load().pa_bm_get_stats(self._h, ctypes.byref(st)))
+        return {name: getattr(st, name) for name in _BM_STATS}
+
+    def request_info(self, rid: int) -> dict:
+        info = PaRequestInfo()
+        _check(load().pa_bm_request_info(self._h, int(rid), ctypes.byref(info)))
+        return dict(state=REQUEST_STATES[info.state], computed=info.computed,
+                    num_tokens=info.num_tokens, arrival=info.arrival,
+                    num_blocks=info.num_blocks, num_cpu_blocks=info.num_cpu_blocks)
+
+    def _ids(self, fn, *args) -> list:
+        import numpy as np
+
+        count = _i64()
+        fn(self._h, *args, None, 0, ctypes.byref(count))
+        out = np.zeros(max(count.value, 1), dtype=np.int32)
+        _check(fn(self._h, *args, out.ctypes.data, out.size, ctypes.byref(count)))
+        return out[:count.value].tolist()
+
+    def table(self, rid: int) -> list:
+        return self._ids(load().pa_bm_blocks, int(rid), 0)
+
+    def cpu_blocks(self, rid: int) -> list:
+        return self._ids(load().pa_bm_blocks, int(rid), 1)
+
+    def free_list(self, cpu: bool = False) -> list:
+        return self._ids(load().pa_bm_free_list, int(bool(cpu)))
+
+    def refcounts(self) -> list:
+        import numpy as np
+
+        out = np.zeros(self.num_gpu_blocks, dtype=np.int32)
+        _check(load().pa_bm_refcounts(self._h, out.ctypes.data, out.size))
+        return out.tolist()
 
 
 def raw_call(name: str, *args) -> int:

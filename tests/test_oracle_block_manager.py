@@ -160,6 +160,8 @@ def test_prefix_cache_worked_example():
     fresh = table[g["cached_blocks"]:]
     assert len(fresh) == g["new_blocks"] and not set(fresh) & set(m.table(0))
     assert abs(n - g["prefill_tokens_about"]) < B
+    st = m.stats()
+    assert st["prefix_hit_tokens"] == cached and st["admitted_tokens"] == 1000 + g["prompt_tokens"]
     # the 1,201st token is the first one of the 76th block
     m.append_token(1, 7)
     plan = m.schedule(4096)
@@ -221,6 +223,7 @@ def test_fork_shares_every_block_then_copies_on_write():
     assert all(src == last for src, _ in plan.cow_pairs)
     assert len({dst for _, dst in plan.cow_pairs}) == n_conv - 1
     assert m.refcount[last] == 1 and m.table(n_conv - 1)[-1] == last
+    assert m.stats()["cow_copies"] == n_conv - 1
     check_invariants(m)
 
 
