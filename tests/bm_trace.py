@@ -11,7 +11,32 @@ prefixes through its table.
 
 from __future__ import annotations
 
+import math
+
 import numpy as np
+
+
+def oracle_plan(p) -> dict:
+    """An oracle step plan as plain lists, for comparison."""
+    return dict(seq_ids=list(p.seq_ids), query_start=list(p.query_start),
+                context_lens=list(p.context_lens), slot_mapping=list(p.slot_mapping),
+                block_tables=[list(t) for t in p.block_tables],
+                cow=[tuple(x) for x in p.cow_pairs], swap_out=[tuple(x) for x in p.swap_out],
+                swap_in=[tuple(x) for x in p.swap_in], preempted=list(p.preempted))
+
+
+def native_plan(p, block_size: int) -> dict:
+    """A native step plan (numpy arrays, padded tables) in the same form."""
+    tables = []
+    for k, L in enumerate(p.context_lens.tolist()):
+        n = math.ceil(L / block_size)
+        assert not p.block_tables[k, n:].any(), "table padding must be 0"
+        tables.append(p.block_tables[k, :n].tolist())
+    return dict(seq_ids=p.seq_ids.tolist(), query_start=p.query_start.tolist(),
+                context_lens=p.context_lens.tolist(), slot_mapping=p.slot_mapping.tolist(),
+                block_tables=tables, cow=[tuple(x) for x in p.cow_pairs.tolist()],
+                swap_out=[tuple(x) for x in p.swap_out.tolist()],
+                swap_in=[tuple(x) for x in p.swap_in.tolist()], preempted=list(p.preempted))
 
 
 class PrefixIds:

@@ -17,7 +17,7 @@ import os
 import numpy as np
 import pytest
 
-from bm_trace import Trace
+from bm_trace import Trace, native_plan, oracle_plan
 from oracle.block_manager import BlockManager as OracleBM
 from paged_kv_cache_93_amd import lib
 
@@ -27,27 +27,6 @@ pytestmark = pytest.mark.skipif(not os.path.exists(lib.LIB_PATH),
 
 def native(*args, **kw):
     return lib.BlockManager(*args, **kw)
-
-
-def oracle_plan(p) -> dict:
-    return dict(seq_ids=list(p.seq_ids), query_start=list(p.query_start),
-                context_lens=list(p.context_lens), slot_mapping=list(p.slot_mapping),
-                block_tables=[list(t) for t in p.block_tables],
-                cow=[tuple(x) for x in p.cow_pairs], swap_out=[tuple(x) for x in p.swap_out],
-                swap_in=[tuple(x) for x in p.swap_in], preempted=list(p.preempted))
-
-
-def native_plan(p, B: int) -> dict:
-    tables = []
-    for k, L in enumerate(p.context_lens.tolist()):
-        n = math.ceil(L / B)
-        assert not p.block_tables[k, n:].any(), "table padding must be 0"
-        tables.append(p.block_tables[k, :n].tolist())
-    return dict(seq_ids=p.seq_ids.tolist(), query_start=p.query_start.tolist(),
-                context_lens=p.context_lens.tolist(), slot_mapping=p.slot_mapping.tolist(),
-                block_tables=tables, cow=[tuple(x) for x in p.cow_pairs.tolist()],
-                swap_out=[tuple(x) for x in p.swap_out.tolist()],
-                swap_in=[tuple(x) for x in p.swap_in.tolist()], preempted=list(p.preempted))
 
 
 def assert_same_state(o: OracleBM, n) -> None:
