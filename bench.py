@@ -19,6 +19,12 @@ event inside: ``--steps`` whole steps (``value``, ``ms_per_step``), then
 
 Prints one JSON line.  ``value`` is the KV bytes the step's decode must read
 divided by the step time (GB/s).
+
+``--part swap`` instead times block swaps between the device pools and pinned
+host pools (pa_swap_blocks, both directions, 8B-class blocks) against the
+PCIe link; ``--part scheduler`` times the host-side block manager's step on a
+serving trace at the batch-64 scale, native against the oracle (no GPU
+needed).  Each prints its own JSON line.
 """
 
 from __future__ import annotations
@@ -41,6 +47,8 @@ from paged_kv_cache_93_amd import lib  # noqa: E402
 from paged_kv_cache_93_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+# PCIe 5.0 x16 host link, per direction: 32 GT/s x 16 lanes x 128/130 / 8 bits
+PCIE_PEAK_GBPS = 32.0 * 16 * 128 / 130 / 8
 
 
 def to_device(arr, dtype):
@@ -213,6 +221,190 @@ def workload_shape(k: int, block_size=None, dtype=None):
     return name, c["num_kv_heads"] * bs * c["head_dim"] * W.element_bytes(dt)
 
 
+def bench_swap(args) -> dict:
+    """pa_swap_blocks at the 8B-class block shape (8 KV heads x 16 x 128 bf16:
+    32 KiB per pool per block), ``--swap-blocks`` random blocks per launch."""
+    hkv, bs, d, dt = 8, 16, 128, torch.bfloat16
+    n = args.swap_blocks
+    n_dev, n_host = 4 * n, 2 * n
+    dk = torch.randn((n_dev, hkv, bs, d), device="cuda").to(dt)
+    dv = torch.randn_like(dk)
+    hk = torch.empty((n_host, hkv, bs, d), dtype=dt, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    rng = np.random.default_rng(9393)
+    out_pairs = torch.from_numpy(np.stack([rng.permutation(n_dev)[:n],
+                                           rng.permutation(n_host)[:n]], 1)).cuda()
+    in_pairs = torch.from_numpy(np.stack([rng.permutation(n_host)[:n],
+                                          rng.permutation(n_dev)[:n]], 1)).cuda()
+    nbytes = 2 * n * hkv * bs * d * dk.element_size()
+
+    def timed(fn, k):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(k):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / k
+
+    swap_out = lambda: lib.pa_swap_blocks(dk, dv, hk, hv, out_pairs, lib.PA_SWAP_OUT)
+    swap_in = lambda: lib.pa_swap_blocks(dk, dv, hk, hv, in_pairs, lib.PA_SWAP_IN)
+    # the same bytes as one contiguous copy each way (torch, DMA): the link's practical rate
+    flat_d, flat_h = dk[:2 * n].reshape(-1), hk.reshape(-1)
+    bulk_out = lambda: flat_h.copy_(flat_d, non_blocking=True)
+    bulk_in = lambda: flat_d.copy_(flat_h, non_blocking=True)
+    res = {}
+    for name, fn in (("swap_out", swap_out), ("swap_in", swap_in), ("bulk_out", bulk_out),
+                     ("bulk_in", bulk_in)):
+        for _ in range(args.warmup):
+            fn()
+        ms = timed(fn, args.steps)
+        res[name] = dict(us=round(ms * 1e3, 1), gbps=round(nbytes / (ms * 1e-3) / 1e9, 2))
+    return {
+        "metric": "KV block swap GB/s between HBM and pinned host memory (pa_swap_blocks)",
+        "value": min(res["swap_out"]["gbps"], res["swap_in"]["gbps"]),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": True, "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"swap {n} random 8B-class blocks (K and V) per launch",
+                   "bytes_per_launch": nbytes, "device_blocks": n_dev, "host_blocks": n_host},
+        "directions": res,
+        "roofline": {"bound": "pcie", "peak": round(PCIE_PEAK_GBPS, 2), "unit": "GB/s",
+                     "frac_out": round(res["swap_out"]["gbps"] / PCIE_PEAK_GBPS, 3),
+                     "frac_in": round(res["swap_in"]["gbps"] / PCIE_PEAK_GBPS, 3)},
+    }
+
+
+class ServingTrace:
+    """Seeded serving workload for the block manager at the batch-64 scale.
+
+    ``live`` requests at a time; prompts of U{128..4096} tokens, 30 % of them
+    opening with one shared 1,008-token system prompt; each request generates
+    U{64..512} tokens and finishes, and a new one arrives in its place.
+    """
+
+    def __init__(self, seed: int, live: int = 64):
+        self.rng = np.random.default_rng(seed)
+        self.live = live
+        self.system = self.rng.integers(0, 32000, 1008).tolist()
+        self.next_rid = 0
+        self.target = {}   # rid -> total length at which it finishes
+        self.length = {}   # rid -> tokens so far
+
+    def _new(self, managers):
+        rid = self.next_rid
+        self.next_rid += 1
+        n = int(self.rng.integers(128, 4097))
+        toks = self.rng.integers(0, 32000, n).tolist()
+        if self.rng.random() < 0.3:
+            toks = (self.system + toks)[:n]
+        for m in managers:
+            m.add_request(rid, toks)
+        self.length[rid] = n
+        self.target[rid] = n + int(self.rng.integers(64, 513))
+
+    def admit(self, managers):
+        while len(self.target) < self.live:
+            self._new(managers)
+
+    def post(self, managers, plan):
+        """After a step: each scheduled request whose KV now covers all its
+        tokens samples one more token, or finishes at its target length."""
+        done, rids = [], []
+        for rid, ctx in zip(list(plan.seq_ids), list(plan.context_lens)):
+            rid = int(rid)
+            if int(ctx) != self.length[rid]:
+                continue          # a prompt slice: nothing to sample yet
+            (done if self.length[rid] >= self.target[rid] else rids).append(rid)
+        toks = self.rng.integers(0, 32000, len(rids)).tolist()
+        for m in managers:
+            if hasattr(m, "append_batch"):
+                m.append_batch(rids, toks)
+            else:
+                for r, t in zip(rids, toks):
+                    m.append_token(r, t)
+            for rid in done:
+                m.finish(rid)
+        for rid in rids:
+            self.length[rid] += 1
+        for rid in done:
+            del self.target[rid], self.length[rid]
+
+    def step(self, managers, budget: int):
+        self.admit(managers)
+        plans = [m.schedule(budget) for m in managers]
+        self.post(managers, plans[0])
+        return plans
+
+
+def bench_scheduler(args) -> dict:
+    """Host time of the block manager's schedule() per serving step (pool and
+    batch of the 8B-class batch-64 workload), the native library against the
+    oracle.  ``step_us`` adds the driver's own work (drawing tokens, appending
+    them, finishing requests)."""
+    sys.path.insert(0, ROOT)
+    from oracle.block_manager import BlockManager as OracleBM
+
+    cfg = dict(num_gpu_blocks=10598, num_cpu_blocks=4096, block_size=16, prefix_caching=True,
+               preempt_mode="swap", watermark_blocks=64)
+    budget = 8192
+    m = lib.BlockManager(**cfg)
+    trace = ServingTrace(9302)
+    t_warm = time.perf_counter()
+    for _ in range(args.warmup):
+        trace.step([m], budget)
+    warm_s = time.perf_counter() - t_warm
+    sched_s, total_s, seqs, toks = 0.0, 0.0, 0, 0
+    for _ in range(args.steps):
+        t0 = time.perf_counter()
+        trace.admit([m])
+        t1 = time.perf_counter()
+        plan = m.schedule(budget)
+        t2 = time.perf_counter()
+        trace.post([m], plan)
+        t3 = time.perf_counter()
+        seqs += len(plan.seq_ids)
+        toks += len(plan.slot_mapping)
+        sched_s += t2 - t1
+        total_s += t3 - t0
+    st = m.stats()
+    # the oracle on the same serving trace, for a bounded number of steps
+    o = OracleBM(**cfg)
+    otrace = ServingTrace(9302)
+    for _ in range(args.warmup):
+        otrace.step([o], budget)
+    o_steps, o_s, o_sched = 0, 0.0, 0.0
+    while o_s < args.cpu_budget and o_steps < args.steps:
+        t0 = time.perf_counter()
+        otrace.admit([o])
+        t1 = time.perf_counter()
+        oplan = o.schedule(budget)
+        t2 = time.perf_counter()
+        otrace.post([o], oplan)
+        o_s += time.perf_counter() - t0
+        o_sched += t2 - t1
+        o_steps += 1
+    return {
+        "metric": "block manager schedule() host time per serving step (plan copied out)",
+        "value": round(sched_s / args.steps * 1e6, 1), "unit": "us",
+        "n_gpus": 0, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
+        "vs_baseline": None, "dtype": "int64", "data": "synthetic",
+        "config": {"workload": "64 live requests, prompts U{128..4096} (30% with a shared "
+                               "1,008-token system prompt), U{64..512} generated tokens each, "
+                               "pool 10,598 blocks of 16, 4,096 CPU blocks, swap preemption, "
+                               "token budget 8,192", **cfg},
+        "step_us": round(total_s / args.steps * 1e6, 1),
+        "seqs_per_step": round(seqs / args.steps, 1),
+        "tokens_per_step": round(toks / args.steps, 1),
+        "warmup_s": round(warm_s, 3),
+        "stats": st,
+        "cpu_baseline": {"value": round(o_sched / max(o_steps, 1) * 1e6, 1), "unit": "us",
+                         "cores": 1, "kind": "oracle",
+                         "sample": f"schedule() over {o_steps} steps of the same serving "
+                                   f"trace after the same {args.warmup} warm-up steps"},
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,7 +425,15 @@ def main() -> int:
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from two --pmc-pass counter runs")
     ap.add_argument("--pmc-command", default="", help="command line recorded in the summary")
+    ap.add_argument("--part", default="decode", choices=["decode", "swap", "scheduler"],
+                    help="decode: the decode step (default); swap: block swaps to pinned host "
+                         "memory; scheduler: the host block manager (no GPU needed)")
+    ap.add_argument("--swap-blocks", type=int, default=1024, help="blocks per swap launch")
     args = ap.parse_args()
+
+    if args.part == "scheduler":
+        print(json.dumps(bench_scheduler(args)), flush=True)
+        return 0
 
     if args.pmc_summary:
         name, block_bytes = workload_shape(args.workload, args.block_size, args.dtype)
@@ -248,6 +448,9 @@ def main() -> int:
         print(json.dumps({"error": "no GPU visible"}), flush=True)
         return 2
     lib.load()
+    if args.part == "swap":
+        print(json.dumps(bench_swap(args)), flush=True)
+        return 0
 
     w = W.make_config(args.workload, dtype=args.dtype, block_size=args.block_size)
     qdt = W.query_dtype(w.dtype)

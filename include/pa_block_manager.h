@@ -181,6 +181,12 @@ int pa_bm_add_request(pa_block_manager *bm, int64_t rid, const int32_t *tokens,
 int pa_bm_append_tokens(pa_block_manager *bm, int64_t rid, const int32_t *tokens,
                         int64_t num_tokens);
 
+/* Appends tokens[i] to request rids[i] for i < n: one sampled token for each of
+ * many requests in one call.  Every id is checked first; on an error nothing
+ * is appended. */
+int pa_bm_append_batch(pa_block_manager *bm, const int64_t *rids, const int32_t *tokens,
+                       int64_t n);
+
 /* Parallel sampling: `child` starts as a copy of the running `parent` that
  * shares all its blocks.  PA_ERR_STATE unless the parent is running. */
 int pa_bm_fork(pa_block_manager *bm, int64_t parent, int64_t child);

@@ -518,6 +518,25 @@ PA_API int pa_bm_append_tokens(pa_block_manager* bm, int64_t rid, const int32_t*
   });
 }
 
+PA_API int pa_bm_append_batch(pa_block_manager* bm, const int64_t* rids, const int32_t* tokens,
+                              int64_t n) {
+  if (!bm) return fail(PA_ERR_NULL, "pa_bm_append_batch: manager is NULL");
+  if (n < 0) return fail(PA_ERR_SHAPE, "pa_bm_append_batch: n < 0");
+  if (n == 0) return PA_OK;
+  if (!rids || !tokens) return fail(PA_ERR_NULL, "pa_bm_append_batch: rids or tokens is NULL");
+  for (int64_t i = 0; i < n; ++i) {
+    const pa::Request* r = pa::find(bm, rids[i]);
+    if (!r) return fail(PA_ERR_ID, "pa_bm_append_batch: no request %lld", (long long)rids[i]);
+    // (a repeated id appends more than once; the bound below is checked per entry)
+    if (int64_t(r->tokens.size()) >= kMaxTokens - n)
+      return fail(PA_ERR_SHAPE, "pa_bm_append_batch: a request holds at most 2^31 - 1 tokens");
+  }
+  return pa::guarded("pa_bm_append_batch", [&] {
+    for (int64_t i = 0; i < n; ++i) pa::find(bm, rids[i])->tokens.push_back(tokens[i]);
+    return int(PA_OK);
+  });
+}
+
 PA_API int pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t child) {
   if (!bm) return fail(PA_ERR_NULL, "pa_bm_fork: manager is NULL");
   pa::Request* p = pa::find(bm, parent);

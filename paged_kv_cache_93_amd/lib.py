@@ -31,6 +31,7 @@ EXPORTED = ("pa_abi_version", "pa_hip_runtime_version", "pa_last_error", "pa_kv_
             "pa_copy_blocks", "pa_swap_blocks", "pa_decode", "pa_decode_workspace_bytes",
             "pa_decode_partitions", "pa_splitkv_reduce", "pa_partials_bytes",
             "pa_bm_create", "pa_bm_destroy", "pa_bm_add_request", "pa_bm_append_tokens",
+            "pa_bm_append_batch",
             "pa_bm_fork", "pa_bm_finish", "pa_bm_schedule", "pa_bm_get_stats",
             "pa_bm_request_info", "pa_bm_blocks", "pa_bm_refcounts", "pa_bm_free_list")
 
@@ -107,6 +108,7 @@ _SIGNATURES = {
     "pa_bm_destroy": (None, [_vp]),
     "pa_bm_add_request": (ctypes.c_int, [_vp, _i64, _vp, _i64]),
     "pa_bm_append_tokens": (ctypes.c_int, [_vp, _i64, _vp, _i64]),
+    "pa_bm_append_batch": (ctypes.c_int, [_vp, _vp, _vp, _i64]),
     "pa_bm_fork": (ctypes.c_int, [_vp, _i64, _i64]),
     "pa_bm_finish": (ctypes.c_int, [_vp, _i64]),
     "pa_bm_schedule": (ctypes.c_int, [_vp, _i64, ctypes.POINTER(PaStepPlan)]),
@@ -365,7 +367,8 @@ class StepPlan:
         def arr(ptr, n, dtype):
             if n == 0:
                 return np.zeros(0, dtype=dtype)
-            return np.ctypeslib.as_array(ptr, shape=(n,)).astype(dtype, copy=True)
+            nbytes = n * np.dtype(dtype).itemsize
+            return np.frombuffer(ctypes.string_at(ptr, nbytes), dtype=dtype).copy()
 
         S = p.num_seqs
         self.seq_ids = arr(p.seq_ids, S, np.int64)
@@ -424,6 +427,15 @@ class BlockManager:
     def append_tokens(self, rid: int, tokens) -> None:
         t = self._tokens(tokens)
         _check(load().pa_bm_append_tokens(self._h, int(rid), t.ctypes.data, t.size))
+
+    def append_batch(self, rids, tokens) -> None:
+        """Appends tokens[i] to request rids[i] for every i, in one call."""
+        import numpy as np
+
+        r = np.ascontiguousarray(np.asarray(rids, dtype=np.int64))
+        t = self._tokens(tokens)
+        _require(r.ndim == 1 and r.size == t.size, "rids and tokens must be equal-length 1-D")
+        _check(load().pa_bm_append_batch(self._h, r.ctypes.data, t.ctypes.data, r.size))
 
     def fork(self, parent: int, child: int) -> None:
         _check(load().pa_bm_fork(self._h, int(parent), int(child)))

@@ -131,3 +131,22 @@ def test_token_ids_cover_the_int32_range():
         m.add_request(2, toks[:15] + [7] * 9)
     assert oracle_plan(o.schedule(100)) == native_plan(n.schedule(100), 4)
     assert_same_state(o, n)
+
+
+def test_append_batch_equals_single_appends():
+    a, b = native(64, 0, 4), native(64, 0, 4)
+    for m in (a, b):
+        for rid in range(5):
+            m.add_request(rid, [rid, 1, 2])
+        m.schedule(100)
+    rids, toks = [3, 0, 4, 3, 1], [9, 8, 7, 6, 5]
+    a.append_batch(rids, toks)
+    for r, t in zip(rids, toks):
+        b.append_token(r, t)
+    assert native_plan(a.schedule(100), 4) == native_plan(b.schedule(100), 4)
+    for rid in range(5):
+        assert a.request_info(rid) == b.request_info(rid)
+    with pytest.raises(lib.PagedAttnError) as err:
+        a.append_batch([0, 77], [1, 2])          # unknown id: nothing appended
+    assert err.value.status == 6
+    assert a.request_info(0)["num_tokens"] == b.request_info(0)["num_tokens"]
