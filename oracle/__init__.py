@@ -23,7 +23,10 @@ from .paged_attention import (  # noqa: F401
     gather_rows,
     kv_append,
     last_block_waste,
+    prefill,
+    query_position,
     slot_of,
     splitkv_merge,
     to_f64,
+    visible_keys,
 )

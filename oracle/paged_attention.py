@@ -306,6 +306,74 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float,
     return out
 
 
+def query_position(context_len: int, num_query: int, j: int) -> int:
+    """Position of the j-th of a sequence's ``num_query`` query tokens.
+
+    A step computes a sequence's last ``num_query`` tokens: the KV of all
+    earlier positions (a cached prefix, earlier prompt slices or earlier
+    decode steps) is already in the cache, and this step's own tokens are
+    written before attention, so the sequence holds ``context_len`` tokens and
+    query token j sits at position context_len - num_query + j.
+    """
+    return context_len - num_query + j
+
+
+def visible_keys(position: int) -> int:
+    """Keys a query at ``position`` attends to under the causal rule: 0..position."""
+    return position + 1
+
+
+def prefill(q, k_pool, v_pool, block_tables, query_start, context_lens, scale: float,
+            dtype: str, k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+    """Causal attention of every scheduled query token of a mixed batch.
+
+    The batch is one flattened sequence of query tokens: sequence i owns rows
+    ``query_start[i] .. query_start[i+1]-1`` of ``q`` (``[num_tokens][Hq][D]``),
+    and metadata says where each request's tokens begin and end and which
+    positions they may look at ("How Paged Attention and Continuous Batching
+    Actually Work", section "Continuous batching: schedule steps, not
+    batches").  Query token j of sequence i sits at position
+    p = :func:`query_position` (L_i, n_i, j) and attends causally to positions
+    0..p, whose K/V rows are gathered block by block through the table
+    ("PagedAttention and continuous batching", section "Attention kernel
+    modification"); scores and softmax are those of :func:`decode`.  A decode
+    row is the case n_i = 1 (p = L_i - 1).  Rows with p < 0 (more query tokens
+    than context: a caller error) are left zero.
+
+    Returns float64 ``[num_tokens][num_heads][head_dim]``.
+    """
+    num_heads = q.shape[1]
+    num_blocks, num_kv_heads, block_size, head_dim = k_pool.shape
+    if q.ndim != 3 or q.shape[2] != head_dim or num_heads % num_kv_heads:
+        raise ValueError("q must be [num_tokens][num_heads][head_dim] with num_heads % num_kv_heads == 0")
+    starts = [int(x) for x in query_start]
+    num_seqs = len(starts) - 1
+    if num_seqs != len(context_lens) or starts[0] != 0 or starts[-1] != q.shape[0] or \
+            any(b < a for a, b in zip(starts, starts[1:])):
+        raise ValueError("query_start must rise from 0 to num_tokens, one entry per sequence + 1")
+    group = num_heads // num_kv_heads
+    q64 = to_f64(q, _q_dtype(dtype))
+    out = np.zeros((q.shape[0], num_heads, head_dim), dtype=np.float64)
+    for i in range(num_seqs):
+        length, n = int(context_lens[i]), starts[i + 1] - starts[i]
+        if n == 0 or length == 0:
+            continue
+        for g in range(num_kv_heads):
+            keys = _kv_f64(gather_rows(k_pool, block_tables[i], length, block_size, g),
+                           dtype, k_scale)
+            values = _kv_f64(gather_rows(v_pool, block_tables[i], length, block_size, g),
+                             dtype, v_scale)
+            for j in range(n):
+                p = query_position(length, n, j)
+                if p < 0:
+                    continue
+                seen = visible_keys(p)
+                for h in range(g * group, (g + 1) * group):
+                    scores = scale * (keys[:seen] @ q64[starts[i] + j, h])
+                    out[starts[i] + j, h], _, _ = _softmax_weighted_sum(scores, values[:seen])
+    return out
+
+
 def decode_partitions(q, k_pool, v_pool, block_tables, context_lens, scale: float,
                       dtype: str, partition_size: int, max_parts: int | None = None,
                       k_scale: float = 1.0, v_scale: float = 1.0):
