@@ -207,6 +207,48 @@ int pa_decode(const pa_cache *cache, const void *q, const int32_t *block_tables,
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim);
 
 /*
+ * pa_prefill - causal attention of a mixed batch: many query tokens per
+ * sequence (prompt slices) and single tokens (decodes) in one call.
+ *
+ * Every scheduled token of the batch is flattened into one sequence of query
+ * rows; metadata says where each request's tokens begin and end and what they
+ * may see ("How Paged Attention and Continuous Batching Actually Work",
+ * section "Continuous batching: schedule steps, not batches").  Sequence i owns
+ * rows query_start[i] .. query_start[i+1]-1 of q; its n_i tokens are its last
+ * n_i positions, so token j sits at position p = context_lens[i] - n_i + j,
+ * and it attends causally to positions 0..p, whose K/V rows are gathered block
+ * by block through block_tables[i] ("PagedAttention and continuous batching",
+ * section "Attention kernel modification"):
+ *     out[row][h] = sum_{t <= p} softmax_t(scale * q[row][h] . K_t) V_t
+ * The K/V of all of a sequence's context_lens[i] positions (this step's tokens
+ * included, written by pa_kv_append) must be in the cache.  The softmax
+ * weights are rounded to bf16 for the matrix product (each within 2^-9 of
+ * its value, relative) and normalised by the sum of the rounded weights.
+ *
+ *   q             DEVICE [num_tokens][num_heads][128] bfloat16
+ *   block_tables  DEVICE int32 [num_seqs][max_blocks_per_seq]
+ *   query_start   DEVICE int32 [num_seqs + 1], rising from 0 to num_tokens
+ *   context_lens  DEVICE int32 [num_seqs], n_i <= L_i <= max_blocks_per_seq*block_size
+ *                 (rows before position 0, n_i > L_i, get zeros)
+ *   num_heads     ratio to num_kv_heads 1, 2, 4 or 8
+ *   out           DEVICE [num_tokens][num_heads][128] of out_dtype (PA_F32 or PA_BF16),
+ *                 16-byte aligned; rows of sequences with n_i = 0 are not written
+ *   workspace     DEVICE scratch, >= pa_prefill_workspace_bytes(), 256-byte aligned;
+ *                 contents need no initialising.  Calls in flight at the same time
+ *                 must not share one.
+ * Supported: bf16 and 8-bit (E4M3) caches, head_dim 128, block_size 16 or 32.
+ */
+int pa_prefill(const pa_cache *cache, const void *q, const int32_t *block_tables,
+               const int32_t *query_start, const int32_t *context_lens, int32_t num_seqs,
+               int32_t num_tokens, int32_t num_heads, int32_t max_blocks_per_seq, float scale,
+               void *out, int32_t out_dtype, void *workspace, size_t workspace_bytes,
+               void *stream);
+
+/* Workspace bytes pa_prefill needs for these sizes (0 for invalid sizes). */
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                  int32_t num_kv_heads);
+
+/*
  * pa_decode_partitions - split-KV decode: per-partition partial results.
  *
  * Same attention as pa_decode, cut along each sequence's context into

@@ -1,0 +1,445 @@
+// Mixed-batch (prefill) attention over the paged cache, for gfx950.
+//
+// What it computes ("How Paged Attention and Continuous Batching Actually
+// Work", section "Continuous batching: schedule steps, not batches": every
+// scheduled token of the batch flattened into one sequence, metadata saying
+// where each request's tokens begin and end and what they may see;
+// "PagedAttention and continuous batching", section "Attention kernel
+// modification": causal attention of position t over K_{0:t}, V_{0:t} loaded
+// block by block through the table, with a running softmax): sequence i owns
+// query rows query_start[i] .. query_start[i+1]-1, its n_i tokens are its last
+// n_i positions, and token j at position p = L_i - n_i + j attends to
+// positions 0..p.  A decode row is n_i = 1.
+//
+// Mapping onto CDNA4:
+// * A workgroup (4 waves) takes a tile of 128 query rows of one sequence and
+//   one KV head: 128/G tokens times the G query heads that share the KV head,
+//   so every K/V row the tile loads serves all of them.  Each wave owns 32
+//   rows (two 16-row MFMA tiles).
+// * The tile walks its keys 32 at a time (positions 0 .. its last row's
+//   position).  The workgroup stages each 32-key K/V tile in LDS (double
+//   buffered, the next tile's global loads in flight during the current one's
+//   math): K row-major (the MFMA A operand of S^T = K Q^T reads 16-byte row
+//   pieces), V transposed (the A operand of O^T = V^T P^T needs keys
+//   contiguous per dimension).  8-bit codes become bf16 on the way into LDS
+//   (exact; the scales are folded into the score scale and the output).
+// * Scores come out as S^T, so lane 16g + r holds keys 4g..4g+3 (and 16 +
+//   4g..) of query row r: the softmax weights P are already the B operand of
+//   O^T = V^T P^T in that lane (the k order of the two operands is permuted
+//   alike), and the output O^T lands in the lane that owns the row's running
+//   max and sum - no shuffles except two lane swaps for the row maximum.
+// * Weights are rounded to bf16 for the matrix product, and the running sum
+//   adds the rounded weights, so the output is an exact convex combination of
+//   V rows with weights within 2^-9 (relative) of the true ones.
+#include "pa_decode_kernel.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+using namespace dev;
+
+constexpr int kD = 128;           // head dim
+constexpr int kRows = 128;        // query rows per workgroup tile
+constexpr int kWaves = 4;
+constexpr int kKeys = 32;         // keys per K/V tile
+constexpr int kKStride = 17;      // 16-byte chunks per K row in LDS (16 + 1 pad)
+constexpr int kVStride = 36;      // bf16 per transposed V row in LDS (32 + 4 pad)
+constexpr int kKBytes = kKeys * kKStride * 16;
+constexpr int kVBytes = kD * kVStride * 2;
+constexpr int kBufBytes = kKBytes + kVBytes;
+
+struct PrefillArgs {
+  const uint8_t* q;
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  const int32_t* block_tables;
+  const int32_t* query_start;
+  const int32_t* context_lens;
+  const int32_t* tiles;  // [0] tile count; then (sequence, tile index) pairs
+  void* out;
+  int64_t num_blocks;
+  int32_t num_seqs;
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t num_heads;
+  int32_t max_blocks;
+  int32_t max_tiles;
+  float scale_log2;  // score scale * log2(e), times the K pool's scale (8-bit cache)
+  float v_scale;     // the V pool's scale (8-bit cache), else 1
+};
+
+// The tile map: tile t of the grid -> (sequence, tile of that sequence), each
+// sequence's tiles from its last (longest context) to its first.  One
+// workgroup of 1024 threads scans the per-sequence tile counts.
+__global__ void __launch_bounds__(1024) prefill_tiles_kernel(const int32_t* qs, int32_t S,
+                                                             int32_t T, int32_t tt,
+                                                             int32_t* tiles, int32_t max_tiles) {
+  __shared__ int32_t s_wave[16];
+  __shared__ int32_t s_total;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  int32_t running = 0;
+  for (int32_t base = 0; base < S; base += 1024) {
+    const int32_t i = base + tid;
+    int32_t n = 0;
+    if (i < S) {
+      const int32_t a = min(max(qs[i], 0), T), b = min(max(qs[i + 1], 0), T);
+      n = max(b - a, 0);
+    }
+    const int32_t cnt = (n + tt - 1) / tt;
+    const int32_t incl = wave_inclusive_sum(cnt);
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    if (tid == 0) {
+      int32_t acc = 0;
+      for (int w = 0; w < 16; ++w) {
+        const int32_t v = s_wave[w];
+        s_wave[w] = acc;
+        acc += v;
+      }
+      s_total = acc;
+    }
+    __syncthreads();
+    const int32_t off = running + s_wave[wave] + incl - cnt;
+    for (int32_t k = 0; k < cnt; ++k) {
+      const int32_t t = off + k;
+      if (t < max_tiles) {
+        tiles[1 + 2 * t] = i;
+        tiles[2 + 2 * t] = cnt - 1 - k;
+      }
+    }
+    running += s_total;
+    __syncthreads();
+  }
+  if (tid == 0) tiles[0] = min(running, max_tiles);
+}
+
+template <int ET, int BS, int G, bool OUT_F32>
+__global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
+  constexpr int EB = ET == kFP8 ? 1 : 2;   // K/V element bytes
+  constexpr int TT = kRows / G;            // tokens per tile
+  using Raw = typename LaneChunk<8 * EB>::type;  // 8 elements of a row
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_mem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int t = blockIdx.x;
+  if (t >= a.tiles[0]) return;
+  const int seq = a.tiles[1 + 2 * t];
+  const int tile = a.tiles[2 + 2 * t];
+  const int g = blockIdx.y;
+  if (seq < 0 || seq >= a.num_seqs) return;
+
+  const int32_t qs0 = min(max(a.query_start[seq], 0), a.num_tokens);
+  const int32_t qs1 = min(max(a.query_start[seq + 1], 0), a.num_tokens);
+  const int32_t n = qs1 - qs0;
+  const int32_t max_len = a.max_blocks * BS;
+  const int32_t L = min(max(a.context_lens[seq], 0), max_len);
+  const int32_t c = L - n;  // position of query token 0 (negative: caller error)
+  const int32_t j0 = tile * TT;
+  const int32_t j1 = min(j0 + TT, n);
+  if (j1 <= j0) return;
+  const int32_t kend = c + j1;  // keys 0 .. kend-1 are needed (kend <= L)
+  const int32_t* table = a.block_tables + int64_t(seq) * a.max_blocks;
+
+  // ---- this lane's query rows and their fragments (B operand of S^T) --------
+  const int r16 = lane & 15, grp = lane >> 4;
+  int pos[2];
+  bool valid[2];
+  int64_t row_index[2];  // output row (token * Hq + head)
+  u32x4 qf[2][4];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int row = wave * 32 + rt * 16 + r16;
+    const int tok = j0 + row / G;
+    valid[rt] = tok < j1;
+    const int tq = min(tok, j1 - 1);
+    pos[rt] = c + tok;
+    const int head = g * G + row % G;
+    row_index[rt] = int64_t(qs0 + tq) * a.num_heads + head;
+    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + row_index[rt] * kD * 2);
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) qf[rt][mm] = qp[4 * mm + grp];
+  }
+
+  // ---- K/V tile staging -------------------------------------------------------
+  // Thread tid loads dims [8*dc, 8*dc+8) of keys 2kp and 2kp+1 of the tile.
+  const int dc = tid & 15, kp = tid >> 4;
+  Raw kr[2], vr[2];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int key = k0 + 2 * kp + e;
+      kr[e] = Raw{};
+      vr[e] = Raw{};
+      if (key < kend) {
+        const int phys = table[key / BS];
+        if (phys >= 0 && int64_t(phys) < a.num_blocks) {
+          const int64_t off =
+              ((int64_t(phys) * a.num_kv_heads + g) * BS + key % BS) * (kD * EB) + dc * 8 * EB;
+          kr[e] = *reinterpret_cast<const Raw*>(a.k_pool + off);
+          vr[e] = *reinterpret_cast<const Raw*>(a.v_pool + off);
+        }
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    u32x4* lk = reinterpret_cast<u32x4*>(s_mem + buf * kBufBytes);
+    uint32_t* lv = reinterpret_cast<uint32_t*>(s_mem + buf * kBufBytes + kKBytes);
+    u32x4 kb[2], vb[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      kb[e] = score_chunk<ET>(kr[e]);
+      vb[e] = score_chunk<ET>(vr[e]);
+      lk[(2 * kp + e) * kKStride + dc] = kb[e];
+    }
+    // V transposed: dim 8dc + x gets the pair (key 2kp, key 2kp+1) as one word
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t a0 = vb[0][w], a1 = vb[1][w];  // dims 8dc+2w, 8dc+2w+1 of each key
+      lv[((8 * dc + 2 * w) * kVStride) / 2 + kp] = (a0 & 0xFFFFu) | (a1 << 16);
+      lv[((8 * dc + 2 * w + 1) * kVStride) / 2 + kp] = (a0 >> 16) | (a1 & 0xFFFF0000u);
+    }
+  };
+
+  // ---- running state: lane 16g + r owns query row r of each 16-row tile -----
+  f32x4 acc[2][8];
+  float m[2], lsum[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    m[rt] = kNegInf;
+    lsum[rt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int min_pos = c + j0;
+  const int ntiles = kend > 0 ? (kend + kKeys - 1) / kKeys : 0;
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    const int k0 = kt * kKeys;
+    if (kt + 1 < ntiles) load_tile(k0 + kKeys);
+    const u32x4* lk = reinterpret_cast<const u32x4*>(s_mem + buf * kBufBytes);
+    const uint8_t* lv = s_mem + buf * kBufBytes + kKBytes;
+
+    // S^T = K Q^T for both 16-key halves and both row tiles
+    f32x4 s[2][2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) s[rt][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) {
+        const u32x4 kf = lk[(16 * h + r16) * kKStride + 4 * mm + grp];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+          s[rt][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, kf), __builtin_bit_cast(bf16x8, qf[rt][mm]), s[rt][h],
+              0, 0, 0);
+      }
+    }
+
+    // online softmax per row; the P^T operand in the k order
+    // [4g .. 4g+3, 16+4g .. 16+4g+3]
+    u32x4 pf[2];
+    const bool diag = k0 + kKeys - 1 > min_pos;  // some key may lie past some row
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      float sv[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float x = s[rt][h][v] * a.scale_log2;
+          if (diag && k0 + 16 * h + 4 * grp + v > pos[rt]) x = kNegInf;
+          sv[4 * h + v] = x;
+        }
+      float mx = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+      mx = xor_max<16>(mx);
+      const float mnew = fmaxf(m[rt], mx);
+      const float base = mnew == kNegInf ? 0.f : mnew;
+      const float alpha = fast_exp2(m[rt] - base);
+      m[rt] = mnew;
+      float psum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const f32x2 pp = {fast_exp2(sv[2 * w] - base), fast_exp2(sv[2 * w + 1] - base)};
+        const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
+        const uint32_t word = __builtin_bit_cast(uint32_t, pb);
+        pf[rt][w] = word;
+        psum += __uint_as_float(word << 16) + __uint_as_float(word & 0xFFFF0000u);
+      }
+      lsum[rt] = fmaf(lsum[rt], alpha, psum);
+      if (alpha != 1.f) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[rt][dt] *= alpha;
+      }
+    }
+
+    // O^T += V^T P^T: A = dims 16dt + r, keys in the permuted k order
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint8_t* row = lv + (16 * dt + r16) * kVStride * 2;
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(row + 8 * grp);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 32 + 8 * grp);
+      const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+        acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, vf), __builtin_bit_cast(bf16x8, pf[rt]), acc[rt][dt], 0,
+            0, 0);
+    }
+
+    if (kt + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- finalise: lane 16g + r holds dims 16dt + 4g + v of row r -------------
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const float l = xor_sum<16>(lsum[rt]);
+    const float inv = l > 0.f ? a.v_scale / l : 0.f;
+    if (!valid[rt]) continue;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int d0 = 16 * dt + 4 * grp;
+      const f32x4 o = acc[rt][dt] * inv;
+      if constexpr (OUT_F32) {
+        float* dst = static_cast<float*>(a.out) + row_index[rt] * kD + d0;
+        *reinterpret_cast<f32x4*>(dst) = o;
+      } else {
+        uint16_t* dst = static_cast<uint16_t*>(a.out) + row_index[rt] * kD + d0;
+        const u32x2 w = {to_bf16(o[0]) | (to_bf16(o[1]) << 16), to_bf16(o[2]) | (to_bf16(o[3]) << 16)};
+        *reinterpret_cast<u32x2*>(dst) = w;
+      }
+    }
+  }
+}
+
+template <int ET, int BS, int G>
+int launch_g(const PrefillArgs& a, bool out_f32, dim3 grid, hipStream_t stream) {
+  const size_t lds = 2 * kBufBytes;
+  if (out_f32)
+    hipLaunchKernelGGL((prefill_kernel<ET, BS, G, true>), grid, dim3(256), lds, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<ET, BS, G, false>), grid, dim3(256), lds, stream, a);
+  return launch_result("pa_prefill");
+}
+
+template <int ET, int BS>
+int launch_bs(const PrefillArgs& a, int group, bool out_f32, dim3 grid, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_g<ET, BS, 1>(a, out_f32, grid, stream);
+    case 2: return launch_g<ET, BS, 2>(a, out_f32, grid, stream);
+    case 4: return launch_g<ET, BS, 4>(a, out_f32, grid, stream);
+    default: return launch_g<ET, BS, 8>(a, out_f32, grid, stream);
+  }
+}
+
+int32_t tokens_per_tile(int32_t group) { return kRows / group; }
+
+int64_t max_tiles_for(int32_t num_seqs, int32_t num_tokens, int32_t group) {
+  const int32_t tt = tokens_per_tile(group);
+  return (int64_t(num_tokens) + tt - 1) / tt + num_seqs;
+}
+
+}  // namespace
+}  // namespace pa
+
+PA_API size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                                         int32_t num_kv_heads) {
+  if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+      num_heads % num_kv_heads != 0)
+    return 0;
+  const int32_t group = num_heads / num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return 0;
+  return size_t(1 + 2 * pa::max_tiles_for(num_seqs, num_tokens, group)) * sizeof(int32_t);
+}
+
+PA_API int pa_prefill(const pa_cache* cache, const void* q, const int32_t* block_tables,
+                      const int32_t* query_start, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_tokens, int32_t num_heads, int32_t max_blocks_per_seq,
+                      float scale, void* out, int32_t out_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  using namespace pa;
+  if (int st = check_cache(cache, "pa_prefill")) return st;
+  if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || max_blocks_per_seq <= 0)
+    return fail(PA_ERR_SHAPE, "pa_prefill: sizes must be non-negative (heads, table width positive)");
+  if (cache->dtype != PA_BF16 && cache->dtype != PA_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: bf16 and 8-bit caches only");
+  if (cache->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: head_dim 128 only");
+  if (cache->block_size != 16 && cache->block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: block_size 16 or 32 only");
+  if (num_heads % cache->num_kv_heads != 0)
+    return fail(PA_ERR_SHAPE, "pa_prefill: num_heads must be a multiple of num_kv_heads");
+  const int32_t group = num_heads / cache->num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: heads per KV head must be 1, 2, 4 or 8");
+  if (!(scale > 0.f) || !(scale < 3.4e38f))
+    return fail(PA_ERR_SHAPE, "pa_prefill: scale must be positive and finite");
+  if (out_dtype != PA_F32 && out_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: out_dtype must be PA_F32 or PA_BF16");
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (!q || !block_tables || !query_start || !context_lens || !out)
+    return fail(PA_ERR_NULL, "pa_prefill: a required pointer is NULL");
+  if (!aligned16(q) || !aligned16(out))
+    return fail(PA_ERR_SHAPE, "pa_prefill: q and out must be 16-byte aligned");
+  if (int64_t(max_blocks_per_seq) * cache->block_size > INT32_MAX)
+    return fail(PA_ERR_SHAPE, "pa_prefill: table width too large");
+  const int64_t max_tiles = max_tiles_for(num_seqs, num_tokens, group);
+  if (max_tiles > INT32_MAX / 2 - 1)
+    return fail(PA_ERR_SHAPE, "pa_prefill: too many tiles");
+  const size_t need = pa_prefill_workspace_bytes(num_seqs, num_tokens, num_heads,
+                                                 cache->num_kv_heads);
+  if (!workspace || workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "pa_prefill: workspace of %zu bytes needed", need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(PA_ERR_SHAPE, "pa_prefill: workspace must be 256-byte aligned");
+  if (cache->num_kv_heads > 65535)
+    return fail(PA_ERR_SHAPE, "pa_prefill: too many KV heads");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* tiles = static_cast<int32_t*>(workspace);
+  hipLaunchKernelGGL(prefill_tiles_kernel, dim3(1), dim3(1024), 0, s, query_start, num_seqs,
+                     num_tokens, tokens_per_tile(group), tiles, int32_t(max_tiles));
+  if (int st = launch_result("pa_prefill")) return st;
+
+  PrefillArgs a;
+  a.q = static_cast<const uint8_t*>(q);
+  a.k_pool = static_cast<const uint8_t*>(cache->k_pool);
+  a.v_pool = static_cast<const uint8_t*>(cache->v_pool);
+  a.block_tables = block_tables;
+  a.query_start = query_start;
+  a.context_lens = context_lens;
+  a.tiles = tiles;
+  a.out = out;
+  a.num_blocks = cache->num_blocks;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.num_heads = num_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_tiles = int32_t(max_tiles);
+  const bool fp8 = cache->dtype == PA_FP8_E4M3;
+  a.scale_log2 = scale * 1.4426950408889634f * (fp8 ? cache->k_scale : 1.0f);
+  a.v_scale = fp8 ? cache->v_scale : 1.0f;
+  const dim3 grid(unsigned(max_tiles), unsigned(cache->num_kv_heads));
+  const bool f32 = out_dtype == PA_F32;
+  if (fp8)
+    return cache->block_size == 16 ? launch_bs<kFP8, 16>(a, group, f32, grid, s)
+                                   : launch_bs<kFP8, 32>(a, group, f32, grid, s);
+  return cache->block_size == 16 ? launch_bs<kBF16, 16>(a, group, f32, grid, s)
+                                 : launch_bs<kBF16, 32>(a, group, f32, grid, s);
+}

@@ -29,7 +29,8 @@ STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSU
 # Every symbol include/pagedattn.h and include/pa_block_manager.h declare.
 EXPORTED = ("pa_abi_version", "pa_hip_runtime_version", "pa_last_error", "pa_kv_append",
             "pa_copy_blocks", "pa_swap_blocks", "pa_decode", "pa_decode_workspace_bytes",
-            "pa_decode_partitions", "pa_splitkv_reduce", "pa_partials_bytes",
+            "pa_decode_partitions", "pa_splitkv_reduce", "pa_partials_bytes", "pa_prefill",
+            "pa_prefill_workspace_bytes",
             "pa_bm_create", "pa_bm_destroy", "pa_bm_add_request", "pa_bm_append_tokens",
             "pa_bm_append_batch",
             "pa_bm_fork", "pa_bm_finish", "pa_bm_schedule", "pa_bm_get_stats",
@@ -104,6 +105,9 @@ _SIGNATURES = {
     "pa_splitkv_reduce": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp,
                                          _i32, _vp, _vp]),
     "pa_partials_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32]),
+    "pa_prefill": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                  _i32, _f32, _vp, _i32, _vp, ctypes.c_size_t, _vp]),
+    "pa_prefill_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32]),
     "pa_bm_create": (ctypes.c_int, [ctypes.POINTER(PaBmConfig), ctypes.POINTER(_vp)]),
     "pa_bm_destroy": (None, [_vp]),
     "pa_bm_add_request": (ctypes.c_int, [_vp, _i64, _vp, _i64]),
@@ -325,6 +329,42 @@ def pa_decode_partitions(k_pool, v_pool, q, block_tables, context_lens, scale: f
                                        block_tables.shape[1], float(scale), int(partition_size),
                                        _ptr(part_out), _ptr(part_max), _ptr(part_sum), max_parts,
                                        _stream(stream)))
+
+
+def prefill_workspace_bytes(num_seqs: int, num_tokens: int, num_heads: int,
+                            num_kv_heads: int) -> int:
+    return load().pa_prefill_workspace_bytes(num_seqs, num_tokens, num_heads, num_kv_heads)
+
+
+def prefill_workspace(num_seqs: int, num_tokens: int, num_heads: int, num_kv_heads: int,
+                      device="cuda") -> torch.Tensor:
+    """A device workspace for pa_prefill (256-byte aligned, as torch allocates)."""
+    n = max(prefill_workspace_bytes(num_seqs, num_tokens, num_heads, num_kv_heads), 16)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def pa_prefill(k_pool, v_pool, q, block_tables, query_start, context_lens, scale: float, out,
+               workspace=None, stream=None, k_scale: float = 1.0, v_scale: float = 1.0) -> None:
+    """Causal attention of a flattened mixed batch (see include/pagedattn.h)."""
+    cache = make_cache(k_pool, v_pool, k_scale, v_scale)
+    num_tokens, num_heads = q.shape[0], q.shape[1]
+    num_seqs = context_lens.shape[0]
+    _require(q.dtype == torch.bfloat16 and q.is_contiguous() and q.dim() == 3,
+             "q must be contiguous bf16 [num_tokens][num_heads][head_dim]")
+    _require(out.shape == q.shape and out.is_contiguous(), "out must match q's shape")
+    _require(block_tables.dtype == torch.int32 and block_tables.is_contiguous() and
+             block_tables.dim() == 2 and block_tables.shape[0] == num_seqs,
+             "block_tables must be contiguous int32 [num_seqs][max_blocks]")
+    _require(query_start.dtype == torch.int32 and query_start.numel() == num_seqs + 1 and
+             context_lens.dtype == torch.int32, "query_start int32 [S+1], context_lens int32 [S]")
+    if workspace is None:
+        workspace = prefill_workspace(num_seqs, num_tokens, num_heads, k_pool.shape[1],
+                                      device=q.device)
+    _check(load().pa_prefill(ctypes.byref(cache), _ptr(q), _ptr(block_tables), _ptr(query_start),
+                             _ptr(context_lens), num_seqs, num_tokens, num_heads,
+                             block_tables.shape[1], float(scale), _ptr(out), _dtype_code(out),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _stream(stream)))
 
 
 def pa_splitkv_reduce(part_out, part_max, part_sum, context_lens, partition_size: int, out,

@@ -590,3 +590,118 @@ def random_partials(seed: int, num_seqs: int, num_heads: int, head_dim: int,
         mx[i, :, live:] = np.nan
         sm[i, :, live:] = np.nan
     return out, mx, sm
+
+
+# ---------------------------------------------------------------------------
+# Mixed-batch (prefill) workloads
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class PrefillWorkload:
+    """Inputs of one mixed-batch attention call (pa_prefill).
+
+    Sequence i owns query rows ``query_start[i] .. query_start[i+1]-1`` of ``q``
+    (its last n_i positions); its ``context_lens[i]`` rows are in the pools
+    already (this step's writes included).  Everything outside the owned rows
+    is NaN, and table entries past a sequence's last block point at a poisoned
+    block.
+    """
+
+    name: str
+    seed: int
+    dtype: str
+    k_scale: float
+    v_scale: float
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    q: np.ndarray              # [num_tokens][num_heads][head_dim], bf16 bits
+    k_pool: np.ndarray
+    v_pool: np.ndarray
+    block_tables: np.ndarray   # int32 [num_seqs][max_blocks]
+    query_start: np.ndarray    # int32 [num_seqs + 1]
+    context_lens: np.ndarray   # int32 [num_seqs]
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.context_lens)
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.query_start[-1])
+
+    def flops(self) -> int:
+        """Algorithmic flops: 4 * head_dim per (query row, head, visible key)."""
+        total = 0
+        for i in range(self.num_seqs):
+            n, L = int(self.query_start[i + 1] - self.query_start[i]), int(self.context_lens[i])
+            first = L - n + 1                       # keys seen by the first query token
+            total += (first + L) * n // 2 if n else 0
+        return 4 * self.head_dim * self.num_heads * total
+
+
+def prefill_batch(name: str, seed: int, lens, nq, num_heads: int = 32, num_kv_heads: int = 8,
+                  head_dim: int = 128, block_size: int = 16, dtype: str = "bf16",
+                  zero_query: bool = False, slack: float = 1.1) -> PrefillWorkload:
+    """A mixed batch: sequence i has context lens[i] and nq[i] query tokens."""
+    lens = [int(x) for x in lens]
+    nq = [int(x) for x in nq]
+    if len(lens) != len(nq) or any(n < 0 or n > L for n, L in zip(nq, lens)):
+        raise ValueError("need 0 <= nq[i] <= lens[i]")
+    streams = _streams(seed)
+    num_blocks, _pool, seq_blocks = _scatter_placement(streams["placement"], lens, block_size,
+                                                       slack=slack, extra_blocks=1)
+    k_pool, v_pool = _fill_pools(streams["pool_seq"], num_blocks, num_kv_heads, block_size,
+                                 head_dim, dtype)
+    owned = np.zeros((num_blocks, block_size), dtype=bool)
+    for blocks, n in zip(seq_blocks, lens):
+        for j, b in enumerate(blocks):
+            owned[b, : min(block_size, n - j * block_size)] = True
+    bidx, ridx = np.nonzero(~owned)
+    for pool in (k_pool, v_pool):
+        pool.view(bits_dtype(dtype))[bidx, :, ridx, :] = nan_bits(dtype)
+    unowned = np.nonzero(~owned.any(axis=1))[0]
+    filler = int(unowned[0]) if len(unowned) else 0
+    width = max(blocks_for(n, block_size) for n in lens) + 1
+    tables = np.full((len(lens), width), filler, dtype=np.int32)
+    for i, blocks in enumerate(seq_blocks):
+        tables[i, : len(blocks)] = blocks
+    qs = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    qdt = query_dtype(dtype)
+    q = draw_values(streams["q"], (int(qs[-1]), num_heads, head_dim), qdt)
+    if zero_query:
+        q = np.zeros_like(q)
+    scale = FP8_SCALE if dtype == "fp8" else 1.0
+    return PrefillWorkload(name=name, seed=seed, dtype=dtype, k_scale=scale, v_scale=scale,
+                           num_heads=num_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                           block_size=block_size, q=q, k_pool=k_pool, v_pool=v_pool,
+                           block_tables=tables, query_start=qs,
+                           context_lens=np.asarray(lens, dtype=np.int32))
+
+
+def prefill_config(name: str, dtype: str = "bf16", block_size: int = 16) -> PrefillWorkload:
+    """Named mixed-batch workloads at the 8B-class head layout (32 / 8 heads, dim 128).
+
+    * ``cached_preamble``: 16 requests of 1,200-token prompts whose first 896
+      tokens (56 blocks) are already cached, so 304 tokens each are computed -
+      the worked example of "LLM paged attention arch", section "End-to-end
+      flow", sixteen times (seed 9311);
+    * ``long_prompts``: 4 prompts of 4,096 tokens computed from scratch (9312);
+    * ``mixed_step``: a chunked-prefill step under an 8,192-token budget - 60
+      decodes with contexts U{128..4096}, one 2,048-token slice of a prompt
+      whose first 2,048 tokens were computed in an earlier step, and one
+      1,024-token prompt from scratch (9313).
+    """
+    if name == "cached_preamble":
+        return prefill_batch(name, 9311, [1200] * 16, [304] * 16, dtype=dtype,
+                             block_size=block_size)
+    if name == "long_prompts":
+        return prefill_batch(name, 9312, [4096] * 4, [4096] * 4, dtype=dtype,
+                             block_size=block_size)
+    if name == "mixed_step":
+        rng = np.random.default_rng(9313)
+        lens = [int(x) for x in rng.integers(128, 4097, 60)] + [4096, 1024]
+        nq = [1] * 60 + [2048, 1024]
+        return prefill_batch(name, 9313, lens, nq, dtype=dtype, block_size=block_size)
+    raise ValueError(f"unknown prefill workload {name!r}")

@@ -3,6 +3,7 @@ symbol the header declares, and rejects bad arguments on the host before any
 HIP call (these calls never reach a kernel)."""
 
 import ctypes
+import math
 import glob
 import os
 import re
@@ -206,3 +207,36 @@ def test_block_manager_structs():
     assert ctypes.sizeof(lib.PaStepPlan) == 7 * 4 + 4 + 10 * 8
     assert ctypes.sizeof(lib.PaBmStats) == 12 * 8
     assert ctypes.sizeof(lib.PaRequestInfo) == 8 + 5 * 8
+
+
+def test_prefill_workspace_bytes():
+    # 1 count + 2 ints per tile; tiles <= ceil(tokens / (128 / G)) + sequences
+    assert lib.prefill_workspace_bytes(3, 100, 8, 2) == 4 * (1 + 2 * (math.ceil(100 / 32) + 3))
+    assert lib.prefill_workspace_bytes(3, 100, 8, 3) == 0       # not a multiple
+    assert lib.prefill_workspace_bytes(3, 100, 48, 3) == 0      # ratio 16
+    assert lib.prefill_workspace_bytes(-1, 100, 8, 2) == 0
+
+
+def test_prefill_rejects_bad_arguments():
+    call = lib.raw_call
+    c = _cache(dtype=lib.PA_BF16, head_dim=128, block_size=16, num_kv_heads=2)
+
+    def pf(cache=c, S=2, T=10, H=8, W=4, scale=0.1, od=lib.PA_F32, ws=256, wsb=4096, q=16,
+           out=16):
+        return call("pa_prefill", ctypes.byref(cache) if cache is not None else None, q, 16, 16,
+                    16, S, T, H, W, scale, out, od, ws, wsb, None)
+    assert pf(cache=None) == 1
+    assert pf(cache=_cache(dtype=lib.PA_F32, head_dim=128, block_size=16, num_kv_heads=2)) == 3
+    assert pf(cache=_cache(dtype=lib.PA_BF16, head_dim=64, block_size=16, num_kv_heads=2)) == 3
+    assert pf(cache=_cache(dtype=lib.PA_BF16, head_dim=128, block_size=8, num_kv_heads=2)) == 3
+    assert pf(H=6) == 3          # ratio 3
+    assert pf(H=7) == 2          # not a multiple
+    assert pf(scale=0.0) == 2
+    assert pf(od=7) == 3
+    assert pf(S=0) == 0 and pf(T=0) == 0
+    assert pf(q=None) == 1
+    assert pf(q=8) == 2          # misaligned
+    assert pf(ws=None) == 4
+    assert pf(wsb=8) == 4
+    assert pf(ws=16) == 2        # not 256-byte aligned
+    assert pf(W=0) == 2
