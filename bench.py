@@ -20,7 +20,8 @@ event inside: ``--steps`` whole steps (``value``, ``ms_per_step``), then
 Prints one JSON line.  ``value`` is the KV bytes the step's decode must read
 divided by the step time (GB/s).
 
-``--part swap`` instead times block swaps between the device pools and pinned
+``--part prefill`` times mixed-batch attention (pa_prefill) on three named
+workloads against the bf16 MFMA peak; ``--part swap`` times block swaps between the device pools and pinned
 host pools (pa_swap_blocks, both directions, 8B-class blocks) against the
 PCIe link; ``--part scheduler`` times the host-side block manager's step on a
 serving trace at the batch-64 scale, native against the oracle (no GPU
@@ -47,6 +48,7 @@ from paged_kv_cache_93_amd import lib  # noqa: E402
 from paged_kv_cache_93_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense
 # PCIe 5.0 x16 host link, per direction: 32 GT/s x 16 lanes x 128/130 / 8 bits
 PCIE_PEAK_GBPS = 32.0 * 16 * 128 / 130 / 8
 
@@ -275,6 +277,60 @@ def bench_swap(args) -> dict:
     }
 
 
+def bench_prefill(args) -> dict:
+    """pa_prefill on the named mixed-batch workloads (8B-class heads, bf16 or
+    8-bit cache): algorithmic flops per launch / average launch time."""
+    import torch
+
+    names = ["cached_preamble", "long_prompts", "mixed_step"]
+    dtype = args.dtype or "bf16"
+    rows = {}
+    for name in names:
+        w = W.prefill_config(name, dtype=dtype)
+        k, v = to_device(w.k_pool, w.dtype), to_device(w.v_pool, w.dtype)
+        q = to_device(w.q, "bf16")
+        tables = torch.from_numpy(w.block_tables).cuda()
+        qs = torch.from_numpy(w.query_start).cuda()
+        lens = torch.from_numpy(w.context_lens).cuda()
+        out = torch.empty((w.num_tokens, w.num_heads, w.head_dim), dtype=torch.bfloat16,
+                          device="cuda")
+        ws = lib.prefill_workspace(w.num_seqs, w.num_tokens, w.num_heads, w.num_kv_heads)
+        scale = 1.0 / math.sqrt(w.head_dim)
+
+        def call():
+            lib.pa_prefill(k, v, q, tables, qs, lens, scale, out, workspace=ws,
+                           k_scale=w.k_scale, v_scale=w.v_scale)
+
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / args.steps * 1e3
+        tflops = w.flops() / (us * 1e-6) / 1e12
+        rows[name] = dict(us=round(us, 1), gflop=round(w.flops() / 1e9, 2),
+                          tflops=round(tflops, 1), frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                          seqs=w.num_seqs, tokens=w.num_tokens)
+        print(f"# prefill {name}: {us:.1f} us, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    head = rows["cached_preamble"]
+    return {
+        "metric": "paged prefill attention TFLOP/s (pa_prefill, mixed batches)",
+        "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": "cached_preamble: 16 x (304 new tokens over a 1,200-token "
+                               "context), 32 query / 8 KV heads, head_dim 128, 16-token blocks"},
+        "workloads": rows,
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": head["tflops"],
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": head["frac"],
+                     "traffic": None},
+    }
+
+
 class ServingTrace:
     """Seeded serving workload for the block manager at the batch-64 scale.
 
@@ -425,7 +481,7 @@ def main() -> int:
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from two --pmc-pass counter runs")
     ap.add_argument("--pmc-command", default="", help="command line recorded in the summary")
-    ap.add_argument("--part", default="decode", choices=["decode", "swap", "scheduler"],
+    ap.add_argument("--part", default="decode", choices=["decode", "swap", "scheduler", "prefill"],
                     help="decode: the decode step (default); swap: block swaps to pinned host "
                          "memory; scheduler: the host block manager (no GPU needed)")
     ap.add_argument("--swap-blocks", type=int, default=1024, help="blocks per swap launch")
@@ -450,6 +506,9 @@ def main() -> int:
     lib.load()
     if args.part == "swap":
         print(json.dumps(bench_swap(args)), flush=True)
+        return 0
+    if args.part == "prefill":
+        print(json.dumps(bench_prefill(args)), flush=True)
         return 0
 
     w = W.make_config(args.workload, dtype=args.dtype, block_size=args.block_size)

@@ -31,6 +31,8 @@
 // * Weights are rounded to bf16 for the matrix product, and the running sum
 //   adds the rounded weights, so the output is an exact convex combination of
 //   V rows with weights within 2^-9 (relative) of the true ones.
+#include <type_traits>
+
 #include "pa_decode_kernel.h"
 #include "pa_internal.h"
 
@@ -48,6 +50,14 @@ constexpr int kVStride = 36;      // bf16 per transposed V row in LDS (32 + 4 pa
 constexpr int kKBytes = kKeys * kKStride * 16;
 constexpr int kVBytes = kD * kVStride * 2;
 constexpr int kBufBytes = kKBytes + kVBytes;
+
+// Key-pair slot swizzle of the transposed V tile: dims 32x..32x+31 XOR their
+// pair slot with 4x (an even number, so the two pairs a fragment read takes
+// stay adjacent).  With 72-byte rows, the transposed writes of a wave (16 dim
+// chunks x 4 key pairs) then land in 64 distinct banks.
+__device__ __forceinline__ int vswz(int dim) { return 4 * ((dim >> 5) & 3); }
+
+constexpr bf16x2 kOnes = {__bf16(1.0f), __bf16(1.0f)};
 
 struct PrefillArgs {
   const uint8_t* q;
@@ -125,11 +135,18 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int t = blockIdx.x;
+  // Workgroups go to the 8 XCDs round-robin by linear id; renumber them so
+  // each XCD takes a contiguous run of (KV head, tile) items - the tiles of one
+  // sequence and head then share that XCD's L2.
+  const int nwg = gridDim.x * gridDim.y;
+  const int id = blockIdx.y * gridDim.x + blockIdx.x;
+  const int xcd = id % 8, slot = id / 8;
+  const int logical = xcd * (nwg / 8) + min(xcd, nwg % 8) + slot;
+  const int t = logical % gridDim.x;
+  const int g = logical / gridDim.x;
   if (t >= a.tiles[0]) return;
   const int seq = a.tiles[1 + 2 * t];
   const int tile = a.tiles[2 + 2 * t];
-  const int g = blockIdx.y;
   if (seq < 0 || seq >= a.num_seqs) return;
 
   const int32_t qs0 = min(max(a.query_start[seq], 0), a.num_tokens);
@@ -165,42 +182,65 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
   }
 
   // ---- K/V tile staging -------------------------------------------------------
-  // Thread tid loads dims [8*dc, 8*dc+8) of keys 2kp and 2kp+1 of the tile.
+  // Thread tid loads dims [8*dc, 8*dc+8) of keys 2kp and 2kp+1 of a tile (one
+  // block: block sizes are even).  Loads run two tiles ahead of the math (two
+  // register sets), block-table entries three tiles ahead.
   const int dc = tid & 15, kp = tid >> 4;
-  Raw kr[2], vr[2];
-  auto load_tile = [&](int k0) {
+  Raw kr[2][2], vr[2][2];
+  // key 2kp of a tile sits at row (2kp) % BS of its block (tiles start at
+  // multiples of 32, a multiple of BS), so a lane's offset inside a block is fixed
+  constexpr int kRowBytes = kD * EB;
+  const int64_t blk_stride = int64_t(a.num_kv_heads) * BS * kRowBytes;
+  const int64_t lane_off = (int64_t(g) * BS + (2 * kp) % BS) * kRowBytes + dc * 8 * EB;
+  auto table_entry = [&](int k0) -> int {
+    const int key = k0 + 2 * kp;
+    return key < kend ? table[key / BS] : -1;
+  };
+  auto load_tile = [&](int set, int k0, int phys) {
+    const bool ok = phys >= 0 && int64_t(phys) < a.num_blocks;
+    if (k0 + kKeys <= kend && __ballot(!ok) == 0) {
+      // whole tile inside the context, every block in the pool: no conditions
+      const uint8_t* kb = a.k_pool + int64_t(phys) * blk_stride + lane_off;
+      const uint8_t* vb = a.v_pool + int64_t(phys) * blk_stride + lane_off;
+      kr[set][0] = *reinterpret_cast<const Raw*>(kb);
+      kr[set][1] = *reinterpret_cast<const Raw*>(kb + kRowBytes);
+      vr[set][0] = *reinterpret_cast<const Raw*>(vb);
+      vr[set][1] = *reinterpret_cast<const Raw*>(vb + kRowBytes);
+      return;
+    }
+    // the context's last tile, or a block id outside the pool: those rows are zero
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int key = k0 + 2 * kp + e;
-      kr[e] = Raw{};
-      vr[e] = Raw{};
-      if (key < kend) {
-        const int phys = table[key / BS];
-        if (phys >= 0 && int64_t(phys) < a.num_blocks) {
-          const int64_t off =
-              ((int64_t(phys) * a.num_kv_heads + g) * BS + key % BS) * (kD * EB) + dc * 8 * EB;
-          kr[e] = *reinterpret_cast<const Raw*>(a.k_pool + off);
-          vr[e] = *reinterpret_cast<const Raw*>(a.v_pool + off);
-        }
+      kr[set][e] = Raw{};
+      vr[set][e] = Raw{};
+      if (key < kend && ok) {
+        const int64_t off = int64_t(phys) * blk_stride + lane_off + e * kRowBytes;
+        kr[set][e] = *reinterpret_cast<const Raw*>(a.k_pool + off);
+        vr[set][e] = *reinterpret_cast<const Raw*>(a.v_pool + off);
       }
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int set, int buf) {
     u32x4* lk = reinterpret_cast<u32x4*>(s_mem + buf * kBufBytes);
     uint32_t* lv = reinterpret_cast<uint32_t*>(s_mem + buf * kBufBytes + kKBytes);
     u32x4 kb[2], vb[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      kb[e] = score_chunk<ET>(kr[e]);
-      vb[e] = score_chunk<ET>(vr[e]);
+      kb[e] = score_chunk<ET>(kr[set][e]);
+      vb[e] = score_chunk<ET>(vr[set][e]);
       lk[(2 * kp + e) * kKStride + dc] = kb[e];
     }
-    // V transposed: dim 8dc + x gets the pair (key 2kp, key 2kp+1) as one word
+    // V transposed: dim 8dc + x gets the pair (key 2kp, key 2kp+1) as one word,
+    // at pair slot kp ^ vswz(dim) (a wave's 64 writes hit 64 distinct banks)
+    const int kps = kp ^ vswz(8 * dc);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t a0 = vb[0][w], a1 = vb[1][w];  // dims 8dc+2w, 8dc+2w+1 of each key
-      lv[((8 * dc + 2 * w) * kVStride) / 2 + kp] = (a0 & 0xFFFFu) | (a1 << 16);
-      lv[((8 * dc + 2 * w + 1) * kVStride) / 2 + kp] = (a0 >> 16) | (a1 & 0xFFFF0000u);
+      // low halves of both words, then high halves (v_perm byte selects)
+      lv[((8 * dc + 2 * w) * kVStride) / 2 + kps] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+      lv[((8 * dc + 2 * w + 1) * kVStride) / 2 + kps] =
+          __builtin_amdgcn_perm(a1, a0, 0x07060302u);
     }
   };
 
@@ -217,15 +257,24 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
   const int min_pos = c + j0;
   const int ntiles = kend > 0 ? (kend + kKeys - 1) / kKeys : 0;
 
+  // prologue: tile 0 in LDS, tile 1 in flight, the table entry of tile 2 in flight
+  int next_phys = -1;
   if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
+    load_tile(0, 0, table_entry(0));
+    if (ntiles > 1) load_tile(1, kKeys, table_entry(kKeys));
+    if (ntiles > 2) next_phys = table_entry(2 * kKeys);
+    store_tile(0, 0);
   }
   __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
+  // one key tile; BUF (= kt & 1) is a constant, so every register set is static
+  auto iteration = [&](int kt, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
     const int k0 = kt * kKeys;
-    if (kt + 1 < ntiles) load_tile(k0 + kKeys);
+    // tile kt+2 into the register set tile kt used (it is in LDS already)
+    if (kt + 2 < ntiles) {
+      load_tile(buf, k0 + 2 * kKeys, next_phys);
+      if (kt + 3 < ntiles) next_phys = table_entry(k0 + 3 * kKeys);
+    }
     const u32x4* lk = reinterpret_cast<const u32x4*>(s_mem + buf * kBufBytes);
     const uint8_t* lv = s_mem + buf * kBufBytes + kKBytes;
 
@@ -249,39 +298,45 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     }
 
     // online softmax per row; the P^T operand in the k order
-    // [4g .. 4g+3, 16+4g .. 16+4g+3]
+    // [4g .. 4g+3, 16+4g .. 16+4g+3].  Only tiles that reach past the tile's
+    // first position need the causal mask; the max is taken on raw scores
+    // (the scale is positive) and the scale enters with the exponent's fma.
     u32x4 pf[2];
-    const bool diag = k0 + kKeys - 1 > min_pos;  // some key may lie past some row
+    if (k0 + kKeys - 1 > min_pos) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (k0 + 16 * h + 4 * grp + v > pos[rt]) s[rt][h][v] = kNegInf;
+    }
+    const float sc = a.scale_log2;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-      float sv[8];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float x = s[rt][h][v] * a.scale_log2;
-          if (diag && k0 + 16 * h + 4 * grp + v > pos[rt]) x = kNegInf;
-          sv[4 * h + v] = x;
-        }
-      float mx = sv[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-      mx = xor_max<16>(mx);
-      const float mnew = fmaxf(m[rt], mx);
+      float mx = fmaxf(fmaxf(fmaxf(s[rt][0][0], s[rt][0][1]), fmaxf(s[rt][0][2], s[rt][0][3])),
+                       fmaxf(fmaxf(s[rt][1][0], s[rt][1][1]), fmaxf(s[rt][1][2], s[rt][1][3])));
+      mx = xor_max<16>(mx) * sc;
+      // The exponent base moves only when the row maximum passes it by more
+      // than 8 (log2 units): weights stay <= 2^8, the accumulators are
+      // rescaled rarely, and the result is the same softmax.
+      const bool move = mx > m[rt] + 8.f;
+      const float mnew = move ? mx : m[rt];
       const float base = mnew == kNegInf ? 0.f : mnew;
-      const float alpha = fast_exp2(m[rt] - base);
+      const float alpha = move ? fast_exp2(m[rt] - base) : 1.f;
       m[rt] = mnew;
       float psum = 0.f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const f32x2 pp = {fast_exp2(sv[2 * w] - base), fast_exp2(sv[2 * w + 1] - base)};
+        const int h = w >> 1, v = 2 * (w & 1);
+        const f32x2 pp = {fast_exp2(fmaf(s[rt][h][v], sc, -base)),
+                          fast_exp2(fmaf(s[rt][h][v + 1], sc, -base))};
         const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
-        const uint32_t word = __builtin_bit_cast(uint32_t, pb);
-        pf[rt][w] = word;
-        psum += __uint_as_float(word << 16) + __uint_as_float(word & 0xFFFF0000u);
+        pf[rt][w] = __builtin_bit_cast(uint32_t, pb);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(pb, kOnes, psum, false);  // adds the rounded pair
       }
       lsum[rt] = fmaf(lsum[rt], alpha, psum);
-      if (alpha != 1.f) {
+      if (__ballot(move) != 0) {
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) acc[rt][dt] *= alpha;
       }
@@ -290,9 +345,11 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     // O^T += V^T P^T: A = dims 16dt + r, keys in the permuted k order
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const uint8_t* row = lv + (16 * dt + r16) * kVStride * 2;
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(row + 8 * grp);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 32 + 8 * grp);
+      const int dim = 16 * dt + r16;
+      const uint8_t* row = lv + dim * kVStride * 2;
+      const int sw = vswz(dim);
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(row + 4 * ((2 * grp) ^ sw));
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 4 * ((8 + 2 * grp) ^ sw));
       const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
@@ -301,8 +358,12 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
             0, 0);
     }
 
-    if (kt + 1 < ntiles) store_tile(buf ^ 1);
+    if (kt + 1 < ntiles) store_tile(buf ^ 1, buf ^ 1);
     __syncthreads();
+  };
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    iteration(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < ntiles) iteration(kt + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- finalise: lane 16g + r holds dims 16dt + 4g + v of row r -------------
@@ -320,7 +381,9 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
         *reinterpret_cast<f32x4*>(dst) = o;
       } else {
         uint16_t* dst = static_cast<uint16_t*>(a.out) + row_index[rt] * kD + d0;
-        const u32x2 w = {to_bf16(o[0]) | (to_bf16(o[1]) << 16), to_bf16(o[2]) | (to_bf16(o[3]) << 16)};
+        const bf16x2 lo = __builtin_convertvector((f32x2{o[0], o[1]}), bf16x2);
+        const bf16x2 hi = __builtin_convertvector((f32x2{o[2], o[3]}), bf16x2);
+        const u32x2 w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
         *reinterpret_cast<u32x2*>(dst) = w;
       }
     }
