@@ -12,6 +12,9 @@ Each module lists the passages it follows.
 
 from .paged_attention import (  # noqa: F401
     E4M3_MAX,
+    alibi_bias,
+    alibi_slopes,
+    attended_range,
     blocks_needed,
     copy_blocks,
     decode,

@@ -269,7 +269,8 @@ def _softmax_weighted_sum(scores: np.ndarray, values: np.ndarray):
 
 
 def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float,
-           dtype: str, k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+           dtype: str, k_scale: float = 1.0, v_scale: float = 1.0, window: int = 0,
+           alibi_slopes=None) -> np.ndarray:
     """Decode attention of one query token per sequence over a paged KV cache.
 
     For sequence i and query head h (KV head g = h // G):
@@ -282,7 +283,9 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float,
     modification".  A sequence with L_i = 0 gets an all-zero output (the pages
     never produce one; decode always has the new token).  For an 8-bit cache
     (``dtype="fp8"``) k_t and v_t are the stored codes' values times
-    ``k_scale`` / ``v_scale`` and q holds bfloat16 bit patterns.
+    ``k_scale`` / ``v_scale`` and q holds bfloat16 bit patterns.  ``window``
+    and ``alibi_slopes`` select the attention variants of :func:`attended_range`
+    and :func:`alibi_bias` (defaults: neither).
 
     Returns float64 ``[num_seqs][num_heads][head_dim]``.
     """
@@ -300,10 +303,51 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float,
                            dtype, k_scale)
             values = _kv_f64(gather_rows(v_pool, block_tables[i], length, block_size, g),
                              dtype, v_scale)
+            lo, hi = attended_range(length - 1, window)
             for h in range(g * group, (g + 1) * group):
-                scores = scale * (keys @ q64[i, h])
-                out[i, h], _, _ = _softmax_weighted_sum(scores, values)
+                scores = scale * (keys[lo:hi] @ q64[i, h])
+                scores = scores + alibi_bias(alibi_slopes, h, lo, hi, length - 1)
+                out[i, h], _, _ = _softmax_weighted_sum(scores, values[lo:hi])
     return out
+
+
+def attended_range(position: int, window: int = 0):
+    """Positions [lo, hi) a query at ``position`` attends to.
+
+    Causal attention sees 0..position ("PagedAttention and continuous
+    batching", section "Attention kernel modification").  A sliding window of W
+    tokens - one of the variants "Paged Attention as a Memory Manager", section
+    "When It Falls Down", names - keeps the last W of them, position-W+1 ..
+    position (the window's usual definition: a token sees itself and the W-1
+    before it).  window = 0 means no window.
+    """
+    if window < 0:
+        raise ValueError("window must be >= 0")
+    hi = visible_keys(position)
+    lo = max(0, position - window + 1) if window else 0
+    return lo, hi
+
+
+def alibi_bias(slopes, head: int, lo: int, hi: int, position: int):
+    """ALiBi score bias of keys lo..hi-1 for a query at ``position`` (0 if no slopes).
+
+    ALiBi, the other variant the same passage names, adds to each score a
+    penalty linear in the key's distance from the query: slope_h * (t - position)
+    for key t and query head h (Press, Smith and Lewis, "Train Short, Test Long:
+    Attention with Linear Biases").
+    """
+    if slopes is None:
+        return 0.0
+    t = np.arange(lo, hi, dtype=np.float64)
+    return float(slopes[head]) * (t - position)
+
+
+def alibi_slopes(num_heads: int) -> np.ndarray:
+    """The geometric ALiBi slopes of the paper for a power-of-two head count:
+    head h (from 0) gets 2^(-8 (h+1) / num_heads)."""
+    if num_heads <= 0 or num_heads & (num_heads - 1):
+        raise ValueError("num_heads must be a power of two")
+    return np.array([2.0 ** (-8.0 * (h + 1) / num_heads) for h in range(num_heads)])
 
 
 def query_position(context_len: int, num_query: int, j: int) -> int:
@@ -324,7 +368,8 @@ def visible_keys(position: int) -> int:
 
 
 def prefill(q, k_pool, v_pool, block_tables, query_start, context_lens, scale: float,
-            dtype: str, k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+            dtype: str, k_scale: float = 1.0, v_scale: float = 1.0, window: int = 0,
+            alibi_slopes=None) -> np.ndarray:
     """Causal attention of every scheduled query token of a mixed batch.
 
     The batch is one flattened sequence of query tokens: sequence i owns rows
@@ -338,7 +383,9 @@ def prefill(q, k_pool, v_pool, block_tables, query_start, context_lens, scale: f
     ("PagedAttention and continuous batching", section "Attention kernel
     modification"); scores and softmax are those of :func:`decode`.  A decode
     row is the case n_i = 1 (p = L_i - 1).  Rows with p < 0 (more query tokens
-    than context: a caller error) are left zero.
+    than context: a caller error) are left zero.  ``window`` and
+    ``alibi_slopes`` select the variants of :func:`attended_range` and
+    :func:`alibi_bias`.
 
     Returns float64 ``[num_tokens][num_heads][head_dim]``.
     """
@@ -367,10 +414,11 @@ def prefill(q, k_pool, v_pool, block_tables, query_start, context_lens, scale: f
                 p = query_position(length, n, j)
                 if p < 0:
                     continue
-                seen = visible_keys(p)
+                lo, hi = attended_range(p, window)
                 for h in range(g * group, (g + 1) * group):
-                    scores = scale * (keys[:seen] @ q64[starts[i] + j, h])
-                    out[starts[i] + j, h], _, _ = _softmax_weighted_sum(scores, values[:seen])
+                    scores = scale * (keys[lo:hi] @ q64[starts[i] + j, h])
+                    scores = scores + alibi_bias(alibi_slopes, h, lo, hi, p)
+                    out[starts[i] + j, h], _, _ = _softmax_weighted_sum(scores, values[lo:hi])
     return out
 
 
