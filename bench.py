@@ -286,7 +286,7 @@ def bench_prefill(args) -> dict:
     dtype = args.dtype or "bf16"
     rows = {}
     for name in names:
-        w = W.prefill_config(name, dtype=dtype)
+        w = W.prefill_config(name, dtype=dtype, block_size=args.block_size or 16)
         k, v = to_device(w.k_pool, w.dtype), to_device(w.v_pool, w.dtype)
         q = to_device(w.q, "bf16")
         tables = torch.from_numpy(w.block_tables).cuda()
@@ -323,7 +323,8 @@ def bench_prefill(args) -> dict:
         "warmup": args.warmup, "higher_is_better": True, "vs_baseline": None, "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": "cached_preamble: 16 x (304 new tokens over a 1,200-token "
-                               "context), 32 query / 8 KV heads, head_dim 128, 16-token blocks"},
+                               "context), 32 query / 8 KV heads, head_dim 128",
+                   "block_size": args.block_size or 16},
         "workloads": rows,
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": head["tflops"],
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": head["frac"],

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 4
+#define PA_ABI_VERSION 5
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -73,7 +73,7 @@ typedef struct pa_cache {
   void *v_pool;          /* DEVICE, same shape and type as k_pool */
   int64_t num_blocks;    /* physical blocks in each pool, > 0 */
   int32_t num_kv_heads;  /* > 0 */
-  int32_t block_size;    /* tokens per block: 16 or 32 */
+  int32_t block_size;    /* tokens per block: 8, 16 or 32 */
   int32_t head_dim;      /* 64 or 128 */
   int32_t dtype;         /* pa_dtype of both pools */
   float k_scale;         /* PA_FP8_E4M3: dequantisation scales of the pools, positive */
@@ -207,6 +207,23 @@ int pa_decode(const pa_cache *cache, const void *q, const int32_t *block_tables,
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim);
 
 /*
+ * Attention variants.  The pages name sliding windows and ALiBi as variants a
+ * paged kernel has to re-derive its block traversal for ("Paged Attention as
+ * a Memory Manager", section "When It Falls Down"); their definitions are the
+ * published ones:
+ *   sliding_window = W > 0: a query at position p attends to p-W+1 .. p only
+ *                    (itself and the W-1 tokens before it); 0: no window.
+ *   alibi_slopes:    DEVICE float [num_heads] or NULL; score(t) gains
+ *                    slope[h] * (t - p) (Press, Smith and Lewis, "Train Short,
+ *                    Test Long: Attention with Linear Biases").
+ */
+typedef struct pa_attn_variant {
+  int32_t sliding_window;
+  int32_t reserved;             /* 0 */
+  const float *alibi_slopes;
+} pa_attn_variant;
+
+/*
  * pa_prefill - causal attention of a mixed batch: many query tokens per
  * sequence (prompt slices) and single tokens (decodes) in one call.
  *
@@ -233,16 +250,18 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t he
  *   num_heads     ratio to num_kv_heads 1, 2, 4 or 8
  *   out           DEVICE [num_tokens][num_heads][128] of out_dtype (PA_F32 or PA_BF16),
  *                 16-byte aligned; rows of sequences with n_i = 0 are not written
+ *   variant       HOST pa_attn_variant, or NULL for plain causal attention
  *   workspace     DEVICE scratch, >= pa_prefill_workspace_bytes(), 256-byte aligned;
  *                 contents need no initialising.  Calls in flight at the same time
  *                 must not share one.
- * Supported: bf16 and 8-bit (E4M3) caches, head_dim 128, block_size 16 or 32.
+ * Supported: bf16 and 8-bit (E4M3) caches, head_dim 128, block_size 8, 16 or 32.
+ * With a variant, decode rows (n_i = 1) go through here too.
  */
 int pa_prefill(const pa_cache *cache, const void *q, const int32_t *block_tables,
                const int32_t *query_start, const int32_t *context_lens, int32_t num_seqs,
                int32_t num_tokens, int32_t num_heads, int32_t max_blocks_per_seq, float scale,
-               void *out, int32_t out_dtype, void *workspace, size_t workspace_bytes,
-               void *stream);
+               const pa_attn_variant *variant, void *out, int32_t out_dtype, void *workspace,
+               size_t workspace_bytes, void *stream);
 
 /* Workspace bytes pa_prefill needs for these sizes (0 for invalid sizes). */
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,

@@ -11,6 +11,8 @@
 static_assert(sizeof(pa_cache) == 48 && offsetof(pa_cache, dtype) == 36 &&
                   offsetof(pa_cache, k_scale) == 40 && offsetof(pa_cache, v_scale) == 44,
               "pa_cache layout is part of the ABI");
+static_assert(sizeof(pa_attn_variant) == 16 && offsetof(pa_attn_variant, alibi_slopes) == 8,
+              "pa_attn_variant layout is part of the ABI");
 
 namespace pa {
 

@@ -81,8 +81,8 @@ int prepare(const char* fn, const pa_cache* cache, const void* q, const int32_t*
   if (cache->head_dim != 64 && cache->head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "%s: head_dim must be 64 or 128 (got %d)", fn,
                 cache->head_dim);
-  if (cache->block_size != 16 && cache->block_size != 32)
-    return fail(PA_ERR_UNSUPPORTED, "%s: block_size must be 16 or 32 (got %d)", fn,
+  if (cache->block_size != 8 && cache->block_size != 16 && cache->block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size must be 8, 16 or 32 (got %d)", fn,
                 cache->block_size);
   if (!(scale > 0.f) || !std::isfinite(scale))
     return fail(PA_ERR_SHAPE, "%s: scale must be positive and finite", fn);
@@ -160,7 +160,7 @@ PA_API int pa_decode(const pa_cache* cache, const void* q, const int32_t* block_
   const hipStream_t s = static_cast<hipStream_t>(stream);
 
   const size_t wave_lds =
-      size_t(waves) * decode_wave_lds_bytes(elem_type(cache->dtype), cache->head_dim, group);
+      size_t(waves) * decode_wave_lds_bytes(elem_type(cache->dtype), cache->head_dim, group, cache->block_size);
   if (workspace == nullptr || num_seqs > kMaxBalancedSeqs) {
     a.mode = kModeSingle;
     return launch(fn, cache, group, a, dim3(unsigned(num_seqs), head_groups), waves, wave_lds, s);
@@ -227,6 +227,6 @@ PA_API int pa_decode_partitions(const pa_cache* cache, const void* q, const int3
   const int waves = waves_per_group(cache->num_kv_heads);
   const dim3 grid(unsigned(max_parts), unsigned(cache->num_kv_heads / waves), unsigned(num_seqs));
   const size_t lds =
-      size_t(waves) * decode_wave_lds_bytes(elem_type(cache->dtype), cache->head_dim, group);
+      size_t(waves) * decode_wave_lds_bytes(elem_type(cache->dtype), cache->head_dim, group, cache->block_size);
   return launch(fn, cache, group, a, grid, waves, lds, static_cast<hipStream_t>(stream));
 }

@@ -276,15 +276,18 @@ __device__ __forceinline__ int group_of_unit(int64_t u, int64_t total, int64_t g
 #define PA_MFMA_SCORES 1  // 0: score every case on the VALU (for comparison)
 #endif
 
-// Scores on the matrix cores: bf16 and 8-bit caches with 128-dim heads.
-constexpr bool decode_uses_mfma(int et, int d) { return PA_MFMA_SCORES && et != kF32 && d == 128; }
+// Scores on the matrix cores: bf16 and 8-bit caches with 128-dim heads and
+// blocks of at least 16 rows (an MFMA tile is 16 rows of one block).
+constexpr bool decode_uses_mfma(int et, int d, int bs) {
+  return PA_MFMA_SCORES && et != kF32 && d == 128 && bs >= 16;
+}
 
 // LDS bytes each wave of the MFMA path uses: a 16-row K tile padded to 17
 // chunks per row (conflict-free transposed reads), the softmax weights
 // [4 row groups][G heads][4 rows], the rescale factors [4][G], and the G
 // query rows of the sequence being scored (16 chunks of 16 bytes each).
-constexpr int decode_wave_lds_bytes(int et, int d, int g) {
-  return decode_uses_mfma(et, d) ? 16 * 17 * 16 + 64 * g + 16 * g + 256 * g : 0;
+constexpr int decode_wave_lds_bytes(int et, int d, int g, int bs) {
+  return decode_uses_mfma(et, d, bs) ? 16 * 17 * 16 + 64 * g + 16 * g + 256 * g : 0;
 }
 
 // Byte offset of the per-wave LDS areas behind the unit prefix (balanced mode).
@@ -303,7 +306,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   constexpr int VEC = LB / EB;                       // elements per lane chunk
   constexpr int LPR = D / VEC;                       // lanes per row
   constexpr int RPI = 64 / LPR;                      // rows per load instruction
-  constexpr bool MF = decode_uses_mfma(ET, D);       // q.k on MFMA (16-row tiles)
+  constexpr bool MF = decode_uses_mfma(ET, D, BS);   // q.k on MFMA (16-row tiles)
   constexpr int QC = MF ? (16 * G + 63) / 64 : 1;    // query chunks a lane loads per tile
   constexpr int TRW = MF ? 16 : (G >= 8 ? 2 : 4) * RPI;  // wide groups keep smaller tiles
   constexpr int TR = BS < TRW ? BS : TRW;            // rows per register tile
@@ -383,7 +386,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   // Per-wave LDS of the MFMA path, behind the unit prefix.
   uint8_t* wave_lds = reinterpret_cast<uint8_t*>(s_prefix) +
                       decode_prefix_lds_bytes(a.num_seqs, a.mode == kModeBalanced) +
-                      size_t(wave) * decode_wave_lds_bytes(ET, D, G);
+                      size_t(wave) * decode_wave_lds_bytes(ET, D, G, BS);
   u32x4* lds_k = reinterpret_cast<u32x4*>(wave_lds);              // [16 rows][17 chunks]
   float* lds_p = reinterpret_cast<float*>(wave_lds + 16 * 17 * 16);  // [4][G][4]
   float* lds_a = lds_p + 16 * G;                                   // [4][G]
@@ -1013,8 +1016,10 @@ bool launch_decode_impl(int d, int bs, int g, const DecodeArgs& a, dim3 grid, in
   }
 #define PA_DECODE_G(D_, BS_) \
   PA_DECODE_CASE(D_, BS_, 1) PA_DECODE_CASE(D_, BS_, 2) PA_DECODE_CASE(D_, BS_, 4) PA_DECODE_CASE(D_, BS_, 8)
+  PA_DECODE_G(64, 8)
   PA_DECODE_G(64, 16)
   PA_DECODE_G(64, 32)
+  PA_DECODE_G(128, 8)
   PA_DECODE_G(128, 16)
   PA_DECODE_G(128, 32)
 #undef PA_DECODE_G
@@ -1039,8 +1044,10 @@ int decode_groups_per_cu_impl(int d, int bs, int g, int waves, size_t lds) {
     return n;                                                                               \
   }
 #define PA_OCC_G(D_, BS_) PA_OCC_CASE(D_, BS_, 1) PA_OCC_CASE(D_, BS_, 2) PA_OCC_CASE(D_, BS_, 4) PA_OCC_CASE(D_, BS_, 8)
+  PA_OCC_G(64, 8)
   PA_OCC_G(64, 16)
   PA_OCC_G(64, 32)
+  PA_OCC_G(128, 8)
   PA_OCC_G(128, 16)
   PA_OCC_G(128, 32)
 #undef PA_OCC_G

@@ -77,6 +77,8 @@ struct PrefillArgs {
   int32_t max_tiles;
   float scale_log2;  // score scale * log2(e), times the K pool's scale (8-bit cache)
   float v_scale;     // the V pool's scale (8-bit cache), else 1
+  int32_t window;    // sliding window in tokens (0: none)
+  const float* alibi;  // ALiBi slope per query head, or NULL
 };
 
 // The tile map: tile t of the grid -> (sequence, tile of that sequence), each
@@ -125,7 +127,7 @@ __global__ void __launch_bounds__(1024) prefill_tiles_kernel(const int32_t* qs, 
   if (tid == 0) tiles[0] = min(running, max_tiles);
 }
 
-template <int ET, int BS, int G, bool OUT_F32>
+template <int ET, int BS, int G, bool OUT_F32, bool AL>
 __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
   constexpr int EB = ET == kFP8 ? 1 : 2;   // K/V element bytes
   constexpr int TT = kRows / G;            // tokens per tile
@@ -255,18 +257,35 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     for (int dt = 0; dt < 8; ++dt) acc[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const int min_pos = c + j0;
+  const int max_pos = kend - 1;
   const int ntiles = kend > 0 ? (kend + kKeys - 1) / kKeys : 0;
+  // Sliding window: a row at position p sees p-W+1 .. p, so the walk starts at
+  // the tile holding the earliest key any row of this tile sees.
+  const int W = a.window;
+  const int kt0 = W > 0 ? max(0, min_pos - W + 1) / kKeys : 0;
+  int lo_row[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) lo_row[rt] = W > 0 ? pos[rt] - W + 1 : INT32_MIN;
+  // ALiBi: slope * log2(e) of each row's query head (the scores are in log2 units)
+  float slope2[2] = {0.f, 0.f};
+  if constexpr (AL) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int row = wave * 32 + rt * 16 + r16;
+      slope2[rt] = a.alibi[g * G + row % G] * 1.4426950408889634f;
+    }
+  }
 
-  // prologue: tile 0 in LDS, tile 1 in flight, the table entry of tile 2 in flight
+  // prologue: tile kt0 in LDS, tile kt0+1 in flight, the table entry of kt0+2 in flight
   int next_phys = -1;
-  if (ntiles > 0) {
-    load_tile(0, 0, table_entry(0));
-    if (ntiles > 1) load_tile(1, kKeys, table_entry(kKeys));
-    if (ntiles > 2) next_phys = table_entry(2 * kKeys);
+  if (ntiles > kt0) {
+    load_tile(0, kt0 * kKeys, table_entry(kt0 * kKeys));
+    if (ntiles > kt0 + 1) load_tile(1, (kt0 + 1) * kKeys, table_entry((kt0 + 1) * kKeys));
+    if (ntiles > kt0 + 2) next_phys = table_entry((kt0 + 2) * kKeys);
     store_tile(0, 0);
   }
   __syncthreads();
-  // one key tile; BUF (= kt & 1) is a constant, so every register set is static
+  // one key tile; BUF (= (kt - kt0) & 1) is a constant, so every register set is static
   auto iteration = [&](int kt, auto buf_c) {
     constexpr int buf = decltype(buf_c)::value;
     const int k0 = kt * kKeys;
@@ -299,24 +318,40 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 
     // online softmax per row; the P^T operand in the k order
     // [4g .. 4g+3, 16+4g .. 16+4g+3].  Only tiles that reach past the tile's
-    // first position need the causal mask; the max is taken on raw scores
-    // (the scale is positive) and the scale enters with the exponent's fma.
+    // first position (or, with a window, start before its last row's window)
+    // need masks; without ALiBi the max is taken on raw scores (the scale is
+    // positive) and the scale enters with the exponent's fma.
+    const float sc = a.scale_log2;
+    if constexpr (AL) {
+      // scores to log2 units plus slope * (key - position)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const float sd = slope2[rt] * float(k0 + 4 * grp - pos[rt]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            s[rt][h][v] = fmaf(s[rt][h][v], sc, fmaf(slope2[rt], float(16 * h + v), sd));
+      }
+    }
     u32x4 pf[2];
-    if (k0 + kKeys - 1 > min_pos) {
+    if (k0 + kKeys - 1 > min_pos || (W > 0 && k0 < max_pos - W + 1)) {
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (k0 + 16 * h + 4 * grp + v > pos[rt]) s[rt][h][v] = kNegInf;
+          for (int v = 0; v < 4; ++v) {
+            const int k = k0 + 16 * h + 4 * grp + v;
+            if (k > pos[rt] || k < lo_row[rt]) s[rt][h][v] = kNegInf;
+          }
     }
-    const float sc = a.scale_log2;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       float mx = fmaxf(fmaxf(fmaxf(s[rt][0][0], s[rt][0][1]), fmaxf(s[rt][0][2], s[rt][0][3])),
                        fmaxf(fmaxf(s[rt][1][0], s[rt][1][1]), fmaxf(s[rt][1][2], s[rt][1][3])));
-      mx = xor_max<16>(mx) * sc;
+      mx = xor_max<16>(mx);
+      if constexpr (!AL) mx *= sc;
       // The exponent base moves only when the row maximum passes it by more
       // than 8 (log2 units): weights stay <= 2^8, the accumulators are
       // rescaled rarely, and the result is the same softmax.
@@ -329,8 +364,12 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const int h = w >> 1, v = 2 * (w & 1);
-        const f32x2 pp = {fast_exp2(fmaf(s[rt][h][v], sc, -base)),
-                          fast_exp2(fmaf(s[rt][h][v + 1], sc, -base))};
+        f32x2 pp;
+        if constexpr (AL)
+          pp = f32x2{fast_exp2(s[rt][h][v] - base), fast_exp2(s[rt][h][v + 1] - base)};
+        else
+          pp = f32x2{fast_exp2(fmaf(s[rt][h][v], sc, -base)),
+                     fast_exp2(fmaf(s[rt][h][v + 1], sc, -base))};
         const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
         pf[rt][w] = __builtin_bit_cast(uint32_t, pb);
         psum = __builtin_amdgcn_fdot2_f32_bf16(pb, kOnes, psum, false);  // adds the rounded pair
@@ -361,7 +400,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     if (kt + 1 < ntiles) store_tile(buf ^ 1, buf ^ 1);
     __syncthreads();
   };
-  for (int kt = 0; kt < ntiles; kt += 2) {
+  for (int kt = kt0; kt < ntiles; kt += 2) {
     iteration(kt, std::integral_constant<int, 0>{});
     if (kt + 1 < ntiles) iteration(kt + 1, std::integral_constant<int, 1>{});
   }
@@ -393,10 +432,15 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 template <int ET, int BS, int G>
 int launch_g(const PrefillArgs& a, bool out_f32, dim3 grid, hipStream_t stream) {
   const size_t lds = 2 * kBufBytes;
-  if (out_f32)
-    hipLaunchKernelGGL((prefill_kernel<ET, BS, G, true>), grid, dim3(256), lds, stream, a);
+  const bool al = a.alibi != nullptr;
+  if (out_f32 && al)
+    hipLaunchKernelGGL((prefill_kernel<ET, BS, G, true, true>), grid, dim3(256), lds, stream, a);
+  else if (out_f32)
+    hipLaunchKernelGGL((prefill_kernel<ET, BS, G, true, false>), grid, dim3(256), lds, stream, a);
+  else if (al)
+    hipLaunchKernelGGL((prefill_kernel<ET, BS, G, false, true>), grid, dim3(256), lds, stream, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<ET, BS, G, false>), grid, dim3(256), lds, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<ET, BS, G, false, false>), grid, dim3(256), lds, stream, a);
   return launch_result("pa_prefill");
 }
 
@@ -433,18 +477,23 @@ PA_API size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens, i
 PA_API int pa_prefill(const pa_cache* cache, const void* q, const int32_t* block_tables,
                       const int32_t* query_start, const int32_t* context_lens, int32_t num_seqs,
                       int32_t num_tokens, int32_t num_heads, int32_t max_blocks_per_seq,
-                      float scale, void* out, int32_t out_dtype, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      float scale, const pa_attn_variant* variant, void* out,
+                      int32_t out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   using namespace pa;
   if (int st = check_cache(cache, "pa_prefill")) return st;
+  const int32_t window = variant ? variant->sliding_window : 0;
+  const float* alibi = variant ? variant->alibi_slopes : nullptr;
+  if (window < 0) return fail(PA_ERR_SHAPE, "pa_prefill: sliding_window must be >= 0");
+  if (alibi && (reinterpret_cast<uintptr_t>(alibi) & 3u) != 0)
+    return fail(PA_ERR_SHAPE, "pa_prefill: alibi_slopes must be 4-byte aligned");
   if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || max_blocks_per_seq <= 0)
     return fail(PA_ERR_SHAPE, "pa_prefill: sizes must be non-negative (heads, table width positive)");
   if (cache->dtype != PA_BF16 && cache->dtype != PA_FP8_E4M3)
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill: bf16 and 8-bit caches only");
   if (cache->head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill: head_dim 128 only");
-  if (cache->block_size != 16 && cache->block_size != 32)
-    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: block_size 16 or 32 only");
+  if (cache->block_size != 8 && cache->block_size != 16 && cache->block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: block_size 8, 16 or 32 only");
   if (num_heads % cache->num_kv_heads != 0)
     return fail(PA_ERR_SHAPE, "pa_prefill: num_heads must be a multiple of num_kv_heads");
   const int32_t group = num_heads / cache->num_kv_heads;
@@ -498,11 +547,16 @@ PA_API int pa_prefill(const pa_cache* cache, const void* q, const int32_t* block
   const bool fp8 = cache->dtype == PA_FP8_E4M3;
   a.scale_log2 = scale * 1.4426950408889634f * (fp8 ? cache->k_scale : 1.0f);
   a.v_scale = fp8 ? cache->v_scale : 1.0f;
+  a.window = window;
+  a.alibi = alibi;
   const dim3 grid(unsigned(max_tiles), unsigned(cache->num_kv_heads));
   const bool f32 = out_dtype == PA_F32;
-  if (fp8)
-    return cache->block_size == 16 ? launch_bs<kFP8, 16>(a, group, f32, grid, s)
-                                   : launch_bs<kFP8, 32>(a, group, f32, grid, s);
-  return cache->block_size == 16 ? launch_bs<kBF16, 16>(a, group, f32, grid, s)
-                                 : launch_bs<kBF16, 32>(a, group, f32, grid, s);
+  switch (cache->block_size) {
+    case 8: return fp8 ? launch_bs<kFP8, 8>(a, group, f32, grid, s)
+                       : launch_bs<kBF16, 8>(a, group, f32, grid, s);
+    case 16: return fp8 ? launch_bs<kFP8, 16>(a, group, f32, grid, s)
+                        : launch_bs<kBF16, 16>(a, group, f32, grid, s);
+    default: return fp8 ? launch_bs<kFP8, 32>(a, group, f32, grid, s)
+                        : launch_bs<kBF16, 32>(a, group, f32, grid, s);
+  }
 }

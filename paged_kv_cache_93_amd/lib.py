@@ -51,6 +51,11 @@ class PaCache(ctypes.Structure):
                 ("v_scale", ctypes.c_float)]
 
 
+class PaAttnVariant(ctypes.Structure):
+    _fields_ = [("sliding_window", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("alibi_slopes", ctypes.c_void_p)]
+
+
 class PaBmConfig(ctypes.Structure):
     _fields_ = [("num_gpu_blocks", ctypes.c_int64), ("num_cpu_blocks", ctypes.c_int64),
                 ("block_size", ctypes.c_int32), ("prefix_caching", ctypes.c_int32),
@@ -106,7 +111,8 @@ _SIGNATURES = {
                                          _i32, _vp, _vp]),
     "pa_partials_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32]),
     "pa_prefill": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _vp, _vp, _vp, _i32, _i32, _i32,
-                                  _i32, _f32, _vp, _i32, _vp, ctypes.c_size_t, _vp]),
+                                  _i32, _f32, ctypes.POINTER(PaAttnVariant), _vp, _i32, _vp,
+                                  ctypes.c_size_t, _vp]),
     "pa_prefill_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32]),
     "pa_bm_create": (ctypes.c_int, [ctypes.POINTER(PaBmConfig), ctypes.POINTER(_vp)]),
     "pa_bm_destroy": (None, [_vp]),
@@ -344,8 +350,13 @@ def prefill_workspace(num_seqs: int, num_tokens: int, num_heads: int, num_kv_hea
 
 
 def pa_prefill(k_pool, v_pool, q, block_tables, query_start, context_lens, scale: float, out,
-               workspace=None, stream=None, k_scale: float = 1.0, v_scale: float = 1.0) -> None:
-    """Causal attention of a flattened mixed batch (see include/pagedattn.h)."""
+               workspace=None, stream=None, k_scale: float = 1.0, v_scale: float = 1.0,
+               window: int = 0, alibi_slopes=None) -> None:
+    """Causal attention of a flattened mixed batch (see include/pagedattn.h).
+
+    ``window`` > 0 restricts each query to its last ``window`` positions;
+    ``alibi_slopes`` (device float32 [num_heads]) adds slope * (t - p) to scores.
+    """
     cache = make_cache(k_pool, v_pool, k_scale, v_scale)
     num_tokens, num_heads = q.shape[0], q.shape[1]
     num_seqs = context_lens.shape[0]
@@ -360,9 +371,17 @@ def pa_prefill(k_pool, v_pool, q, block_tables, query_start, context_lens, scale
     if workspace is None:
         workspace = prefill_workspace(num_seqs, num_tokens, num_heads, k_pool.shape[1],
                                       device=q.device)
+    variant = None
+    if window or alibi_slopes is not None:
+        if alibi_slopes is not None:
+            _require(alibi_slopes.dtype == torch.float32 and alibi_slopes.is_contiguous() and
+                     alibi_slopes.numel() == num_heads and alibi_slopes.device.type != "cpu",
+                     "alibi_slopes must be a contiguous device float32 [num_heads]")
+        variant = ctypes.byref(PaAttnVariant(int(window), 0, _ptr(alibi_slopes)))
     _check(load().pa_prefill(ctypes.byref(cache), _ptr(q), _ptr(block_tables), _ptr(query_start),
                              _ptr(context_lens), num_seqs, num_tokens, num_heads,
-                             block_tables.shape[1], float(scale), _ptr(out), _dtype_code(out),
+                             block_tables.shape[1], float(scale), variant, _ptr(out),
+                             _dtype_code(out),
                              _ptr(workspace), workspace.numel() * workspace.element_size(),
                              _stream(stream)))
 

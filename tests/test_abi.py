@@ -93,7 +93,7 @@ def _partitions(cache, **kw):
     (dict(dtype=7), {}, 3),
     (dict(num_blocks=0), {}, 2),
     (dict(head_dim=96), {}, 3),
-    (dict(block_size=8), {}, 3),
+    (dict(block_size=4), {}, 3),
     (dict(k_pool=8), {}, 2),                       # misaligned pool
     ({}, dict(num_heads=3), 2),                    # not a multiple of num_kv_heads
     ({}, dict(num_heads=32), 3),                   # 16 query heads per KV head
@@ -222,13 +222,13 @@ def test_prefill_rejects_bad_arguments():
     c = _cache(dtype=lib.PA_BF16, head_dim=128, block_size=16, num_kv_heads=2)
 
     def pf(cache=c, S=2, T=10, H=8, W=4, scale=0.1, od=lib.PA_F32, ws=256, wsb=4096, q=16,
-           out=16):
+           out=16, variant=None):
         return call("pa_prefill", ctypes.byref(cache) if cache is not None else None, q, 16, 16,
-                    16, S, T, H, W, scale, out, od, ws, wsb, None)
+                    16, S, T, H, W, scale, variant, out, od, ws, wsb, None)
     assert pf(cache=None) == 1
     assert pf(cache=_cache(dtype=lib.PA_F32, head_dim=128, block_size=16, num_kv_heads=2)) == 3
     assert pf(cache=_cache(dtype=lib.PA_BF16, head_dim=64, block_size=16, num_kv_heads=2)) == 3
-    assert pf(cache=_cache(dtype=lib.PA_BF16, head_dim=128, block_size=8, num_kv_heads=2)) == 3
+    assert pf(cache=_cache(dtype=lib.PA_BF16, head_dim=128, block_size=4, num_kv_heads=2)) == 3
     assert pf(H=6) == 3          # ratio 3
     assert pf(H=7) == 2          # not a multiple
     assert pf(scale=0.0) == 2
@@ -240,3 +240,9 @@ def test_prefill_rejects_bad_arguments():
     assert pf(wsb=8) == 4
     assert pf(ws=16) == 2        # not 256-byte aligned
     assert pf(W=0) == 2
+    assert pf(variant=ctypes.byref(lib.PaAttnVariant(-1, 0, None))) == 2     # negative window
+    assert pf(variant=ctypes.byref(lib.PaAttnVariant(4, 0, 18))) == 2        # misaligned slopes
+
+
+def test_variant_struct_layout():
+    assert ctypes.sizeof(lib.PaAttnVariant) == 16 and lib.PaAttnVariant.alibi_slopes.offset == 8

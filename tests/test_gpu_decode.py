@@ -99,7 +99,7 @@ RAGGED = [1, 2, 15, 16, 17, 31, 32, 33, 64, 100, 257, 515]
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("bs", [8, 16, 32])
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
 def test_ragged_shapes(dtype, d, bs, group):
     w = W.small_random(7 + d + bs + group, dtype=dtype, num_seqs=len(RAGGED),
@@ -250,6 +250,20 @@ def test_shared_prefix_gives_the_bits_of_private_copies():
     private, _ = run_decode(t2, w, "balanced")
     torch.cuda.synchronize()
     assert torch.equal(shared.view(torch.int16), private.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_named_workload_at_block_size_8(dtype):
+    """The 8B batch re-drawn with 8-token blocks, every output element, every mode."""
+    w, _, ref = named(2, dtype, block_size=8)
+    t = upload(w)
+    run_writes(t)
+    for mode in ("balanced", "single", 512):
+        out, _ = run_decode(t, w, mode, out_f32=True)
+        torch.cuda.synchronize()
+        err = max_abs_err(out, ref)
+        print(f"{w.name} B=8 {dtype} mode={mode}: max abs err {err:.3g}")
+        assert err <= TOL["f32"], mode
 
 
 def test_block_size_16_and_32_agree():

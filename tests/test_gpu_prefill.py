@@ -58,7 +58,7 @@ MIX = ([40, 300, 17, 1, 33, 129, 64, 5],
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("bs", [8, 16, 32])
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (8, 2), (16, 2)])
 def test_prefill_matches_the_oracle(dtype, bs, hq, hkv):
     w = W.prefill_batch("mix", 500 + hq + hkv + bs, *MIX, num_heads=hq, num_kv_heads=hkv,
@@ -73,7 +73,7 @@ def test_prefill_matches_the_oracle(dtype, bs, hq, hkv):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-@pytest.mark.parametrize("bs,hq,hkv", [(16, 8, 2), (32, 16, 2), (16, 8, 8)])
+@pytest.mark.parametrize("bs,hq,hkv", [(16, 8, 2), (32, 16, 2), (16, 8, 8), (8, 8, 2)])
 def test_zero_query_gives_the_exact_mean_of_visible_rows(dtype, bs, hq, hkv):
     w = W.prefill_batch("zeroq", 600 + bs + hq, *MIX, num_heads=hq, num_kv_heads=hkv,
                         block_size=bs, dtype=dtype, zero_query=True)
@@ -122,3 +122,71 @@ def test_named_workloads_on_sampled_rows(name):
                                 k_scale=w.k_scale, v_scale=w.v_scale)
             worst = max(worst, float(np.abs(got[row] - ref[0]).max()))
     assert worst <= 2e-2, worst
+
+
+# ---------------------------------------------------------------------------
+# attention variants: sliding window and ALiBi
+# ---------------------------------------------------------------------------
+
+def run_variant(w, window=0, slopes=None, out_f32=True):
+    t = upload(w)
+    out = torch.empty((w.num_tokens, w.num_heads, w.head_dim), device="cuda",
+                      dtype=torch.float32 if out_f32 else torch.bfloat16)
+    sl = None if slopes is None else torch.tensor(np.asarray(slopes, np.float32)).cuda()
+    print(f"prefill variant {w.name} {w.dtype} B={w.block_size} W={window} "
+          f"alibi={slopes is not None}", flush=True)
+    lib.pa_prefill(t["k"], t["v"], t["q"], t["tables"], t["qs"], t["lens"],
+                   1.0 / math.sqrt(w.head_dim), out, k_scale=w.k_scale, v_scale=w.v_scale,
+                   window=window, alibi_slopes=sl)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def variant_reference(w, window=0, slopes=None):
+    # the kernel computes with float32 slopes: the oracle takes the same values
+    sl = None if slopes is None else np.asarray(slopes, np.float32).astype(np.float64)
+    return oracle.prefill(w.q, w.k_pool, w.v_pool, w.block_tables, w.query_start,
+                          w.context_lens, 1.0 / math.sqrt(w.head_dim), w.dtype,
+                          k_scale=w.k_scale, v_scale=w.v_scale, window=window, alibi_slopes=sl)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("bs,hq,hkv", [(16, 8, 2), (32, 8, 4), (8, 16, 2)])
+@pytest.mark.parametrize("window", [1, 7, 33, 100])
+def test_sliding_window_matches_the_oracle(dtype, bs, hq, hkv, window):
+    w = W.prefill_batch("mix", 700 + bs + hq, *MIX, num_heads=hq, num_kv_heads=hkv,
+                        block_size=bs, dtype=dtype)
+    got = run_variant(w, window=window)
+    assert np.abs(got - variant_reference(w, window=window)).max() <= 2e-2
+
+
+@pytest.mark.parametrize("window", [1, 5, 32, 33, 64])
+def test_sliding_window_zero_query_is_the_exact_window_mean(window):
+    w = W.prefill_batch("zeroq", 11, *MIX, num_heads=8, num_kv_heads=2, block_size=16,
+                        zero_query=True)
+    got = run_variant(w, window=window)
+    assert np.abs(got - variant_reference(w, window=window)).max() <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 2), (8, 8)])
+def test_alibi_matches_the_oracle(dtype, hq, hkv):
+    w = W.prefill_batch("mix", 900 + hq, *MIX, num_heads=hq, num_kv_heads=hkv, dtype=dtype)
+    for slopes in (oracle.alibi_slopes(hq), np.random.default_rng(hq).uniform(0, 0.3, hq)):
+        for out_f32 in (True, False):
+            got = run_variant(w, slopes=slopes, out_f32=out_f32)
+            assert np.abs(got - variant_reference(w, slopes=slopes)).max() <= 2e-2
+        both = run_variant(w, window=20, slopes=slopes)
+        assert np.abs(both - variant_reference(w, window=20, slopes=slopes)).max() <= 2e-2
+
+
+def test_decode_rows_with_variants_match_the_decode_oracle():
+    """A decode batch (n_i = 1) with a window and ALiBi, through pa_prefill."""
+    lens = [1, 16, 17, 300, 1025, 4096]
+    w = W.prefill_batch("decode", 21, lens, [1] * len(lens), num_heads=32, num_kv_heads=8)
+    slopes = oracle.alibi_slopes(32)
+    got = run_variant(w, window=256, slopes=slopes)
+    ref = oracle.decode(w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens,
+                        1.0 / math.sqrt(128), "bf16", window=256,
+                        alibi_slopes=np.asarray(slopes, np.float32).astype(np.float64))
+    assert np.abs(got - ref).max() <= 2e-2
