@@ -297,9 +297,15 @@ def bench_prefill(args) -> dict:
         ws = lib.prefill_workspace(w.num_seqs, w.num_tokens, w.num_heads, w.num_kv_heads)
         scale = 1.0 / math.sqrt(w.head_dim)
 
+        slopes = None
+        if args.alibi:
+            h = np.arange(1, w.num_heads + 1, dtype=np.float64)
+            slopes = torch.tensor(2.0 ** (-8.0 * h / w.num_heads), dtype=torch.float32).cuda()
+
         def call():
             lib.pa_prefill(k, v, q, tables, qs, lens, scale, out, workspace=ws,
-                           k_scale=w.k_scale, v_scale=w.v_scale)
+                           k_scale=w.k_scale, v_scale=w.v_scale, window=args.window,
+                           alibi_slopes=slopes)
 
         for _ in range(args.warmup):
             call()
@@ -311,8 +317,9 @@ def bench_prefill(args) -> dict:
         b.record()
         torch.cuda.synchronize()
         us = a.elapsed_time(b) / args.steps * 1e3
-        tflops = w.flops() / (us * 1e-6) / 1e12
-        rows[name] = dict(us=round(us, 1), gflop=round(w.flops() / 1e9, 2),
+        flops = w.flops(args.window)
+        tflops = flops / (us * 1e-6) / 1e12
+        rows[name] = dict(us=round(us, 1), gflop=round(flops / 1e9, 2),
                           tflops=round(tflops, 1), frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                           seqs=w.num_seqs, tokens=w.num_tokens)
         print(f"# prefill {name}: {us:.1f} us, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
@@ -324,7 +331,8 @@ def bench_prefill(args) -> dict:
         "data": "synthetic",
         "config": {"workload": "cached_preamble: 16 x (304 new tokens over a 1,200-token "
                                "context), 32 query / 8 KV heads, head_dim 128",
-                   "block_size": args.block_size or 16},
+                   "block_size": args.block_size or 16, "sliding_window": args.window,
+                   "alibi": bool(args.alibi)},
         "workloads": rows,
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": head["tflops"],
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": head["frac"],
@@ -486,6 +494,8 @@ def main() -> int:
                     help="decode: the decode step (default); swap: block swaps to pinned host "
                          "memory; scheduler: the host block manager (no GPU needed)")
     ap.add_argument("--swap-blocks", type=int, default=1024, help="blocks per swap launch")
+    ap.add_argument("--window", type=int, default=0, help="prefill: sliding window (0: none)")
+    ap.add_argument("--alibi", action="store_true", help="prefill: ALiBi with the paper's slopes")
     args = ap.parse_args()
 
     if args.part == "scheduler":

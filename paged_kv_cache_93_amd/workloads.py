@@ -631,13 +631,16 @@ class PrefillWorkload:
     def num_tokens(self) -> int:
         return int(self.query_start[-1])
 
-    def flops(self) -> int:
-        """Algorithmic flops: 4 * head_dim per (query row, head, visible key)."""
+    def flops(self, window: int = 0) -> int:
+        """Algorithmic flops: 4 * head_dim per (query row, head, visible key);
+        a query at position p sees p + 1 keys, or min(p + 1, window) with a window."""
         total = 0
         for i in range(self.num_seqs):
             n, L = int(self.query_start[i + 1] - self.query_start[i]), int(self.context_lens[i])
-            first = L - n + 1                       # keys seen by the first query token
-            total += (first + L) * n // 2 if n else 0
+            seen = np.arange(L - n + 1, L + 1, dtype=np.int64)   # keys seen by each query token
+            if window:
+                seen = np.minimum(seen, window)
+            total += int(seen.sum())
         return 4 * self.head_dim * self.num_heads * total
 
 
