@@ -12,7 +12,9 @@ pools and both host pools bit-identical to the numpy ones.
 
 The KV rows of a token are drawn from a seed that names the token's whole
 prefix, as a model's would depend on it; a recomputed token therefore gets
-the same rows again.
+the same rows again.  For bf16 and 8-bit caches every scheduled token (prompt
+slices and decodes alike) also gets its causal attention from pa_prefill over
+the same plan, against the oracle's, within the bf16-weight bound (2e-2).
 """
 
 import math
@@ -70,7 +72,8 @@ def test_engine_loop_matches_the_oracle(dtype, mode):
     thk, thv = pinned_like(hk, dtype), pinned_like(hv, dtype)
     ids = PrefixIds()
     rng = np.random.default_rng(seed)
-    state = dict(kp=kp, vp=vp, hk=hk, hv=hv, steps=0, preempt=0, swaps=0, cow=0, worst=0.0)
+    state = dict(kp=kp, vp=vp, hk=hk, hv=hv, steps=0, preempt=0, swaps=0, cow=0, worst=0.0,
+                 worst_prefill=0.0, prompt_rows=0)
 
     def step(plans):
         po, pn = plans
@@ -84,6 +87,7 @@ def test_engine_loop_matches_the_oracle(dtype, mode):
                                                          po.context_lens[k])]
         k_new, v_new = rows_for(idents, seed, dtype)
         q = W.draw_values(rng, (S, HQ, D), qdt)
+        q_all = W.draw_values(rng, (len(idents), HQ, D), qdt)   # every scheduled token
         print(f"engine {dtype}/{mode} step {state['steps']}: {S} seqs, {len(idents)} tokens, "
               f"{len(po.swap_out)}/{len(po.swap_in)} swaps, {len(po.cow_pairs)} copies", flush=True)
         # device, from the native plan
@@ -103,6 +107,11 @@ def test_engine_loop_matches_the_oracle(dtype, mode):
             lib.pa_decode(dk, dv, to_device(q, qdt), dev(pn.block_tables), dev(pn.context_lens),
                           1.0 / math.sqrt(D), out, workspace=lib.decode_workspace(S, HQ, D),
                           k_scale=k_scale, v_scale=v_scale)
+            if dtype != "f32":
+                out_all = torch.empty((len(idents), HQ, D), dtype=torch.float32, device="cuda")
+                lib.pa_prefill(dk, dv, to_device(q_all, qdt), dev(pn.block_tables),
+                               dev(pn.query_start), dev(pn.context_lens), 1.0 / math.sqrt(D),
+                               out_all, k_scale=k_scale, v_scale=v_scale)
         # numpy, from the oracle plan
         state["hk"] = swap_blocks(state["hk"], state["kp"], po.swap_out)
         state["hv"] = swap_blocks(state["hv"], state["vp"], po.swap_out)
@@ -121,6 +130,15 @@ def test_engine_loop_matches_the_oracle(dtype, mode):
             err = float(np.abs(got - ref).max())
             assert err <= 1e-5, f"step {state['steps']}: max abs error {err}"
             state["worst"] = max(state["worst"], err)
+            if dtype != "f32":
+                ref_all = oracle.prefill(q_all, state["kp"], state["vp"], tables,
+                                         np.array(po.query_start, np.int32),
+                                         np.array(po.context_lens, np.int32), 1.0 / math.sqrt(D),
+                                         dtype, k_scale=k_scale, v_scale=v_scale)
+                err_all = float(np.abs(out_all.cpu().numpy().astype(np.float64) - ref_all).max())
+                assert err_all <= 2e-2, f"step {state['steps']}: prefill max abs error {err_all}"
+                state["worst_prefill"] = max(state["worst_prefill"], err_all)
+                state["prompt_rows"] += len(idents) - S
         state["steps"] += 1
         state["preempt"] += len(po.preempted)
         state["swaps"] += len(po.swap_out) + len(po.swap_in)
@@ -136,4 +154,7 @@ def test_engine_loop_matches_the_oracle(dtype, mode):
     assert state["preempt"] > 0 and state["cow"] > 0
     if mode == "swap":
         assert state["swaps"] > 0
-    print(f"engine {dtype}/{mode}: worst abs error {state['worst']:.2e}", flush=True)
+    if dtype != "f32":
+        assert state["prompt_rows"] > 0      # prompt slices went through pa_prefill
+    print(f"engine {dtype}/{mode}: worst abs error {state['worst']:.2e} (decode), "
+          f"{state['worst_prefill']:.2e} (prefill)", flush=True)
