@@ -60,13 +60,26 @@ def to_device(arr, dtype):
     return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
 
 
-def algorithmic_bytes(w: W.Workload) -> dict:
-    """Bytes the decode step must move, per component."""
+def paper_alibi_slopes(num_heads: int) -> torch.Tensor:
+    """ALiBi's geometric slopes 2^(-8h/H), h = 1..H (Press, Smith and Lewis), on
+    the device as float32."""
+    h = np.arange(1, num_heads + 1, dtype=np.float64)
+    return torch.tensor(2.0 ** (-8.0 * h / num_heads), dtype=torch.float32).cuda()
+
+
+def algorithmic_bytes(w: W.Workload, window: int = 0) -> dict:
+    """Bytes the decode step must move, per component (a sliding window reads
+    only its last ``window`` positions and the table entries of their blocks)."""
     e = W.element_bytes(w.dtype)                    # cache element
     eq = W.element_bytes(W.query_dtype(w.dtype))    # q, new tokens and output
-    table_entries = sum(W.blocks_for(int(n), w.block_size) for n in w.context_lens)
+
+    def entries(n):
+        first = (n - window) // w.block_size if 0 < window < n else 0
+        return W.blocks_for(n, w.block_size) - first
+
+    table_entries = sum(entries(int(n)) for n in w.context_lens)
     return dict(
-        kv=w.kv_bytes(),
+        kv=w.kv_bytes(window),
         q=w.num_seqs * w.num_heads * w.head_dim * eq,
         out=w.num_seqs * w.num_heads * w.head_dim * eq,
         tables=4 * table_entries,
@@ -75,8 +88,9 @@ def algorithmic_bytes(w: W.Workload) -> dict:
     )
 
 
-def cpu_baseline(w: W.Workload, budget_s: float) -> dict:
-    """The float64 oracle's decode on a bounded sample of the same workload."""
+def cpu_baseline(w: W.Workload, budget_s: float, window: int = 0, alibi: bool = False) -> dict:
+    """The float64 oracle's decode on a bounded sample of the same workload
+    (with the same attention variant)."""
     import oracle
 
     try:
@@ -88,14 +102,19 @@ def cpu_baseline(w: W.Workload, budget_s: float) -> dict:
     kp, vp = oracle.kv_append(kp, vp, w.k_new, w.v_new, w.slot_mapping,
                               fp8_scales=(w.k_scale, w.v_scale) if w.dtype == "fp8" else None)
     scale = 1.0 / math.sqrt(w.head_dim)
+    slopes = None
+    if alibi:
+        slopes = paper_alibi_slopes(w.num_heads).cpu().numpy().astype(np.float64)
     done = 0
     kv = 0
     t0 = time.perf_counter()
     while done < w.num_seqs and time.perf_counter() - t0 < budget_s:
         sl = slice(done, done + 1)
         oracle.decode(w.q[sl], kp, vp, w.block_tables[sl], w.context_lens[sl], scale, w.dtype,
-                      k_scale=w.k_scale, v_scale=w.v_scale)
-        kv += int(w.context_lens[done]) * w.num_kv_heads * w.head_dim * 2 * W.element_bytes(w.dtype)
+                      k_scale=w.k_scale, v_scale=w.v_scale, window=window, alibi_slopes=slopes)
+        n = int(w.context_lens[done])
+        n = min(n, window) if window > 0 else n
+        kv += n * w.num_kv_heads * w.head_dim * 2 * W.element_bytes(w.dtype)
         done += 1
     dt = time.perf_counter() - t0
     return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
@@ -297,10 +316,7 @@ def bench_prefill(args) -> dict:
         ws = lib.prefill_workspace(w.num_seqs, w.num_tokens, w.num_heads, w.num_kv_heads)
         scale = 1.0 / math.sqrt(w.head_dim)
 
-        slopes = None
-        if args.alibi:
-            h = np.arange(1, w.num_heads + 1, dtype=np.float64)
-            slopes = torch.tensor(2.0 ** (-8.0 * h / w.num_heads), dtype=torch.float32).cuda()
+        slopes = paper_alibi_slopes(w.num_heads) if args.alibi else None
 
         def call():
             lib.pa_prefill(k, v, q, tables, qs, lens, scale, out, workspace=ws,
@@ -494,8 +510,10 @@ def main() -> int:
                     help="decode: the decode step (default); swap: block swaps to pinned host "
                          "memory; scheduler: the host block manager (no GPU needed)")
     ap.add_argument("--swap-blocks", type=int, default=1024, help="blocks per swap launch")
-    ap.add_argument("--window", type=int, default=0, help="prefill: sliding window (0: none)")
-    ap.add_argument("--alibi", action="store_true", help="prefill: ALiBi with the paper's slopes")
+    ap.add_argument("--window", type=int, default=0,
+                    help="decode and prefill: sliding window in tokens (0: none)")
+    ap.add_argument("--alibi", action="store_true",
+                    help="decode and prefill: ALiBi with the paper's slopes")
     args = ap.parse_args()
 
     if args.part == "scheduler":
@@ -527,7 +545,11 @@ def main() -> int:
     sc = dict(k_scale=w.k_scale, v_scale=w.v_scale)
     mode = args.mode if args.mode in ("balanced", "single") else int(args.mode)
     scale = 1.0 / math.sqrt(w.head_dim)
-    nbytes = algorithmic_bytes(w)
+    variant = bool(args.window or args.alibi)
+    if variant and isinstance(mode, int):
+        print(json.dumps({"error": "split-KV partitions take no attention variant"}), flush=True)
+        return 2
+    nbytes = algorithmic_bytes(w, args.window)
     print(f"# workload {w.name}: {w.num_seqs} seqs, KV {nbytes['kv'] / 1e6:.1f} MB, "
           f"pool {w.num_blocks} blocks, mode {mode}", file=sys.stderr, flush=True)
 
@@ -537,6 +559,9 @@ def main() -> int:
                   slots=torch.from_numpy(w.slot_mapping).cuda(),
                   pairs=torch.from_numpy(w.copy_pairs).cuda(),
                   k_new=to_device(w.k_new, qdt), v_new=to_device(w.v_new, qdt))
+    var = dict(window=args.window)
+    if args.alibi:
+        var["alibi_slopes"] = paper_alibi_slopes(w.num_heads)
     pools = []
     k0, v0 = to_device(w.k_pool, w.dtype), to_device(w.v_pool, w.dtype)
     for r in range(args.rotate):
@@ -560,7 +585,7 @@ def main() -> int:
             lib.pa_splitkv_reduce(po, pm, ps, shared["lens"], psize, out)
         else:
             lib.pa_decode(kp, vp, shared["q"], shared["tables"], shared["lens"], scale, out,
-                          workspace=ws, **sc)
+                          workspace=ws, **sc, **var)
 
     def step(r):
         kp, vp = pools[r]
@@ -631,7 +656,8 @@ def main() -> int:
                    "block_size": w.block_size, "decode_mode": str(mode),
                    "context_lens": f"{int(w.context_lens.min())}..{int(w.context_lens.max())}, "
                                    f"mean {float(w.context_lens.mean()):.0f}",
-                   "seed": w.seed, "rotating_caches": args.rotate},
+                   "seed": w.seed, "rotating_caches": args.rotate,
+                   "sliding_window": args.window, "alibi": bool(args.alibi)},
         "seqs_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "hbm_peak_frac_step": round(kv_gbps_step / HBM_PEAK_GBPS, 4),
         "kv_bytes": nbytes["kv"],
@@ -640,11 +666,11 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": kernels, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": read_traffic(w.name, str(mode)),
+                     "traffic": None if variant else read_traffic(w.name, str(mode)),
                      "algorithmic_bytes_per_launch": decode_bytes},
     }
     if args.cpu_budget > 0:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, args.window, args.alibi)
     print(json.dumps(result), flush=True)
     return 0
 

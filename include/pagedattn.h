@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 5
+#define PA_ABI_VERSION 6
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -163,50 +163,6 @@ int pa_swap_blocks(const pa_cache *cache, void *host_k_pool, void *host_v_pool,
                    int32_t direction, void *stream);
 
 /*
- * pa_decode - attention of one query token per sequence over its paged cache.
- *
- * For sequence i, query head h and its KV head g = h / (num_heads/num_kv_heads):
- *     s_t = scale * q[i][h] . K_t      for t < L_i = context_lens[i]
- *     out[i][h] = sum_t softmax(s)_t * V_t
- * with K_t, V_t the rows of logical token t, found through block_tables[i]
- * ("Paged Attention as a Memory Manager", section "How the Kernel Executes
- * Paged Attention": one table read per block, keys loaded per block, scores
- * q.k/sqrt(d_k), padding masked, softmax-weighted value sum; "PagedAttention
- * and continuous batching", section "Attention kernel modification": blocks
- * accumulated with a running softmax).  L_i includes the token appended this
- * step.  Rows at positions >= L_i never affect the result, whatever they hold;
- * L_i = 0 gives a zero output.
- *
- * With a workspace, the (sequence, block) pairs of the whole batch are split
- * evenly over a fixed grid of workgroups, so long and short sequences finish
- * together; the parts of a sequence split between workgroups are merged with
- * the log-sum-exp rule by a second kernel enqueued on the same stream.
- * Without one (workspace = NULL), one workgroup walks each sequence.
- *
- *   q             DEVICE [num_seqs][num_heads][head_dim], cache->dtype (bfloat16
- *                 for an 8-bit cache, whose K/V values are codes times scales)
- *   block_tables  DEVICE int32 [num_seqs][max_blocks_per_seq]; entries past
- *                 ceil(L_i / block_size) are not read
- *   context_lens  DEVICE int32 [num_seqs], 0 <= L_i <= max_blocks_per_seq*block_size
- *   num_heads     multiple of num_kv_heads; ratio 1, 2, 4 or 8
- *   scale         > 0 and finite (normally 1/sqrt(head_dim))
- *   out           DEVICE [num_seqs][num_heads][head_dim] of out_dtype, 16-byte aligned
- *   out_dtype     PA_F32, or PA_BF16 for a bf16 or 8-bit cache
- *   workspace     DEVICE scratch of workspace_bytes >= pa_decode_workspace_bytes(),
- *                 256-byte aligned, or NULL; its contents need no initialising
- *                 and are meaningless afterwards.  Calls in flight at the same
- *                 time must not share one.
- */
-int pa_decode(const pa_cache *cache, const void *q, const int32_t *block_tables,
-              const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
-              int32_t max_blocks_per_seq, float scale, void *out, int32_t out_dtype,
-              void *workspace, size_t workspace_bytes, void *stream);
-
-/* Workspace bytes pa_decode needs on the current device for these sizes
- * (0 for a negative or zero size). */
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim);
-
-/*
  * Attention variants.  The pages name sliding windows and ALiBi as variants a
  * paged kernel has to re-derive its block traversal for ("Paged Attention as
  * a Memory Manager", section "When It Falls Down"); their definitions are the
@@ -222,6 +178,56 @@ typedef struct pa_attn_variant {
   int32_t reserved;             /* 0 */
   const float *alibi_slopes;
 } pa_attn_variant;
+
+/*
+ * pa_decode - attention of one query token per sequence over its paged cache.
+ *
+ * For sequence i, query head h and its KV head g = h / (num_heads/num_kv_heads):
+ *     s_t = scale * q[i][h] . K_t      for t < L_i = context_lens[i]
+ *     out[i][h] = sum_t softmax(s)_t * V_t
+ * with K_t, V_t the rows of logical token t, found through block_tables[i]
+ * ("Paged Attention as a Memory Manager", section "How the Kernel Executes
+ * Paged Attention": one table read per block, keys loaded per block, scores
+ * q.k/sqrt(d_k), padding masked, softmax-weighted value sum; "PagedAttention
+ * and continuous batching", section "Attention kernel modification": blocks
+ * accumulated with a running softmax).  L_i includes the token appended this
+ * step.  Rows at positions >= L_i (or before a sliding window) never affect
+ * the result, whatever they hold; L_i = 0 gives a zero output.
+ *
+ * With a workspace, the (sequence, block) pairs of the whole batch are split
+ * evenly over a fixed grid of workgroups, so long and short sequences finish
+ * together; the parts of a sequence split between workgroups are merged with
+ * the log-sum-exp rule by a second kernel enqueued on the same stream.
+ * Without one (workspace = NULL), one workgroup walks each sequence.
+ *
+ *   q             DEVICE [num_seqs][num_heads][head_dim], cache->dtype (bfloat16
+ *                 for an 8-bit cache, whose K/V values are codes times scales)
+ *   block_tables  DEVICE int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                 ceil(L_i / block_size) are not read
+ *   context_lens  DEVICE int32 [num_seqs], 0 <= L_i <= max_blocks_per_seq*block_size
+ *   num_heads     multiple of num_kv_heads; ratio 1, 2, 4 or 8
+ *   scale         > 0 and finite (normally 1/sqrt(head_dim))
+ *   variant       HOST pa_attn_variant, or NULL for plain attention.  The query
+ *                 sits at position p = L_i - 1: a window W keeps t >= L_i - W
+ *                 (blocks wholly before it are neither read nor counted in the
+ *                 split), and ALiBi adds slope[h] * (t - p) to s_t.
+ *                 sliding_window < 0 or misaligned slopes give PA_ERR_SHAPE.
+ *   out           DEVICE [num_seqs][num_heads][head_dim] of out_dtype, 16-byte aligned
+ *   out_dtype     PA_F32, or PA_BF16 for a bf16 or 8-bit cache
+ *   workspace     DEVICE scratch of workspace_bytes >= pa_decode_workspace_bytes(),
+ *                 256-byte aligned, or NULL; its contents need no initialising
+ *                 and are meaningless afterwards.  Calls in flight at the same
+ *                 time must not share one.
+ */
+int pa_decode(const pa_cache *cache, const void *q, const int32_t *block_tables,
+              const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+              int32_t max_blocks_per_seq, float scale, const pa_attn_variant *variant,
+              void *out, int32_t out_dtype, void *workspace, size_t workspace_bytes,
+              void *stream);
+
+/* Workspace bytes pa_decode needs on the current device for these sizes
+ * (0 for a negative or zero size). */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim);
 
 /*
  * pa_prefill - causal attention of a mixed batch: many query tokens per
@@ -255,7 +261,7 @@ typedef struct pa_attn_variant {
  *                 contents need no initialising.  Calls in flight at the same time
  *                 must not share one.
  * Supported: bf16 and 8-bit (E4M3) caches, head_dim 128, block_size 8, 16 or 32.
- * With a variant, decode rows (n_i = 1) go through here too.
+ * Decode rows (n_i = 1) are computed like the others, with or without a variant.
  */
 int pa_prefill(const pa_cache *cache, const void *q, const int32_t *block_tables,
                const int32_t *query_start, const int32_t *context_lens, int32_t num_seqs,

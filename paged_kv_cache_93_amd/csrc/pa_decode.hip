@@ -111,6 +111,8 @@ int prepare(const char* fn, const pa_cache* cache, const void* q, const int32_t*
   const bool fp8 = cache->dtype == PA_FP8_E4M3;
   a->scale_log2 = scale * 1.4426950408889634f * (fp8 ? cache->k_scale : 1.f);
   a->v_scale = fp8 ? cache->v_scale : 1.f;
+  a->window = 0;
+  a->alibi = nullptr;
   return PA_OK;
 }
 
@@ -138,8 +140,9 @@ PA_API size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int
 
 PA_API int pa_decode(const pa_cache* cache, const void* q, const int32_t* block_tables,
                      const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
-                     int32_t max_blocks_per_seq, float scale, void* out, int32_t out_dtype,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     int32_t max_blocks_per_seq, float scale, const pa_attn_variant* variant,
+                     void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   using namespace pa;
   const char* fn = "pa_decode";
   DecodeArgs a;
@@ -147,6 +150,14 @@ PA_API int pa_decode(const pa_cache* cache, const void* q, const int32_t* block_
   if (int st = prepare(fn, cache, q, block_tables, context_lens, num_seqs, num_heads,
                        max_blocks_per_seq, scale, &a, &group))
     return st;
+  if (variant) {
+    if (variant->sliding_window < 0)
+      return fail(PA_ERR_SHAPE, "%s: sliding_window must be >= 0", fn);
+    if (variant->alibi_slopes && (reinterpret_cast<uintptr_t>(variant->alibi_slopes) & 3u) != 0)
+      return fail(PA_ERR_SHAPE, "%s: alibi_slopes must be 4-byte aligned", fn);
+    a.window = variant->sliding_window;
+    a.alibi = variant->alibi_slopes;
+  }
   if (!out) return fail(PA_ERR_NULL, "%s: out is NULL", fn);
   if (out_dtype != PA_F32 && !(out_dtype == PA_BF16 && cache->dtype != PA_F32))
     return fail(PA_ERR_UNSUPPORTED,

@@ -75,6 +75,8 @@ struct DecodeArgs {
   int32_t out_f32;           // 1: binary32 output; 0: bf16 output (bf16 or 8-bit cache)
   float scale_log2;          // score scale * log2(e), times the K pool's scale (8-bit cache)
   float v_scale;             // the V pool's scale (8-bit cache), else 1
+  int32_t window;            // sliding window in tokens (0: none): attend to L-W .. L-1
+  const float* alibi;        // ALiBi slope per query head, or NULL
 };
 
 namespace dev {
@@ -260,6 +262,12 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// First block of a sequence of `len` tokens that a window of W tokens (W > 0)
+// reaches: its units are blocks first .. ceil(len / bs) - 1.
+__device__ __forceinline__ int window_first_block(int len, int window, int bs) {
+  return window > 0 && len > window ? (len - window) / bs : 0;
+}
+
 // Workgroup that processes unit u when `total` units are split evenly over
 // `groups` workgroups (workgroup g takes [g*total/groups, (g+1)*total/groups)).
 __device__ __forceinline__ int group_of_unit(int64_t u, int64_t total, int64_t groups) {
@@ -341,7 +349,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     for (int i = threadIdx.x; i < S; i += blockDim.x) {
       int len = a.context_lens[i];
       len = len < 0 ? 0 : (len > max_tokens ? max_tokens : len);
-      s_prefix[i + 1] = (len + BS - 1) / BS;
+      s_prefix[i + 1] = (len + BS - 1) / BS - window_first_block(len, a.window, BS);
     }
     if (threadIdx.x == 0) s_prefix[0] = 0;
     __syncthreads();
@@ -374,7 +382,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     int len = a.context_lens[fixed_seq];
     len = len < 0 ? 0 : (len > max_tokens ? max_tokens : len);
     const int nblk = (len + BS - 1) / BS;
-    ubeg = 0;
+    ubeg = window_first_block(len, a.window, BS);  // (partition mode has no window)
     uend = nblk;
     if (a.mode == kModePartition) {
       ubeg = int64_t(blockIdx.x) * a.partition_blocks;
@@ -397,6 +405,22 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   const uint8_t* kbase = a.k_pool + kvh * head_bytes;
   const uint8_t* vbase = a.v_pool + kvh * head_bytes;
   const float cl2 = a.scale_log2;
+  // ALiBi slopes in log2 units: the MFMA path's lane 16g + h scores head h
+  // (lanes past G repeat a head whose column is never used); the VALU path
+  // keeps all G of its group.
+  float alibi2 = 0.f;
+  float alibi2h[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) alibi2h[h] = 0.f;
+  if (a.alibi) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    if constexpr (MF) {
+      alibi2 = a.alibi[head0 + min(lane & 15, G - 1)] * kLog2e;
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h) alibi2h[h] = a.alibi[head0 + h] * kLog2e;
+    }
+  }
 
   // Single pass over an empty sequence: the output is zero.
   if (a.mode == kModeSingle && uend == 0) {
@@ -526,13 +550,15 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     Window w;
     if (fixed_seq >= 0) {
       w.sk = fixed_seq;
+      w.lk = a.context_lens[w.sk];
       w.jk = int(uu);
     } else {
       w.sk = seq_of(uu);
-      w.jk = int(uu - s_prefix[w.sk]);
+      w.lk = a.context_lens[w.sk];
+      const int len = w.lk < 0 ? 0 : (w.lk > max_tokens ? max_tokens : w.lk);
+      w.jk = int(uu - s_prefix[w.sk]) + window_first_block(len, a.window, BS);
     }
     w.ek = a.block_tables[size_t(w.sk) * a.max_blocks + w.jk];
-    w.lk = a.context_lens[w.sk];
     return w;
   };
 
@@ -662,7 +688,10 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     const int tok0 = __builtin_amdgcn_readlane(w0.jk, idx) * BS + (t % TPB) * TR;
     const int nvalid = (phys < 0 || int64_t(phys) >= a.num_blocks) ? 0 : min(TR, len - tok0);
     if (nvalid <= 0) return;
-    const bool partial = nvalid < TR;
+    // rows before a sliding window (positions < len - W) are masked like the
+    // rows past the end
+    const int nskip = a.window > 0 ? max(0, len - a.window - tok0) : 0;
+    const bool partial = nvalid < TR || nskip > 0;
     if constexpr (MF) {
       // K tile -> LDS, then read back transposed: lane 16g + t gets row t's
       // dims [32mm + 8g, 32mm + 8g + 8) as the A operand of MFMA mm, and lane
@@ -700,10 +729,15 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
       const int g4 = 4 * (lane >> 4);
       float sv[4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        sv[v] = sc[v] * cl2;
-        if (partial && g4 + v >= nvalid) sv[v] = kNegInf;
+      for (int v = 0; v < 4; ++v) sv[v] = sc[v] * cl2;
+      if (a.alibi) {  // slope * (position - (len - 1)), in log2 units
+        const float d0 = float(tok0 + g4 - (len - 1));
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sv[v] = fmaf(alibi2, d0 + float(v), sv[v]);
       }
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (partial && (g4 + v >= nvalid || g4 + v < nskip)) sv[v] = kNegInf;
       const float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       const float mnew = fmaxf(mf_m, mx);
       const float base = (mnew == kNegInf) ? 0.f : mnew;
@@ -737,7 +771,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
       if (__builtin_expect(partial, 0)) {  // the last block of a sequence only
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (4 * r + i >= nvalid)
+          if (4 * r + i >= nvalid || 4 * r + i < nskip)
 #pragma unroll
             for (int e = 0; e < VEC; ++e) v[i][e] = 0.f;  // masked rows may hold NaN
       }
@@ -758,10 +792,18 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int h = 0; h < G; ++h)
           s[i][h] = group_sum<LPR>(dot16<BF16>(0.f, qc[h], score_chunk<ET>(kr[i]))) * cl2;
+      if (a.alibi) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const float d = float(tok0 + i * RPI + r - (len - 1));
+#pragma unroll
+          for (int h = 0; h < G; ++h) s[i][h] = fmaf(alibi2h[h], d, s[i][h]);
+        }
+      }
       if (partial) {
 #pragma unroll
         for (int i = 0; i < NI; ++i)
-          if (i * RPI + r >= nvalid)
+          if (i * RPI + r >= nvalid || i * RPI + r < nskip)
 #pragma unroll
             for (int h = 0; h < G; ++h) s[i][h] = kNegInf;
       }
@@ -789,7 +831,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
       for (int i = 0; i < NI; ++i) {
         float v[VEC];
         unpack_chunk<ET>(vr[i], v);
-        if (partial && i * RPI + r >= nvalid) {
+        if (partial && (i * RPI + r >= nvalid || i * RPI + r < nskip)) {
 #pragma unroll
           for (int e = 0; e < VEC; ++e) v[e] = 0.f;  // masked rows may hold NaN
         }

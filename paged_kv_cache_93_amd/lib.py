@@ -103,7 +103,8 @@ _SIGNATURES = {
     "pa_swap_blocks": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _vp, _i64, _vp, _i32, _i32,
                                       _vp]),
     "pa_decode": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _vp, _vp, _i32, _i32, _i32, _f32,
-                                 _vp, _i32, _vp, ctypes.c_size_t, _vp]),
+                                 ctypes.POINTER(PaAttnVariant), _vp, _i32, _vp, ctypes.c_size_t,
+                                 _vp]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32]),
     "pa_decode_partitions": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _vp, _vp, _i32, _i32,
                                             _i32, _f32, _i32, _vp, _vp, _vp, _i32, _vp]),
@@ -292,13 +293,27 @@ def _decode_common(k_pool, v_pool, q, block_tables, context_lens, k_scale, v_sca
     return cache
 
 
+def _variant(window, alibi_slopes, num_heads):
+    """The pa_attn_variant argument: None (plain attention) or a reference to one."""
+    if not window and alibi_slopes is None:
+        return None
+    if alibi_slopes is not None:
+        _require(alibi_slopes.dtype == torch.float32 and alibi_slopes.is_contiguous() and
+                 alibi_slopes.numel() == num_heads and alibi_slopes.device.type != "cpu",
+                 "alibi_slopes must be a contiguous device float32 [num_heads]")
+    return ctypes.byref(PaAttnVariant(int(window), 0, _ptr(alibi_slopes)))
+
+
 def pa_decode(k_pool, v_pool, q, block_tables, context_lens, scale: float, out, workspace=None,
-              stream=None, k_scale=1.0, v_scale=1.0) -> None:
+              stream=None, k_scale=1.0, v_scale=1.0, window: int = 0,
+              alibi_slopes=None) -> None:
     """Decode attention into out [num_seqs][num_heads][head_dim].
 
     ``workspace`` (from decode_workspace()) enables the balanced split of the
     batch; None walks each sequence in one workgroup.  ``k_scale``/``v_scale``
-    are an 8-bit cache's dequantisation scales.
+    are an 8-bit cache's dequantisation scales.  ``window`` > 0 keeps only the
+    last ``window`` positions; ``alibi_slopes`` (device float32 [num_heads])
+    adds slope * (t - p) to the score of key t for the query at position p.
     """
     cache = _decode_common(k_pool, v_pool, q, block_tables, context_lens, k_scale, v_scale)
     num_seqs, num_heads = q.shape[0], q.shape[1]
@@ -310,7 +325,8 @@ def pa_decode(k_pool, v_pool, q, block_tables, context_lens, scale: float, out, 
         _require(workspace.is_contiguous(), "workspace must be contiguous")
         ws_bytes = workspace.numel() * workspace.element_size()
     _check(load().pa_decode(ctypes.byref(cache), _ptr(q), _ptr(block_tables), _ptr(context_lens),
-                            num_seqs, num_heads, block_tables.shape[1], float(scale), _ptr(out),
+                            num_seqs, num_heads, block_tables.shape[1], float(scale),
+                            _variant(window, alibi_slopes, num_heads), _ptr(out),
                             _dtype_code(out), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
@@ -371,13 +387,7 @@ def pa_prefill(k_pool, v_pool, q, block_tables, query_start, context_lens, scale
     if workspace is None:
         workspace = prefill_workspace(num_seqs, num_tokens, num_heads, k_pool.shape[1],
                                       device=q.device)
-    variant = None
-    if window or alibi_slopes is not None:
-        if alibi_slopes is not None:
-            _require(alibi_slopes.dtype == torch.float32 and alibi_slopes.is_contiguous() and
-                     alibi_slopes.numel() == num_heads and alibi_slopes.device.type != "cpu",
-                     "alibi_slopes must be a contiguous device float32 [num_heads]")
-        variant = ctypes.byref(PaAttnVariant(int(window), 0, _ptr(alibi_slopes)))
+    variant = _variant(window, alibi_slopes, num_heads)
     _check(load().pa_prefill(ctypes.byref(cache), _ptr(q), _ptr(block_tables), _ptr(query_start),
                              _ptr(context_lens), num_seqs, num_tokens, num_heads,
                              block_tables.shape[1], float(scale), variant, _ptr(out),

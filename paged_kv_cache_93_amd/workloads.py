@@ -245,10 +245,14 @@ class Workload:
     def max_blocks_per_seq(self) -> int:
         return int(self.block_tables.shape[1])
 
-    def kv_bytes(self) -> int:
-        """Bytes of K and V that decode must read: sum_i L_i * Hkv * D * 2 * e."""
+    def kv_bytes(self, window: int = 0) -> int:
+        """Bytes of K and V that decode must read: sum_i L_i * Hkv * D * 2 * e,
+        with L_i capped at ``window`` for a sliding window (0: none)."""
         e = element_bytes(self.dtype)
-        return int(self.context_lens.astype(np.int64).sum()) * self.num_kv_heads * self.head_dim * 2 * e
+        lens = self.context_lens.astype(np.int64)
+        if window > 0:
+            lens = np.minimum(lens, window)
+        return int(lens.sum()) * self.num_kv_heads * self.head_dim * 2 * e
 
     def unique_kv_bytes(self) -> int:
         """K/V bytes of distinct (physical block, row) pairs decode reads."""

@@ -70,12 +70,12 @@ def test_cache_struct_layout():
 
 def _decode(cache, **kw):
     a = dict(q=16, tables=16, lens=16, num_seqs=1, num_heads=4, max_blocks=4, scale=0.1,
-             out=16, out_dtype=lib.PA_BF16, ws=None, ws_bytes=0)
+             variant=None, out=16, out_dtype=lib.PA_BF16, ws=None, ws_bytes=0)
     a.update(kw)
     return lib.raw_call("pa_decode", ctypes.byref(cache) if cache is not None else None,
                         a["q"], a["tables"], a["lens"], a["num_seqs"], a["num_heads"],
-                        a["max_blocks"], a["scale"], a["out"], a["out_dtype"], a["ws"],
-                        a["ws_bytes"], None)
+                        a["max_blocks"], a["scale"], a["variant"], a["out"], a["out_dtype"],
+                        a["ws"], a["ws_bytes"], None)
 
 
 def _partitions(cache, **kw):
@@ -107,6 +107,8 @@ def _partitions(cache, **kw):
     ({}, dict(q=0), 1),
     ({}, dict(q=8), 2),                            # misaligned q
     ({}, dict(ws=256, ws_bytes=64), 4),            # workspace too small
+    ({}, dict(variant=ctypes.byref(lib.PaAttnVariant(-1, 0, None))), 2),  # negative window
+    ({}, dict(variant=ctypes.byref(lib.PaAttnVariant(8, 0, 18))), 2),     # misaligned slopes
     (dict(dtype=lib.PA_FP8_E4M3, k_scale=0.0), {}, 2),            # 8-bit cache needs scales
     (dict(dtype=lib.PA_FP8_E4M3, v_scale=float("nan")), {}, 2),
     (dict(dtype=lib.PA_FP8_E4M3, k_scale=float("inf")), {}, 2),
