@@ -2,7 +2,10 @@
 
 A step is the whole hot path over one batch: copy-on-write block copies (when
 the workload has any), the append of every sequence's new K/V through the slot
-mapping, decode attention, and the log-sum-exp merge of split sequences.  The
+mapping, decode attention, and the log-sum-exp merge of split sequences.  By
+default the append runs inside the decode launch (pa_decode_append) when every
+write of the step is a sequence's last position; ``--append separate`` times
+pa_kv_append and pa_decode as two launches.  The
 default workload is the Llama-3.1-8B-class batch (32 query / 8 KV heads,
 head_dim 128, bf16, 16-token blocks, 64 sequences with context lengths uniform
 in [128, 4096]).
@@ -510,6 +513,10 @@ def main() -> int:
                     help="decode: the decode step (default); swap: block swaps to pinned host "
                          "memory; scheduler: the host block manager (no GPU needed)")
     ap.add_argument("--swap-blocks", type=int, default=1024, help="blocks per swap launch")
+    ap.add_argument("--append", default="fused", choices=["fused", "separate"],
+                    help="step: append fused into the decode launch (pa_decode_append; not "
+                         "with split-KV partitions or extra writes) or pa_kv_append then "
+                         "pa_decode")
     ap.add_argument("--window", type=int, default=0,
                     help="decode and prefill: sliding window in tokens (0: none)")
     ap.add_argument("--alibi", action="store_true",
@@ -587,12 +594,23 @@ def main() -> int:
             lib.pa_decode(kp, vp, shared["q"], shared["tables"], shared["lens"], scale, out,
                           workspace=ws, **sc, **var)
 
+    S = w.num_seqs
+    # the fused call writes each sequence's token at its last position; a step
+    # with other writes too (a copy-on-write divergence) keeps pa_kv_append
+    fused = args.append == "fused" and not psize and len(w.slot_mapping) == S
+    if fused:
+        k_own, v_own = shared["k_new"], shared["v_new"]
+
     def step(r):
         kp, vp = pools[r]
         if shared["pairs"].numel():
             lib.pa_copy_blocks(kp, vp, shared["pairs"])
-        lib.pa_kv_append(kp, vp, shared["k_new"], shared["v_new"], shared["slots"], **sc)
-        decode(r)
+        if not fused:
+            lib.pa_kv_append(kp, vp, shared["k_new"], shared["v_new"], shared["slots"], **sc)
+            decode(r)
+            return
+        lib.pa_decode_append(kp, vp, shared["q"], k_own, v_own, shared["tables"], shared["lens"],
+                             scale, out, workspace=ws, **sc, **var)
 
     def timed(fn, n):
         """Mean milliseconds per call of fn over n back-to-back calls, from HIP
@@ -654,6 +672,7 @@ def main() -> int:
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "decode_mode": str(mode),
+                   "append": "fused into decode" if fused else "separate launch",
                    "context_lens": f"{int(w.context_lens.min())}..{int(w.context_lens.max())}, "
                                    f"mean {float(w.context_lens.mean()):.0f}",
                    "seed": w.seed, "rotating_caches": args.rotate,

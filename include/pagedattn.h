@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 6
+#define PA_ABI_VERSION 7
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -224,6 +224,31 @@ int pa_decode(const pa_cache *cache, const void *q, const int32_t *block_tables,
               int32_t max_blocks_per_seq, float scale, const pa_attn_variant *variant,
               void *out, int32_t out_dtype, void *workspace, size_t workspace_bytes,
               void *stream);
+
+/*
+ * pa_decode_append - one decode step in one launch: the append of every
+ * sequence's new token, then pa_decode.
+ *
+ * Sequence i's token sits at position p = L_i - 1 ("How Paged Attention and
+ * Continuous Batching Actually Work", section "One step, end to end": the
+ * forward pass writes the token's K/V through the slot mapping, then attention
+ * reads the cache); its slot is block_tables[i][p / block_size] * block_size +
+ * p % block_size.  The result - pools and out - equals pa_kv_append with
+ * those slots followed by pa_decode with the same arguments, bit for bit.  The
+ * wave that writes a row is the one that reads it back later in the launch,
+ * so no other ordering is needed.  Sequences with L_i = 0, or whose last table
+ * entry is outside the pool, write nothing.
+ *
+ *   k_new, v_new  DEVICE [num_seqs][num_kv_heads][head_dim], the cache type
+ *                 (bfloat16 for an 8-bit cache, quantised with the cache's
+ *                 scales as pa_kv_append does), 16-byte aligned
+ * All other arguments, the workspace and the errors are those of pa_decode.
+ */
+int pa_decode_append(const pa_cache *cache, const void *q, const void *k_new, const void *v_new,
+                     const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
+                     int32_t num_heads, int32_t max_blocks_per_seq, float scale,
+                     const pa_attn_variant *variant, void *out, int32_t out_dtype,
+                     void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes pa_decode needs on the current device for these sizes
  * (0 for a negative or zero size). */

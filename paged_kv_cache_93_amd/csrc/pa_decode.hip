@@ -138,18 +138,30 @@ PA_API size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int
   return layout_for(int64_t(device_cus()) * kMaxGroupsPerCu, num_seqs, num_heads, head_dim).total;
 }
 
-PA_API int pa_decode(const pa_cache* cache, const void* q, const int32_t* block_tables,
-                     const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
-                     int32_t max_blocks_per_seq, float scale, const pa_attn_variant* variant,
-                     void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes,
-                     void* stream) {
-  using namespace pa;
-  const char* fn = "pa_decode";
+namespace pa {
+namespace {
+
+// pa_decode, and pa_decode_append when k_new / v_new are given.
+int decode_call(const char* fn, const pa_cache* cache, const void* q, const void* k_new,
+                const void* v_new, const int32_t* block_tables, const int32_t* context_lens,
+                int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq, float scale,
+                const pa_attn_variant* variant, void* out, int32_t out_dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
   DecodeArgs a;
   int group = 0;
   if (int st = prepare(fn, cache, q, block_tables, context_lens, num_seqs, num_heads,
                        max_blocks_per_seq, scale, &a, &group))
     return st;
+  if (k_new != nullptr || v_new != nullptr) {
+    if (num_seqs > 0 && (!k_new || !v_new))
+      return fail(PA_ERR_NULL, "%s: k_new or v_new is NULL", fn);
+    if (!aligned16(k_new) || !aligned16(v_new))
+      return fail(PA_ERR_SHAPE, "%s: k_new and v_new must be 16-byte aligned", fn);
+    a.k_new = static_cast<const uint8_t*>(k_new);
+    a.v_new = static_cast<const uint8_t*>(v_new);
+    a.k_enc = cache->k_scale;
+    a.v_enc = cache->v_scale;
+  }
   if (variant) {
     if (variant->sliding_window < 0)
       return fail(PA_ERR_SHAPE, "%s: sliding_window must be >= 0", fn);
@@ -207,6 +219,32 @@ PA_API int pa_decode(const pa_cache* cache, const void* q, const int32_t* block_
   else
     hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(256), 0, s, m);
   return launch_result(fn);
+}
+
+}  // namespace
+}  // namespace pa
+
+PA_API int pa_decode(const pa_cache* cache, const void* q, const int32_t* block_tables,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                     int32_t max_blocks_per_seq, float scale, const pa_attn_variant* variant,
+                     void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return pa::decode_call("pa_decode", cache, q, nullptr, nullptr, block_tables, context_lens,
+                         num_seqs, num_heads, max_blocks_per_seq, scale, variant, out, out_dtype,
+                         workspace, workspace_bytes, stream);
+}
+
+PA_API int pa_decode_append(const pa_cache* cache, const void* q, const void* k_new,
+                            const void* v_new, const int32_t* block_tables,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                            int32_t max_blocks_per_seq, float scale,
+                            const pa_attn_variant* variant, void* out, int32_t out_dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (k_new == nullptr || v_new == nullptr))
+    return pa::fail(PA_ERR_NULL, "pa_decode_append: k_new or v_new is NULL");
+  return pa::decode_call("pa_decode_append", cache, q, k_new, v_new, block_tables, context_lens,
+                         num_seqs, num_heads, max_blocks_per_seq, scale, variant, out, out_dtype,
+                         workspace, workspace_bytes, stream);
 }
 
 PA_API int pa_decode_partitions(const pa_cache* cache, const void* q, const int32_t* block_tables,

@@ -45,6 +45,8 @@
 
 #include <cstdint>
 
+#include "pa_e4m3.h"
+
 namespace pa {
 
 enum DecodeMode : int32_t { kModeSingle = 0, kModePartition = 1, kModeBalanced = 2 };
@@ -77,6 +79,14 @@ struct DecodeArgs {
   float v_scale;             // the V pool's scale (8-bit cache), else 1
   int32_t window;            // sliding window in tokens (0: none): attend to L-W .. L-1
   const float* alibi;        // ALiBi slope per query head, or NULL
+  // Fused append (single and balanced modes): sequence i's new-token K and V
+  // rows, [num_seqs][num_kv_heads][D] of the cache type (bf16 for an 8-bit
+  // cache), written at position L_i - 1 through its block table before they
+  // are read; NULL: none.  k_enc / v_enc: an 8-bit cache's pool scales.
+  const uint8_t* k_new;
+  const uint8_t* v_new;
+  float k_enc;
+  float v_enc;
 };
 
 namespace dev {
@@ -615,6 +625,53 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   int64_t cbase = ubeg;
   Window w0 = fetch_window(cbase);
   Window w1 = fetch_window(cbase + 64);
+
+  // Fused append, part 1: each wave writes the new token's K and V rows of its
+  // KV head for every sequence whose last block is one of this workgroup's
+  // units.  The input rows of the first two such sequences are loaded here,
+  // ahead of the first tiles, so writing them later waits for no tile.  Lanes
+  // 0..31 handle K, 32..63 V, one 16-byte input chunk each.
+  const bool appending = a.k_new != nullptr && a.mode != kModePartition;
+  constexpr int kAppChunks = D * QEB / 16;  // 16-byte chunks of an input row
+  const bool app_v = lane >= 32;
+  const int app_ch = lane & 31;
+  // The K-or-V choice of a lane is an offset from the K pointer (a per-lane
+  // choice between two argument fields would be a per-lane memory load); lanes
+  // past the row read its last chunk again, so every lane loads.
+  const int64_t app_src_off = app_v ? a.v_new - a.k_new : 0;
+  const int64_t app_pool_off = app_v ? a.v_pool - a.k_pool : 0;
+  const uint32_t app_scale = app_v ? __builtin_amdgcn_readfirstlane(__float_as_uint(a.v_enc))
+                                   : __builtin_amdgcn_readfirstlane(__float_as_uint(a.k_enc));
+  const int app_chl = app_ch < kAppChunks ? app_ch : kAppChunks - 1;
+  auto new_chunk = [&](int sq) {
+    return reinterpret_cast<const uint4*>(a.k_new + app_src_off +
+                                          (size_t(sq) * a.num_kv_heads + kvh) * D * QEB)[app_chl];
+  };
+  int app_seq[2] = {-1, -1};
+  int64_t app_last[2] = {0, 0};
+  uint4 app_in[2];
+  int app_resume = a.num_seqs;
+  if (appending) {
+    if (fixed_seq >= 0) {
+      app_seq[0] = fixed_seq;
+      app_last[0] = uend - 1;
+    } else {
+      int k = 0, sq = seq_of(ubeg);
+      for (; sq < a.num_seqs && k < 2; ++sq) {
+        const int64_t last = int64_t(s_prefix[sq + 1]) - 1;
+        if (last >= uend) break;
+        if (s_prefix[sq + 1] > s_prefix[sq] && last >= ubeg) {
+          app_seq[k] = sq;
+          app_last[k] = last;
+          ++k;
+        }
+      }
+      app_resume = sq;
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if (app_seq[k] >= 0) app_in[k] = new_chunk(app_seq[k]);
+  }
   start_piece(ubeg);
   // VALU path: the current piece's query and the next piece's, swapped at a
   // piece boundary.  (The MFMA path carries the query in the tile ring.)
@@ -883,6 +940,60 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   u32x4 qb[NB][QC];
 #pragma unroll
   for (int i = 0; i < PF; ++i) load_tile(kb[i], vb[i], qb[i], i);
+
+  // Fused append, part 2 (part 1 loaded the first two rows ahead of the
+  // tiles): write the rows, then load and write those of any further
+  // sequences.  A wavefront's memory operations take effect in program order
+  // and the same wave reads the rows later from its tiles; a row that falls in
+  // a tile already in flight has that tile loaded again after the write.
+  if (appending) {
+    bool reload = false;
+    auto write_row = [&](int sq, int64_t last, uint4 in) {
+      const int idx = int(last - cbase);
+      int phys, len;
+      if (idx < 64) {
+        phys = __builtin_amdgcn_readlane(w0.ek, idx);
+        len = __builtin_amdgcn_readlane(w0.lk, idx);
+      } else if (idx < 128) {
+        phys = __builtin_amdgcn_readlane(w1.ek, idx - 64);
+        len = __builtin_amdgcn_readlane(w1.lk, idx - 64);
+      } else {  // (scalar results, so no other path waits for these loads)
+        len = __builtin_amdgcn_readfirstlane(a.context_lens[sq]);
+        const int cl = len < 0 ? 0 : (len > max_tokens ? max_tokens : len);
+        phys = cl > 0 ? __builtin_amdgcn_readfirstlane(
+                            a.block_tables[size_t(sq) * a.max_blocks + (cl - 1) / BS])
+                      : -1;
+      }
+      len = len < 0 ? 0 : (len > max_tokens ? max_tokens : len);
+      if (len == 0 || phys < 0 || int64_t(phys) >= a.num_blocks) return;
+      const int pos = len - 1;
+      if (int64_t(idx) * TPB + (pos % BS) / TR < PF) reload = true;  // tile already loaded
+      if (app_ch >= kAppChunks) return;
+      uint8_t* row = const_cast<uint8_t*>(a.k_pool) + app_pool_off + size_t(phys) * block_bytes +
+                     kvh * head_bytes + size_t(pos % BS) * D * EB;
+      if constexpr (ET == kFP8)
+        reinterpret_cast<uint2*>(row)[app_ch] =
+            codec::quantize_chunk(in, __uint_as_float(app_scale));
+      else
+        reinterpret_cast<uint4*>(row)[app_ch] = in;
+    };
+    if (app_seq[0] >= 0) write_row(app_seq[0], app_last[0], app_in[0]);
+    if (app_seq[1] >= 0) write_row(app_seq[1], app_last[1], app_in[1]);
+    if (fixed_seq < 0) {
+      for (int sq = app_resume; sq < a.num_seqs; ++sq) {
+        const int64_t last = int64_t(s_prefix[sq + 1]) - 1;
+        if (last >= uend) break;
+        if (s_prefix[sq + 1] > s_prefix[sq] && last >= ubeg) write_row(sq, last, new_chunk(sq));
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (__builtin_amdgcn_readfirstlane(int(reload))) {
+#pragma unroll
+      for (int i = 0; i < PF; ++i) load_tile(kb[i], vb[i], qb[i], i);
+    }
+  }
+
   for (int t0 = 0; t0 < ntiles; t0 += NB) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {

@@ -5,6 +5,7 @@
 // consecutive chunks of a block, so each wave reads and writes whole
 // contiguous runs.  An 8-bit cache's append reads 32 bytes of bf16 per chunk
 // and quantises them.
+#include "pa_e4m3.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -28,32 +29,6 @@ struct AppendArgs {
   float k_scale;
   float v_scale;
 };
-
-// E4M3 code of a binary32 value: nearest, ties to the even code, magnitudes
-// of 448 and more clamped to 448 (the largest code, 0x7E), NaN kept as NaN.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return sign | 0x7Fu;  // NaN
-  if (a >= 0x43E00000u) return sign | 0x7Eu;  // |y| >= 448
-  if (a < 0x3C800000u) {                      // |y| < 2^-6: subnormal codes m * 2^-9
-    const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);  // exact scaling, RNE
-    return sign | uint32_t(m);                // m = 8 is the smallest normal, 0x08
-  }
-  // normal: biased exponent (e - 127) + 7 in 1..15, three mantissa bits kept
-  uint32_t code = ((a >> 23) - 120u) << 3 | ((a >> 20) & 7u);
-  const uint32_t rest = a & 0xFFFFFu;
-  if (rest > 0x80000u || (rest == 0x80000u && (code & 1u))) ++code;  // a carry moves the exponent
-  return sign | code;  // < 448 keeps the code at or below 0x7E
-}
-
-// x / scale rounded to binary32: the binary64 quotient of two binary32 values
-// rounds to the correctly rounded binary32 quotient.
-__device__ __forceinline__ uint32_t quantize_bf16(uint32_t bits16, float scale) {
-  const float x = __uint_as_float(bits16 << 16);
-  return e4m3_code(float(double(x) / double(scale)));
-}
 
 // "How Paged Attention and Continuous Batching Actually Work", section "One
 // step, end to end": the forward pass writes the new token's K/V through the
@@ -83,16 +58,9 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
     }
     // 16 bf16 inputs (two 16-byte chunks of the input row) -> 16 codes
     const float scale = is_v ? a.v_scale : a.k_scale;
-    const uint4 lo = src[2 * src_chunk], hi = src[2 * src_chunk + 1];
-    const uint32_t in[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    uint32_t outw[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t p = in[2 * w], q = in[2 * w + 1];  // elements 4w .. 4w+3
-      outw[w] = quantize_bf16(p & 0xFFFFu, scale) | quantize_bf16(p >> 16, scale) << 8 |
-                quantize_bf16(q & 0xFFFFu, scale) << 16 | quantize_bf16(q >> 16, scale) << 24;
-    }
-    *dst = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+    const uint2 lo = codec::quantize_chunk(src[2 * src_chunk], scale);
+    const uint2 hi = codec::quantize_chunk(src[2 * src_chunk + 1], scale);
+    *dst = make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
 }
 

@@ -28,7 +28,8 @@ STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSU
 
 # Every symbol include/pagedattn.h and include/pa_block_manager.h declare.
 EXPORTED = ("pa_abi_version", "pa_hip_runtime_version", "pa_last_error", "pa_kv_append",
-            "pa_copy_blocks", "pa_swap_blocks", "pa_decode", "pa_decode_workspace_bytes",
+            "pa_copy_blocks", "pa_swap_blocks", "pa_decode", "pa_decode_append",
+            "pa_decode_workspace_bytes",
             "pa_decode_partitions", "pa_splitkv_reduce", "pa_partials_bytes", "pa_prefill",
             "pa_prefill_workspace_bytes",
             "pa_bm_create", "pa_bm_destroy", "pa_bm_add_request", "pa_bm_append_tokens",
@@ -105,6 +106,9 @@ _SIGNATURES = {
     "pa_decode": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _vp, _vp, _i32, _i32, _i32, _f32,
                                  ctypes.POINTER(PaAttnVariant), _vp, _i32, _vp, ctypes.c_size_t,
                                  _vp]),
+    "pa_decode_append": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _vp, _vp, _vp, _vp, _i32,
+                                        _i32, _i32, _f32, ctypes.POINTER(PaAttnVariant), _vp,
+                                        _i32, _vp, ctypes.c_size_t, _vp]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32]),
     "pa_decode_partitions": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _vp, _vp, _i32, _i32,
                                             _i32, _f32, _i32, _vp, _vp, _vp, _i32, _vp]),
@@ -328,6 +332,37 @@ def pa_decode(k_pool, v_pool, q, block_tables, context_lens, scale: float, out, 
                             num_seqs, num_heads, block_tables.shape[1], float(scale),
                             _variant(window, alibi_slopes, num_heads), _ptr(out),
                             _dtype_code(out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pa_decode_append(k_pool, v_pool, q, k_new, v_new, block_tables, context_lens, scale: float,
+                     out, workspace=None, stream=None, k_scale=1.0, v_scale=1.0, window: int = 0,
+                     alibi_slopes=None) -> None:
+    """Append every sequence's new K/V at position L_i - 1 and decode, in one launch.
+
+    ``k_new``/``v_new``: [num_seqs][num_kv_heads][head_dim] of the token dtype
+    (bf16 for an 8-bit cache).  Same result as pa_kv_append with the
+    table-derived slots followed by pa_decode.
+    """
+    cache = _decode_common(k_pool, v_pool, q, block_tables, context_lens, k_scale, v_scale)
+    num_seqs, num_heads = q.shape[0], q.shape[1]
+    for t in (k_new, v_new):
+        _require(t is not None and t.is_contiguous() and t.dtype == _token_dtype(cache) and
+                 tuple(t.shape) == (num_seqs, cache.num_kv_heads, cache.head_dim),
+                 "k_new/v_new must be contiguous [num_seqs][num_kv_heads][head_dim] of the "
+                 "token dtype")
+    _require(out is not None and out.is_contiguous() and
+             tuple(out.shape) == (num_seqs, num_heads, cache.head_dim),
+             "out must be contiguous [num_seqs][num_heads][head_dim]")
+    ws_bytes = 0
+    if workspace is not None:
+        _require(workspace.is_contiguous(), "workspace must be contiguous")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().pa_decode_append(ctypes.byref(cache), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                   _ptr(block_tables), _ptr(context_lens), num_seqs, num_heads,
+                                   block_tables.shape[1], float(scale),
+                                   _variant(window, alibi_slopes, num_heads), _ptr(out),
+                                   _dtype_code(out), _ptr(workspace), ws_bytes,
+                                   _stream(stream)))
 
 
 def pa_decode_partitions(k_pool, v_pool, q, block_tables, context_lens, scale: float,

@@ -78,6 +78,37 @@ def _decode(cache, **kw):
                         a["ws"], a["ws_bytes"], None)
 
 
+def _decode_append(cache, **kw):
+    a = dict(q=16, k_new=16, v_new=16, tables=16, lens=16, num_seqs=1, num_heads=4,
+             max_blocks=4, scale=0.1, variant=None, out=16, out_dtype=lib.PA_BF16, ws=None,
+             ws_bytes=0)
+    a.update(kw)
+    return lib.raw_call("pa_decode_append", ctypes.byref(cache) if cache is not None else None,
+                        a["q"], a["k_new"], a["v_new"], a["tables"], a["lens"], a["num_seqs"],
+                        a["num_heads"], a["max_blocks"], a["scale"], a["variant"], a["out"],
+                        a["out_dtype"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("cache_kw,call_kw,status", [
+    (None, {}, 1),
+    ({}, dict(k_new=0), 1),
+    ({}, dict(v_new=0), 1),
+    ({}, dict(k_new=8), 2),                        # misaligned k_new
+    ({}, dict(v_new=24), 2),
+    ({}, dict(num_heads=3), 2),                    # the checks of pa_decode apply too
+    ({}, dict(ws=256, ws_bytes=64), 4),
+    ({}, dict(variant=ctypes.byref(lib.PaAttnVariant(-1, 0, None))), 2),
+])
+def test_decode_append_rejects_bad_arguments(cache_kw, call_kw, status):
+    cache = None if cache_kw is None else _cache(**cache_kw)
+    assert _decode_append(cache, **call_kw) == status
+    assert lib.load().pa_last_error().decode().startswith("pa_decode_append:")
+
+
+def test_decode_append_with_no_sequences_is_a_no_op():
+    assert _decode_append(_cache(), num_seqs=0, k_new=0, v_new=0) == 0
+
+
 def _partitions(cache, **kw):
     a = dict(q=16, tables=16, lens=16, num_seqs=1, num_heads=4, max_blocks=4, scale=0.1,
              psize=32, po=16, pm=16, ps=16, max_parts=1)
