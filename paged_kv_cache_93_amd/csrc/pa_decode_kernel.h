@@ -565,8 +565,11 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     } else {
       w.sk = seq_of(uu);
       w.lk = a.context_lens[w.sk];
-      const int len = w.lk < 0 ? 0 : (w.lk > max_tokens ? max_tokens : w.lk);
-      w.jk = int(uu - s_prefix[w.sk]) + window_first_block(len, a.window, BS);
+      w.jk = int(uu - s_prefix[w.sk]);
+      if (a.window > 0) {  // only then does the table entry's index wait for the length
+        const int len = w.lk < 0 ? 0 : (w.lk > max_tokens ? max_tokens : w.lk);
+        w.jk += window_first_block(len, a.window, BS);
+      }
     }
     w.ek = a.block_tables[size_t(w.sk) * a.max_blocks + w.jk];
     return w;
