@@ -290,6 +290,13 @@ __device__ __forceinline__ int group_of_unit(int64_t u, int64_t total, int64_t g
 #define PA_PACE 1  // 0: no issue-priority pacing between the waves of a SIMD
 #endif
 
+#ifndef PA_DECODE_MFMA_PV
+#define PA_DECODE_MFMA_PV 1  // 1: the MFMA path's P.V on MFMA too; 0: on the VALU
+#endif
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+#define PA_LDS_PTR(T) __attribute__((address_space(3))) T*
+
 #ifndef PA_MFMA_SCORES
 #define PA_MFMA_SCORES 1  // 0: score every case on the VALU (for comparison)
 #endif
@@ -456,12 +463,61 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   // head h in mf_m / mf_l; m[] and l[] are filled only when a piece is emitted.
   float m[G], l[G], acc[G][VEC];
   float mf_m = kNegInf, mf_l = 0.f;
+  // MFMA P.V: O^T blocks of 16 dims (lane 16g + h: dims 16b + 4g + v of
+  // head h), the exponent base mf_m (shared by the four row groups of a head
+  // and moved lazily) and the true running maximum mf_top
+  constexpr bool MFPV = MF && PA_DECODE_MFMA_PV;
+  constexpr int NB16 = D / 16;
+  f32x4 oacc[MFPV ? NB16 : 1];
+  float mf_top = kNegInf;
   u32x4 qc[MF ? 1 : G];  // VALU path: chunk c of each head's query
   u32x4 qf[MF ? 4 : 1];  // MFMA path: the current sequence's query as B operands
 
   // Emit the finished piece of sequence `seq`: the final output when the piece
   // is the whole sequence, else a partial row.
   auto emit = [&](int seq, bool whole) {
+    if constexpr (MFPV) {
+      // the four row groups' sums share the base; the maximum and the sum are
+      // reported against the true maximum
+      const float lt = xor_sum<16>(mf_l);
+      const int hh = lane & 15;
+      if (hh < G) {
+        const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
+        const int head = head0 + hh;
+        const int d0 = 4 * (lane >> 4);
+        if (whole) {
+          const size_t idx = (size_t(seq) * a.num_heads + head) * D + d0;
+#pragma unroll
+          for (int b = 0; b < NB16; ++b) {
+            const f32x4 o = oacc[b] * inv;
+            if (a.out_f32) {
+              *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + idx + 16 * b) = o;
+            } else {
+              const u32x2 w = {to_bf16(o[0]) | (to_bf16(o[1]) << 16),
+                               to_bf16(o[2]) | (to_bf16(o[3]) << 16)};
+              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + idx + 16 * b) = w;
+            }
+          }
+        } else {
+          size_t row;
+          if (a.mode == kModePartition)
+            row = (size_t(seq) * a.num_heads + head) * a.max_parts + blockIdx.x;
+          else
+            row = (size_t(blockIdx.x) + seq) * a.num_heads + head;  // piece slot g + seq
+          float* o = a.part_out + row * D + d0;
+#pragma unroll
+          for (int b = 0; b < NB16; ++b) *reinterpret_cast<f32x4*>(o + 16 * b) = oacc[b] * inv;
+          if (lane < 16) {
+            const float lsum = mf_top == kNegInf ? 0.f : lt * fast_exp2(mf_m - mf_top);
+            // partition partials carry natural-log maxima; pieces stay in log2 units
+            a.part_max[row] = (mf_top == kNegInf || a.mode == kModeBalanced) ? mf_top
+                                                                             : mf_top * kLn2;
+            a.part_sum[row] = lsum;
+          }
+        }
+      }
+      return;
+    }
     if constexpr (MF) {
       // hand each row group's (m, l) of every head to all lanes of the group
       if ((lane & 15) < G) {
@@ -595,6 +651,11 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   auto reset_state = [&]() {
     mf_m = kNegInf;
     mf_l = 0.f;
+    mf_top = kNegInf;
+    if constexpr (MFPV) {
+#pragma unroll
+      for (int b = 0; b < NB16; ++b) oacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       m[h] = kNegInf;
@@ -798,6 +859,63 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int v = 0; v < 4; ++v)
         if (partial && (g4 + v >= nvalid || g4 + v < nskip)) sv[v] = kNegInf;
+      if constexpr (MFPV) {
+        // One base per head over its four row groups (lanes h, 16+h, 32+h,
+        // 48+h).  It moves only when the maximum passes it by more than 8
+        // (log2 units): weights stay <= 2^8 and O is rescaled rarely.
+        const float mx = xor_max<16>(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+        mf_top = fmaxf(mf_top, mx);
+        const bool move = mx > mf_m + 8.f;
+        const float mnew = move ? mx : mf_m;
+        const float base = (mnew == kNegInf) ? 0.f : mnew;
+        const float alpha = move ? fast_exp2(mf_m - base) : 1.f;
+        mf_m = mnew;
+        float pv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) pv[v] = fast_exp2(sv[v] - base);
+        mf_l = fmaf(mf_l, alpha, (pv[0] + pv[1]) + (pv[2] + pv[3]));
+        if (__ballot(move) != 0) {
+#pragma unroll
+          for (int b = 0; b < NB16; ++b) oacc[b] *= alpha;
+        }
+        // The weights of rows 4g..4g+3 of head h, already in lane 16g + h, are
+        // the B operand of O^T += V^T P, as three bf16 terms: the weight's top
+        // 16 bits, then those of each remainder (both subtractions are exact);
+        // together they leave out less than 2^-23 of the weight.
+        v4s p3[3];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float rest = pv[v];
+#pragma unroll
+          for (int k = 0; k < 3; ++k) {
+            const uint32_t top = __float_as_uint(rest) & 0xFFFF0000u;
+            p3[k][v] = short(top >> 16);
+            rest -= __uint_as_float(top);
+          }
+        }
+        // V tile -> LDS over the K tile just read (row-major, 17 chunks a row),
+        // rows that do not count zeroed (they may hold NaN); then transposed
+        // reads give lane 16g + s dim 16b + s of rows 4g..4g+3: the A operand.
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u32x4 vc = score_chunk<ET>(vr[i]);
+          if (partial && (4 * r + i >= nvalid || 4 * r + i < nskip)) vc = u32x4{0u, 0u, 0u, 0u};
+          lds_k[(4 * r + i) * 17 + c] = vc;
+        }
+        asm volatile("" ::: "memory");
+        PA_LDS_PTR(uint8_t) lv = (PA_LDS_PTR(uint8_t))lds_k;
+        const int voff = (4 * (lane >> 4) + ((lane & 15) >> 2)) * 272 + 8 * (lane & 3);
+#pragma unroll
+        for (int b = 0; b < NB16; ++b) {
+          const v4s vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS_PTR(v4s))(lv + voff + 32 * b));
+#pragma unroll
+          for (int k = 0; k < 3; ++k)
+            oacc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, p3[k], oacc[b], 0, 0, 0);
+        }
+        asm volatile("" ::: "memory");
+        return;
+      }
       const float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       const float mnew = fmaxf(mf_m, mx);
       const float base = (mnew == kNegInf) ? 0.f : mnew;
