@@ -171,6 +171,12 @@ def _kv_f64(rows, dtype: str, scale: float) -> np.ndarray:
     return to_f64(rows, dtype)
 
 
+def head_scale(scale, kv_head: int) -> float:
+    """The scale of KV head ``kv_head``: one number for the whole pool, or one
+    per KV head (a sequence indexed by head)."""
+    return float(scale) if np.ndim(scale) == 0 else float(scale[kv_head])
+
+
 def _q_dtype(dtype: str) -> str:
     return "bf16" if dtype == "fp8" else dtype
 
@@ -300,9 +306,9 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale: float,
             continue
         for g in range(num_kv_heads):
             keys = _kv_f64(gather_rows(k_pool, block_tables[i], length, block_size, g),
-                           dtype, k_scale)
+                           dtype, head_scale(k_scale, g))
             values = _kv_f64(gather_rows(v_pool, block_tables[i], length, block_size, g),
-                             dtype, v_scale)
+                             dtype, head_scale(v_scale, g))
             lo, hi = attended_range(length - 1, window)
             for h in range(g * group, (g + 1) * group):
                 scores = scale * (keys[lo:hi] @ q64[i, h])
@@ -407,9 +413,9 @@ def prefill(q, k_pool, v_pool, block_tables, query_start, context_lens, scale: f
             continue
         for g in range(num_kv_heads):
             keys = _kv_f64(gather_rows(k_pool, block_tables[i], length, block_size, g),
-                           dtype, k_scale)
+                           dtype, head_scale(k_scale, g))
             values = _kv_f64(gather_rows(v_pool, block_tables[i], length, block_size, g),
-                             dtype, v_scale)
+                             dtype, head_scale(v_scale, g))
             for j in range(n):
                 p = query_position(length, n, j)
                 if p < 0:
@@ -457,9 +463,9 @@ def decode_partitions(q, k_pool, v_pool, block_tables, context_lens, scale: floa
             raise ValueError("max_parts too small for context_lens")
         for g in range(num_kv_heads):
             keys = _kv_f64(gather_rows(k_pool, block_tables[i], length, block_size, g),
-                           dtype, k_scale)
+                           dtype, head_scale(k_scale, g))
             values = _kv_f64(gather_rows(v_pool, block_tables[i], length, block_size, g),
-                             dtype, v_scale)
+                             dtype, head_scale(v_scale, g))
             for h in range(g * group, (g + 1) * group):
                 scores = scale * (keys @ q64[i, h])
                 for p in range(nparts):
@@ -510,6 +516,17 @@ def splitkv_merge(part_out, part_max, part_sum, context_lens, partition_size: in
 # KV writes (byte-exact)
 # ---------------------------------------------------------------------------
 
+def _quantize_heads(rows, scale) -> np.ndarray:
+    """fp8_quantize of [n][num_kv_heads][head_dim] rows, head by head."""
+    rows = np.asarray(rows)
+    if np.ndim(scale) == 0:
+        return fp8_quantize(rows, scale)
+    out = np.empty(rows.shape, dtype=np.uint8)
+    for g in range(rows.shape[1]):
+        out[:, g, :] = fp8_quantize(rows[:, g, :], float(scale[g]))
+    return out
+
+
 def kv_append(k_pool, v_pool, k_new, v_new, slot_mapping, fp8_scales=None):
     """Pools after writing each new token's K/V rows at its slot.
 
@@ -524,13 +541,15 @@ def kv_append(k_pool, v_pool, k_new, v_new, slot_mapping, fp8_scales=None):
 
     With ``fp8_scales = (k_scale, v_scale)`` the pools are an 8-bit cache and
     k_new / v_new hold bfloat16 bit patterns: each row is stored as
-    :func:`fp8_quantize` of it with the pool's scale instead of a bit copy.
+    :func:`fp8_quantize` of it with the pool's scale instead of a bit copy.  A
+    scale may also be one per KV head (a sequence indexed by head), each head's
+    rows then quantised with their own.
     """
     k_out = np.array(k_pool, copy=True)
     v_out = np.array(v_pool, copy=True)
     if fp8_scales is not None:
-        k_new = fp8_quantize(k_new, fp8_scales[0])
-        v_new = fp8_quantize(v_new, fp8_scales[1])
+        k_new = _quantize_heads(k_new, fp8_scales[0])
+        v_new = _quantize_heads(v_new, fp8_scales[1])
     block_size = k_pool.shape[2]
     slots = [int(s) for s in slot_mapping]
     live = [s for s in slots if s >= 0]
