@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 7
+#define PA_ABI_VERSION 8
 
 typedef enum pa_status {
   PA_OK = 0,
@@ -78,6 +78,13 @@ typedef struct pa_cache {
   int32_t dtype;         /* pa_dtype of both pools */
   float k_scale;         /* PA_FP8_E4M3: dequantisation scales of the pools, positive */
   float v_scale;         /*   and finite; ignored for the other types */
+  /* PA_FP8_E4M3 only, optional: one scale per KV head, DEVICE float
+   * [num_kv_heads] each, positive and finite, 4-byte aligned; both or
+   * neither.  When given they replace k_scale / v_scale: head g's codes are
+   * its values divided by k_scales[g] (v_scales[g]).  NULL for the other
+   * types. */
+  const float *k_scales;
+  const float *v_scales;
 } pa_cache;
 
 /* Version of this header the library was built from (PA_ABI_VERSION). */

@@ -8,8 +8,9 @@
 
 #include <cstddef>
 
-static_assert(sizeof(pa_cache) == 48 && offsetof(pa_cache, dtype) == 36 &&
-                  offsetof(pa_cache, k_scale) == 40 && offsetof(pa_cache, v_scale) == 44,
+static_assert(sizeof(pa_cache) == 64 && offsetof(pa_cache, dtype) == 36 &&
+                  offsetof(pa_cache, k_scale) == 40 && offsetof(pa_cache, v_scale) == 44 &&
+                  offsetof(pa_cache, k_scales) == 48 && offsetof(pa_cache, v_scales) == 56,
               "pa_cache layout is part of the ABI");
 static_assert(sizeof(pa_attn_variant) == 16 && offsetof(pa_attn_variant, alibi_slopes) == 8,
               "pa_attn_variant layout is part of the ABI");
@@ -57,6 +58,15 @@ int check_cache(const pa_cache* cache, const char* fn) {
       !(cache->k_scale > 0.f && cache->v_scale > 0.f && std::isfinite(cache->k_scale) &&
         std::isfinite(cache->v_scale)))
     return fail(PA_ERR_SHAPE, "%s: an 8-bit cache needs positive finite k_scale and v_scale", fn);
+  if (cache->k_scales != nullptr || cache->v_scales != nullptr) {
+    if (cache->dtype != PA_FP8_E4M3)
+      return fail(PA_ERR_SHAPE, "%s: per-head scales belong to an 8-bit cache only", fn);
+    if (cache->k_scales == nullptr || cache->v_scales == nullptr)
+      return fail(PA_ERR_NULL, "%s: k_scales and v_scales go together", fn);
+    if ((reinterpret_cast<uintptr_t>(cache->k_scales) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(cache->v_scales) & 3u) != 0)
+      return fail(PA_ERR_SHAPE, "%s: k_scales and v_scales must be 4-byte aligned", fn);
+  }
   return PA_OK;
 }
 

@@ -109,8 +109,12 @@ int prepare(const char* fn, const pa_cache* cache, const void* q, const int32_t*
   a->out_f32 = 1;
   // an 8-bit cache's K scale multiplies every score, its V scale every output
   const bool fp8 = cache->dtype == PA_FP8_E4M3;
-  a->scale_log2 = scale * 1.4426950408889634f * (fp8 ? cache->k_scale : 1.f);
-  a->v_scale = fp8 ? cache->v_scale : 1.f;
+  // (one scale per KV head: applied per head in the kernel instead)
+  const bool per_head = fp8 && cache->k_scales != nullptr;
+  a->scale_log2 = scale * 1.4426950408889634f * (fp8 && !per_head ? cache->k_scale : 1.f);
+  a->v_scale = fp8 && !per_head ? cache->v_scale : 1.f;
+  a->k_scales = per_head ? cache->k_scales : nullptr;
+  a->v_scales = per_head ? cache->v_scales : nullptr;
   a->window = 0;
   a->alibi = nullptr;
   return PA_OK;

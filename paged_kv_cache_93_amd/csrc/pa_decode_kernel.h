@@ -87,6 +87,11 @@ struct DecodeArgs {
   const uint8_t* v_new;
   float k_enc;
   float v_enc;
+  // 8-bit cache with one scale per KV head (or NULL): k_scales[g] multiplies
+  // head g's scores (scale_log2 then leaves it out) and also encodes the fused
+  // append's K codes; v_scales[g] its outputs and V codes
+  const float* k_scales;
+  const float* v_scales;
 };
 
 namespace dev {
@@ -421,7 +426,8 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   const size_t block_bytes = head_bytes * a.num_kv_heads;
   const uint8_t* kbase = a.k_pool + kvh * head_bytes;
   const uint8_t* vbase = a.v_pool + kvh * head_bytes;
-  const float cl2 = a.scale_log2;
+  const float cl2 = a.k_scales ? a.scale_log2 * a.k_scales[kvh] : a.scale_log2;
+  const float vsc = a.v_scales ? a.v_scales[kvh] : a.v_scale;
   // ALiBi slopes in log2 units: the MFMA path's lane 16g + h scores head h
   // (lanes past G repeat a head whose column is never used); the VALU path
   // keeps all G of its group.
@@ -482,7 +488,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
       const float lt = xor_sum<16>(mf_l);
       const int hh = lane & 15;
       if (hh < G) {
-        const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
+        const float inv = lt > 0.f ? vsc / lt : 0.f;
         const int head = head0 + hh;
         const int d0 = 4 * (lane >> 4);
         if (whole) {
@@ -546,7 +552,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     if (r != 0) return;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float inv = l[h] > 0.f ? a.v_scale / l[h] : 0.f;
+      const float inv = l[h] > 0.f ? vsc / l[h] : 0.f;
       const int head = head0 + h;
       if (whole) {
         const size_t idx = (size_t(seq) * a.num_heads + head) * D + c * VEC;
@@ -704,8 +710,10 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   // past the row read its last chunk again, so every lane loads.
   const int64_t app_src_off = app_v ? a.v_new - a.k_new : 0;
   const int64_t app_pool_off = app_v ? a.v_pool - a.k_pool : 0;
-  const uint32_t app_scale = app_v ? __builtin_amdgcn_readfirstlane(__float_as_uint(a.v_enc))
-                                   : __builtin_amdgcn_readfirstlane(__float_as_uint(a.k_enc));
+  const float app_kenc = appending && a.k_scales ? a.k_scales[kvh] : a.k_enc;
+  const float app_venc = appending && a.v_scales ? a.v_scales[kvh] : a.v_enc;
+  const uint32_t app_scale = app_v ? __builtin_amdgcn_readfirstlane(__float_as_uint(app_venc))
+                                   : __builtin_amdgcn_readfirstlane(__float_as_uint(app_kenc));
   const int app_chl = app_ch < kAppChunks ? app_ch : kAppChunks - 1;
   auto new_chunk = [&](int sq) {
     return reinterpret_cast<const uint4*>(a.k_new + app_src_off +

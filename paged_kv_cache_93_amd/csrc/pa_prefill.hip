@@ -85,6 +85,8 @@ struct PrefillArgs {
   int32_t max_tiles;
   float scale_log2;  // score scale * log2(e), times the K pool's scale (8-bit cache)
   float v_scale;     // the V pool's scale (8-bit cache), else 1
+  const float* k_scales;  // 8-bit cache with one scale per KV head (then the two above
+  const float* v_scales;  //   leave them out), or NULL
   int32_t window;    // sliding window in tokens (0: none)
   const float* alibi;  // ALiBi slope per query head, or NULL
 };
@@ -227,6 +229,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
   const int logical = xcd * (nwg / 8) + min(xcd, nwg % 8) + slot;
   const int t = logical % gridDim.x;
   const int g = logical / gridDim.x;
+  const float sl2 = a.k_scales ? a.scale_log2 * a.k_scales[g] : a.scale_log2;
+  const float vsc = a.v_scales ? a.v_scales[g] : a.v_scale;
   if (t >= a.tiles[0]) return;
   const int seq = a.tiles[1 + 2 * t];
   const int tile = a.tiles[2 + 2 * t];
@@ -398,7 +402,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     }
 
     u32x4 pf[2];
-    softmax_step<AL>(s, pf, k0, pos, lo_row, slope2, min_pos, max_pos, W, a.scale_log2, grp, m,
+    softmax_step<AL>(s, pf, k0, pos, lo_row, slope2, min_pos, max_pos, W, sl2, grp, m,
                      lsum, acc);
 
     // O^T += V^T P^T: A = dims 16dt + r, keys in the permuted k order
@@ -429,7 +433,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     const float l = xor_sum<16>(lsum[rt]);
-    const float inv = l > 0.f ? a.v_scale / l : 0.f;
+    const float inv = l > 0.f ? vsc / l : 0.f;
     if (!valid[rt]) continue;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -497,6 +501,8 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
   const int logical = xcd * (nwg / 8) + min(xcd, nwg % 8) + slot;
   const int t = logical % gridDim.x;
   const int g = logical / gridDim.x;
+  const float sl2 = a.k_scales ? a.scale_log2 * a.k_scales[g] : a.scale_log2;
+  const float vsc = a.v_scales ? a.v_scales[g] : a.v_scale;
   if (t >= a.tiles[0]) return;
   const int seq = a.tiles[1 + 2 * t];
   const int tile = a.tiles[2 + 2 * t];
@@ -669,7 +675,7 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
     }
 
     u32x4 pf[NRT];
-    softmax_step<AL, NRT>(sc4, pf, k0, pos, lo_row, slope2, min_pos, max_pos, W, a.scale_log2,
+    softmax_step<AL, NRT>(sc4, pf, k0, pos, lo_row, slope2, min_pos, max_pos, W, sl2,
                           grp, m, lsum, acc);
 
     // O^T += V^T P^T: two transposed reads give keys 4g..4g+3 and 16+4g..16+4g+3
@@ -701,7 +707,7 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     const float l = xor_sum<16>(lsum[rt]);
-    const float inv = l > 0.f ? a.v_scale / l : 0.f;
+    const float inv = l > 0.f ? vsc / l : 0.f;
     if (!valid[rt]) continue;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -851,8 +857,11 @@ PA_API int pa_prefill(const pa_cache* cache, const void* q, const int32_t* block
   a.max_blocks = max_blocks_per_seq;
   a.max_tiles = int32_t(max_tiles);
   const bool fp8 = cache->dtype == PA_FP8_E4M3;
-  a.scale_log2 = scale * 1.4426950408889634f * (fp8 ? cache->k_scale : 1.0f);
-  a.v_scale = fp8 ? cache->v_scale : 1.0f;
+  const bool per_head = fp8 && cache->k_scales != nullptr;
+  a.scale_log2 = scale * 1.4426950408889634f * (fp8 && !per_head ? cache->k_scale : 1.0f);
+  a.v_scale = fp8 && !per_head ? cache->v_scale : 1.0f;
+  a.k_scales = per_head ? cache->k_scales : nullptr;
+  a.v_scales = per_head ? cache->v_scales : nullptr;
   a.window = window;
   a.alibi = alibi;
   const dim3 grid(unsigned(max_tiles), unsigned(cache->num_kv_heads));

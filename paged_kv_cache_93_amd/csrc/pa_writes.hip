@@ -28,6 +28,8 @@ struct AppendArgs {
   int32_t quantize;         // 8-bit cache: bf16 inputs stored as E4M3 codes
   float k_scale;
   float v_scale;
+  const float* k_scales;    // per KV head, or NULL (then k_scale / v_scale)
+  const float* v_scales;
 };
 
 // "How Paged Attention and Continuous Batching Actually Work", section "One
@@ -57,7 +59,8 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
       continue;
     }
     // 16 bf16 inputs (two 16-byte chunks of the input row) -> 16 codes
-    const float scale = is_v ? a.v_scale : a.k_scale;
+    const float* per_head = is_v ? a.v_scales : a.k_scales;
+    const float scale = per_head ? per_head[head] : (is_v ? a.v_scale : a.k_scale);
     const uint2 lo = codec::quantize_chunk(src[2 * src_chunk], scale);
     const uint2 hi = codec::quantize_chunk(src[2 * src_chunk + 1], scale);
     *dst = make_uint4(lo.x, lo.y, hi.x, hi.y);
@@ -134,6 +137,8 @@ PA_API int pa_kv_append(const pa_cache* cache, const void* k_new, const void* v_
   a.quantize = cache->dtype == PA_FP8_E4M3 ? 1 : 0;
   a.k_scale = cache->k_scale;
   a.v_scale = cache->v_scale;
+  a.k_scales = cache->k_scales;
+  a.v_scales = cache->v_scales;
   a.total_chunks = int64_t(num_tokens) * 2 * cache->num_kv_heads * a.chunks_per_row;
   hipLaunchKernelGGL(append_kernel, dim3(grid_for(a.total_chunks)), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), a);

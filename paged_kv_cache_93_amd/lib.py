@@ -49,7 +49,8 @@ class PaCache(ctypes.Structure):
                 ("num_blocks", ctypes.c_int64), ("num_kv_heads", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("k_scale", ctypes.c_float),
-                ("v_scale", ctypes.c_float)]
+                ("v_scale", ctypes.c_float), ("k_scales", ctypes.c_void_p),
+                ("v_scales", ctypes.c_void_p)]
 
 
 class PaAttnVariant(ctypes.Structure):
@@ -191,15 +192,24 @@ def make_cache(k_pool: torch.Tensor, v_pool: torch.Tensor, k_scale: float = 1.0,
                v_scale: float = 1.0) -> PaCache:
     """pa_cache for two [num_blocks][num_kv_heads][block_size][head_dim] pools.
 
-    The scales are the dequantisation scales of an 8-bit (E4M3) cache; the
-    other element types ignore them.
+    The scales are the dequantisation scales of an 8-bit (E4M3) cache: floats
+    (one per pool), or device float32 tensors [num_kv_heads] (one per KV head,
+    both pools alike); the other element types ignore float scales.
     """
     _require(k_pool.dim() == 4 and k_pool.shape == v_pool.shape and k_pool.dtype == v_pool.dtype,
              "k_pool and v_pool must be equal-shaped 4-D tensors")
     _require(k_pool.is_contiguous() and v_pool.is_contiguous(), "pools must be contiguous")
     nb, hkv, bs, d = k_pool.shape
+    per_head = isinstance(k_scale, torch.Tensor) or isinstance(v_scale, torch.Tensor)
+    if not per_head:
+        return PaCache(k_pool.data_ptr(), v_pool.data_ptr(), nb, hkv, bs, d, _dtype_code(k_pool),
+                       float(k_scale), float(v_scale), None, None)
+    for t in (k_scale, v_scale):
+        _require(isinstance(t, torch.Tensor) and t.dtype == torch.float32 and t.is_contiguous()
+                 and t.numel() == hkv and t.device.type != "cpu",
+                 "per-head scales: contiguous device float32 tensors [num_kv_heads], both")
     return PaCache(k_pool.data_ptr(), v_pool.data_ptr(), nb, hkv, bs, d, _dtype_code(k_pool),
-                   float(k_scale), float(v_scale))
+                   1.0, 1.0, k_scale.data_ptr(), v_scale.data_ptr())
 
 
 def abi_version() -> int:

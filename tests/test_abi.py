@@ -55,17 +55,19 @@ def test_partials_bytes():
 
 def _cache(**kw):
     c = dict(k_pool=16, v_pool=32, num_blocks=4, num_kv_heads=2, block_size=16, head_dim=128,
-             dtype=lib.PA_BF16, k_scale=1.0, v_scale=1.0)
+             dtype=lib.PA_BF16, k_scale=1.0, v_scale=1.0, k_scales=None, v_scales=None)
     c.update(kw)
     return lib.PaCache(c["k_pool"], c["v_pool"], c["num_blocks"], c["num_kv_heads"],
-                       c["block_size"], c["head_dim"], c["dtype"], c["k_scale"], c["v_scale"])
+                       c["block_size"], c["head_dim"], c["dtype"], c["k_scale"], c["v_scale"],
+                       c["k_scales"], c["v_scales"])
 
 
 def test_cache_struct_layout():
     # the C side asserts the same size and offsets (pa_api.hip)
-    assert ctypes.sizeof(lib.PaCache) == 48
+    assert ctypes.sizeof(lib.PaCache) == 64
     assert lib.PaCache.dtype.offset == 36 and lib.PaCache.k_scale.offset == 40
     assert lib.PaCache.v_scale.offset == 44
+    assert lib.PaCache.k_scales.offset == 48 and lib.PaCache.v_scales.offset == 56
 
 
 def _decode(cache, **kw):
@@ -144,6 +146,9 @@ def _partitions(cache, **kw):
     (dict(dtype=lib.PA_FP8_E4M3, v_scale=float("nan")), {}, 2),
     (dict(dtype=lib.PA_FP8_E4M3, k_scale=float("inf")), {}, 2),
     (dict(dtype=lib.PA_FP8_E4M3), dict(out_dtype=lib.PA_FP8_E4M3), 3),  # no 8-bit output
+    (dict(k_scales=64, v_scales=128), {}, 2),                    # per-head scales: 8-bit only
+    (dict(dtype=lib.PA_FP8_E4M3, k_scales=64), {}, 1),           # both or neither
+    (dict(dtype=lib.PA_FP8_E4M3, k_scales=64, v_scales=130), {}, 2),  # misaligned
     (dict(dtype=lib.PA_F32), dict(out_dtype=lib.PA_BF16), 3),          # f32 cache: f32 out
 ])
 def test_decode_rejects_bad_arguments(cache_kw, call_kw, status):
