@@ -23,16 +23,22 @@
 //   ones write the output, pieces write partials merged by merge_kernel).
 // * Rows are loaded in 16-byte chunks with non-temporal loads (the cache is
 //   streamed once); one load instruction covers 1 KiB of contiguous rows.
-// * q.k, bf16 with 128-dim heads: a 16-row K tile goes through LDS into the
-//   MFMA A layout and four v_mfma_f32_16x16x32_bf16 score it against the G
-//   query heads (the B operand; columns past G are ignored).  Other cases:
-//   each lane dots its 16-byte chunk against the same chunk of each query
-//   head (v_dot2 for bf16 pairs, f32 accumulation) and the lanes of a row add
-//   up their partial sums with DPP row rotations.
-// * Running softmax in log2 units (s*scale*log2 e), so weights are exp2(s - m)
-//   and the maximum gets exactly 1; the V rows are accumulated on the VALU in
-//   f32.  Row groups (lanes that see the same rows) keep their own running
-//   state and are merged once per piece with the log-sum-exp rule.
+// * q.k, bf16 and 8-bit caches with 128-dim heads and blocks of 16 or 32: a
+//   16-row K tile goes through LDS into the MFMA A layout and four
+//   v_mfma_f32_16x16x32_bf16 score it against the G query heads (the B
+//   operand; columns past G are ignored).  P.V then runs on MFMA too: the
+//   weights, in lane 16g + h for rows 4g..4g+3 of head h, are already the B
+//   operand of O^T += V^T P, and the V tile goes through the same LDS area and
+//   comes back transposed (ds_read_b64_tr_b16) as the A operand; each weight
+//   enters as three bf16 terms, so the product keeps it to 2^-23.  Other
+//   cases (float32 caches, 64-dim heads, 8-token blocks): each lane dots its
+//   16-byte chunk against the same chunk of each query head (v_dot2 for bf16
+//   pairs, f32 accumulation), the lanes of a row add up their partial sums
+//   with DPP row rotations, and the V rows are accumulated on the VALU in f32.
+// * Running softmax in log2 units (s*scale*log2 e), so weights are exp2(s - m).
+//   On the VALU path row groups (lanes that see the same rows) keep their own
+//   running state and are merged once per piece with the log-sum-exp rule; on
+//   the MFMA path the four row groups of a head share one base.
 // * The workgroup's units are walked as one stream: a ring of PF+1 register
 //   tiles keeps the next PF tiles in flight while the current one is scored,
 //   across piece boundaries too.  Block-table entries, context lengths and
