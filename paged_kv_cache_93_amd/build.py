@@ -99,5 +99,26 @@ def build(verbose: bool = False, jobs: int | None = None, defines=(), out: str =
     return out
 
 
+def link_c_program(source: str, out: str, lib: str = LIB_PATH) -> str:
+    """Compile a plain C99 program against include/ and link it to libpagedattn.
+
+    This is how a C caller uses the library: the header, the HIP runtime's C
+    API for memory and streams, and ``-lpagedattn`` with an rpath to the
+    library's directory.  Returns ``out``.
+    """
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if not cc:
+        raise RuntimeError("no C compiler found")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    lib_dir = os.path.dirname(os.path.abspath(lib))
+    # relative to the program, so the pair can move together
+    rel = os.path.relpath(lib_dir, os.path.dirname(os.path.abspath(out)))
+    _run([cc, "-std=c99", "-O2", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+          f"-I{INCLUDE}", f"-I{rocm}/include", source, "-o", out,
+          f"-L{lib_dir}", "-lpagedattn", f"-L{rocm}/lib", "-lamdhip64", "-lm",
+          f"-Wl,-rpath,$ORIGIN/{rel}", f"-Wl,-rpath,{rocm}/lib"])
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
