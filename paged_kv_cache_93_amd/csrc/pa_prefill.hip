@@ -219,7 +219,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // Workgroups go to the 8 XCDs round-robin by linear id; renumber them so
   // each XCD takes a contiguous run of (KV head, tile) items - the tiles of one
   // sequence and head then share that XCD's L2.
@@ -331,6 +331,11 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     }
   };
 
+  // A wave whose 32 rows all lie past the tile's last token (a short slice or a
+  // decode row in a 128-row tile) still stages its share of every key tile but
+  // computes nothing.
+  const bool busy = j0 + (wave * 32) / G < j1;
+
   // ---- running state: lane 16g + r owns query row r of each 16-row tile -----
   f32x4 acc[2][8];
   float m[2], lsum[2];
@@ -382,6 +387,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     const u32x4* lk = reinterpret_cast<const u32x4*>(s_mem + buf * kBufBytes);
     const uint8_t* lv = s_mem + buf * kBufBytes + kKBytes;
 
+    if (busy) {
     // S^T = K Q^T for both 16-key halves and both row tiles
     f32x4 s[2][2];
 #pragma unroll
@@ -420,6 +426,7 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
             __builtin_bit_cast(bf16x8, vf), __builtin_bit_cast(bf16x8, pf[rt]), acc[rt][dt], 0,
             0, 0);
     }
+    }  // busy
 
     if (kt + 1 < ntiles) store_tile(buf ^ 1, buf ^ 1);
     __syncthreads();
@@ -539,6 +546,10 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
     for (int mm = 0; mm < 4; ++mm) qf[rt][mm] = qp[4 * mm + grp];
   }
 
+  // a wave with no row before the tile's last token stages its share of every
+  // key tile and computes nothing
+  const bool busy = j0 + (wave * 16 * NRT) / G < j1;
+
   f32x4 acc[NRT][8];
   float m[NRT], lsum[NRT];
 #pragma unroll
@@ -653,6 +664,7 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
     const uint8_t* lk = s_mem + stage * kStageBytes;
     const uint8_t* lv = lk + kKeys * kRowBytes;
 
+    if (busy) {
     // S^T = K Q^T: A = key rows (16h + r16), pieces (4mm + grp) ^ (row % 8)
     f32x4 sc4[NRT][2];
 #pragma unroll
@@ -701,6 +713,7 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
             __builtin_bit_cast(bf16x8, vf), __builtin_bit_cast(bf16x8, pf[rt]), acc[rt][dt], 0,
             0, 0);
     }
+    }  // busy
     stage = stage == kStages - 1 ? 0 : stage + 1;
   }
 
