@@ -15,7 +15,9 @@
 //   meet at no barrier after the preamble; each owns its head end to end and
 //   only publishes its progress, so that the two waves sharing a SIMD keep
 //   pace (the one behind runs at raised issue priority).
-// * Work unit = one (sequence, block).  Three ways to hand units out:
+// * Work unit = one (sequence, block), or on the MFMA path with 8-token
+//   blocks a pair of consecutive blocks (one 16-row tile).  Three ways to
+//   hand units out:
 //   single pass (a workgroup per sequence), fixed partitions (a workgroup per
 //   (sequence, partition), writing split-KV partials), and balanced (a fixed
 //   grid; all units of the batch are split evenly over the workgroups, so a
@@ -23,7 +25,7 @@
 //   ones write the output, pieces write partials merged by merge_kernel).
 // * Rows are loaded in 16-byte chunks with non-temporal loads (the cache is
 //   streamed once); one load instruction covers 1 KiB of contiguous rows.
-// * q.k, bf16 and 8-bit caches with 128-dim heads and blocks of 16 or 32: a
+// * q.k, bf16 and 8-bit caches with 128-dim heads (blocks of 8, 16 or 32): a
 //   16-row K tile goes through LDS into the MFMA A layout and four
 //   v_mfma_f32_16x16x32_bf16 score it against the G query heads (the B
 //   operand; columns past G are ignored).  P.V then runs on MFMA too: the
@@ -31,7 +33,7 @@
 //   operand of O^T += V^T P, and the V tile goes through the same LDS area and
 //   comes back transposed (ds_read_b64_tr_b16) as the A operand; each weight
 //   enters as three bf16 terms, so the product keeps it to 2^-23.  Other
-//   cases (float32 caches, 64-dim heads, 8-token blocks): each lane dots its
+//   cases (float32 caches, 64-dim heads): each lane dots its
 //   16-byte chunk against the same chunk of each query head (v_dot2 for bf16
 //   pairs, f32 accumulation), the lanes of a row add up their partial sums
 //   with DPP row rotations, and the V rows are accumulated on the VALU in f32.
@@ -315,7 +317,7 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 // Scores on the matrix cores: bf16 and 8-bit caches with 128-dim heads and
 // blocks of at least 16 rows (an MFMA tile is 16 rows of one block).
 constexpr bool decode_uses_mfma(int et, int d, int bs) {
-  return PA_MFMA_SCORES && et != kF32 && d == 128 && bs >= 16;
+  return PA_MFMA_SCORES && et != kF32 && d == 128 && bs >= 8;
 }
 
 // LDS bytes each wave of the MFMA path uses: a 16-row K tile padded to 17
@@ -345,11 +347,16 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   constexpr bool MF = decode_uses_mfma(ET, D, BS);   // q.k on MFMA (16-row tiles)
   constexpr int QC = MF ? (16 * G + 63) / 64 : 1;    // query chunks a lane loads per tile
   constexpr int TRW = MF ? 16 : (G >= 8 ? 2 : 4) * RPI;  // wide groups keep smaller tiles
-  constexpr int TR = BS < TRW ? BS : TRW;            // rows per register tile
+  constexpr int TR = MF ? 16 : BS < TRW ? BS : TRW;  // rows per register tile
   constexpr int NI = TR / RPI;                       // load instructions per tile
-  constexpr int TPB = BS / TR;                       // tiles per block
+  // A unit is BPT consecutive blocks of one sequence: one block, or on the
+  // MFMA path with 8-token blocks a pair of them filling one 16-row tile
+  // (rows 0..7 from the first block, 8..15 from the second).
+  constexpr int BPT = TR > BS ? TR / BS : 1;         // blocks per unit
+  constexpr int TPB = BPT > 1 ? 1 : BS / TR;         // tiles per unit
   constexpr int NB = PF + 1;                         // ring buffers
-  static_assert(D % VEC == 0 && 64 % LPR == 0 && TR % RPI == 0 && BS % TR == 0, "tiling");
+  static_assert(D % VEC == 0 && 64 % LPR == 0 && TR % RPI == 0, "tiling");
+  static_assert(BPT == 1 ? BS % TR == 0 : (MF && BPT == 2), "a unit is one block or an MFMA pair");
   static_assert(RPI * D * EB == 64 * LB, "one load instruction covers whole rows");
   static_assert(!BF16 || VEC == 8, "bf16 query chunks hold 8 elements");
   static_assert(!MF || (RPI == 4 && NI == 4 && TR == 16), "MFMA tiles are 16 rows of 4 groups");
@@ -371,13 +378,17 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   if (threadIdx.x < 8) s_prog[threadIdx.x] = 0;
   int fixed_seq = -1;
   int64_t ubeg, uend;
+  // single and partition modes: unit uu starts at block fix_blk0 + BPT * uu and
+  // the walk's blocks end at fix_bend (units are block indices when BPT = 1)
+  int fix_blk0 = 0, fix_bend = 0;
   int64_t total_units = 0, num_groups = 0;
   if (a.mode == kModeBalanced) {
     const int S = a.num_seqs;
     for (int i = threadIdx.x; i < S; i += blockDim.x) {
       int len = a.context_lens[i];
       len = len < 0 ? 0 : (len > max_tokens ? max_tokens : len);
-      s_prefix[i + 1] = (len + BS - 1) / BS - window_first_block(len, a.window, BS);
+      s_prefix[i + 1] =
+          ((len + BS - 1) / BS - window_first_block(len, a.window, BS) + BPT - 1) / BPT;
     }
     if (threadIdx.x == 0) s_prefix[0] = 0;
     __syncthreads();
@@ -416,6 +427,12 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
       ubeg = int64_t(blockIdx.x) * a.partition_blocks;
       uend = min(int64_t(nblk), ubeg + a.partition_blocks);
       if (ubeg >= uend) return;  // whole workgroup, before any barrier
+    }
+    fix_bend = int(uend);
+    if constexpr (BPT > 1) {
+      fix_blk0 = int(ubeg);
+      uend = (uend - ubeg + BPT - 1) / BPT;
+      ubeg = 0;
     }
   }
 
@@ -620,8 +637,10 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   // past the range repeat the range's last unit, so every lane loads and the
   // loads write the window's registers directly; entries and lengths are
   // checked where they are used.
+  // With block pairs (BPT = 2), jk is the pair's first block and ek2 the
+  // second block's entry, or -1 when the walk ends at the first.
   struct Window {
-    int ek, lk, jk, sk;
+    int ek, lk, jk, sk, ek2;
   };
   auto fetch_window = [&](int64_t cbase) {
     const int64_t uu = min(cbase + lane, uend - 1);
@@ -629,17 +648,28 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     if (fixed_seq >= 0) {
       w.sk = fixed_seq;
       w.lk = a.context_lens[w.sk];
-      w.jk = int(uu);
+      w.jk = fix_blk0 + BPT * int(uu);
     } else {
       w.sk = seq_of(uu);
       w.lk = a.context_lens[w.sk];
-      w.jk = int(uu - s_prefix[w.sk]);
+      w.jk = BPT * int(uu - s_prefix[w.sk]);
       if (a.window > 0) {  // only then does the table entry's index wait for the length
         const int len = w.lk < 0 ? 0 : (w.lk > max_tokens ? max_tokens : w.lk);
         w.jk += window_first_block(len, a.window, BS);
       }
     }
-    w.ek = a.block_tables[size_t(w.sk) * a.max_blocks + w.jk];
+    const int32_t* trow = a.block_tables + size_t(w.sk) * a.max_blocks;
+    w.ek = trow[w.jk];
+    w.ek2 = -1;
+    if constexpr (BPT > 1) {
+      // the second block's entry is read only when the walk reaches it
+      int bend = fix_bend;
+      if (fixed_seq < 0) {
+        const int len = w.lk < 0 ? 0 : (w.lk > max_tokens ? max_tokens : w.lk);
+        bend = (len + BS - 1) / BS;
+      }
+      if (w.jk + 1 < bend) w.ek2 = trow[w.jk + 1];
+    }
     return w;
   };
 
@@ -768,16 +798,18 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   int q_loaded = -1;     // sequence of the last query loaded into the ring
   int q_staged = -1;     // sequence whose query rows sit in lds_q
   auto load_tile = [&](Raw(&kr)[NI], Raw(&vr)[NI], u32x4(&qr)[QC], int t) {
-    int phys = -1, sq = 0;
+    int phys = -1, phys2 = -1, sq = 0;
     size_t off = 0;
     if (t < ntiles) {
       const int idx = int(ubeg + t / TPB - cbase);  // < 128: at most PF tiles ahead
       if (idx < 64) {
         phys = __builtin_amdgcn_readlane(w0.ek, idx);
         sq = __builtin_amdgcn_readlane(w0.sk, idx);
+        if constexpr (BPT > 1) phys2 = __builtin_amdgcn_readlane(w0.ek2, idx);
       } else {
         phys = __builtin_amdgcn_readlane(w1.ek, idx - 64);
         sq = __builtin_amdgcn_readlane(w1.sk, idx - 64);
+        if constexpr (BPT > 1) phys2 = __builtin_amdgcn_readlane(w1.ek2, idx - 64);
       }
       off = size_t(t % TPB) * (TR * D * EB);
     }
@@ -802,8 +834,16 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     // so each row group sees 4 consecutive rows, as the MFMA result rows.
     // (Every instruction reads 1 KiB of whole rows; loading K straight in
     // the MFMA operand layout instead - 64-byte pieces of 16 rows - was
-    // measured slower than transposing it through LDS.)
-    const int lo = MF ? r * 64 + c : lane;
+    // measured slower than transposing it through LDS.)  With block pairs,
+    // row groups 2 and 3 read rows 0..7 of the second block.
+    int lo = MF ? r * 64 + c : lane;
+    if constexpr (BPT > 1) {
+      if (phys2 < 0 || int64_t(phys2) >= a.num_blocks) phys2 = 0;
+      if (r >= 2) {
+        off = size_t(phys2) * block_bytes;
+        lo -= 128;
+      }
+    }
     constexpr int step = MF ? 16 : 64;
     const Raw* kp = reinterpret_cast<const Raw*>(kbase + off) + lo;
     const Raw* vp = reinterpret_cast<const Raw*>(vbase + off) + lo;
@@ -821,21 +861,24 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     int len = __builtin_amdgcn_readlane(w0.lk, idx);
     len = len < 0 ? 0 : (len > max_tokens ? max_tokens : len);
     const int tok0 = __builtin_amdgcn_readlane(w0.jk, idx) * BS + (t % TPB) * TR;
-    const int nvalid = (phys < 0 || int64_t(phys) >= a.num_blocks) ? 0 : min(TR, len - tok0);
-    if (nvalid <= 0) return;
+    const bool ok1 = phys >= 0 && int64_t(phys) < a.num_blocks;
+    int nvalid = min(TR, len - tok0);
     // rows before a sliding window (positions < len - W) are masked like the
     // rows past the end
-    const int nskip = a.window > 0 ? max(0, len - a.window - tok0) : 0;
-    const bool partial = nvalid < TR || nskip > 0;
+    int nskip = a.window > 0 ? max(0, len - a.window - tok0) : 0;
+    if constexpr (BPT > 1) {
+      // a pair: a first block outside the pool masks rows 0..7, a missing or
+      // bad second block rows 8..15
+      const int phys2 = __builtin_amdgcn_readlane(w0.ek2, idx);
+      if (!(phys2 >= 0 && int64_t(phys2) < a.num_blocks)) nvalid = min(nvalid, BS);
+      if (!ok1) nskip = max(nskip, BS);
+    } else {
+      if (!ok1) nvalid = 0;
+    }
     if constexpr (MF) {
-      // K tile -> LDS, then read back transposed: lane 16g + t gets row t's
-      // dims [32mm + 8g, 32mm + 8g + 8) as the A operand of MFMA mm, and lane
-      // 16g + h holds the same dims of query head h as B (h < G; the other
-      // lanes repeat a head whose score column is never used).  The first
-      // tile of a sequence brought its query rows (see load_tile): they go
-      // through LDS into the B layout once, and stay in qf after.
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lds_k[(4 * r + i) * 17 + c] = score_chunk<ET>(kr[i]);
+      // The first tile of a sequence brought its query rows (see load_tile):
+      // they go through LDS into the B layout once, and stay in qf after -
+      // also when that tile itself contributes nothing.
       const int tseq = __builtin_amdgcn_readlane(w0.sk, idx);
       if (tseq != q_staged) {
         q_staged = tseq;
@@ -847,6 +890,16 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int mm = 0; mm < 4; ++mm) qf[mm] = lds_q[qh * 16 + 4 * mm + (lane >> 4)];
       }
+    }
+    if (nvalid <= nskip) return;  // every row masked: the state would not change
+    const bool partial = nvalid < TR || nskip > 0;
+    if constexpr (MF) {
+      // K tile -> LDS, then read back transposed: lane 16g + t gets row t's
+      // dims [32mm + 8g, 32mm + 8g + 8) as the A operand of MFMA mm, and lane
+      // 16g + h holds the same dims of query head h as B (h < G; the other
+      // lanes repeat a head whose score column is never used).
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lds_k[(4 * r + i) * 17 + c] = score_chunk<ET>(kr[i]);
       // two independent accumulation chains of two MFMAs each
       f32x4 sc_even = {0.f, 0.f, 0.f, 0.f}, sc_odd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1086,12 +1139,17 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     auto write_row = [&](int sq, int64_t last, uint4 in) {
       const int idx = int(last - cbase);
       int phys, len;
-      if (idx < 64) {
-        phys = __builtin_amdgcn_readlane(w0.ek, idx);
-        len = __builtin_amdgcn_readlane(w0.lk, idx);
-      } else if (idx < 128) {
-        phys = __builtin_amdgcn_readlane(w1.ek, idx - 64);
-        len = __builtin_amdgcn_readlane(w1.lk, idx - 64);
+      if (idx < 128) {
+        const Window& w = idx < 64 ? w0 : w1;
+        const int k = idx & 63;
+        phys = __builtin_amdgcn_readlane(w.ek, k);
+        len = __builtin_amdgcn_readlane(w.lk, k);
+        if constexpr (BPT > 1) {
+          // the token sits in the pair's second block unless the pair ends early
+          const int cl = len < 0 ? 0 : (len > max_tokens ? max_tokens : len);
+          if (cl > 0 && (cl - 1) / BS != __builtin_amdgcn_readlane(w.jk, k))
+            phys = __builtin_amdgcn_readlane(w.ek2, k);
+        }
       } else {  // (scalar results, so no other path waits for these loads)
         len = __builtin_amdgcn_readfirstlane(a.context_lens[sq]);
         const int cl = len < 0 ? 0 : (len > max_tokens ? max_tokens : len);
