@@ -212,7 +212,8 @@ typedef struct pa_attn_variant {
  *   block_tables  DEVICE int32 [num_seqs][max_blocks_per_seq]; entries past
  *                 ceil(L_i / block_size) are not read
  *   context_lens  DEVICE int32 [num_seqs], 0 <= L_i <= max_blocks_per_seq*block_size
- *   num_heads     multiple of num_kv_heads; ratio 1, 2, 4 or 8
+ *   num_heads     multiple of num_kv_heads; ratio G = 1..8, or 16 for a bf16 or
+ *                 8-bit cache with head_dim 128 (other ratios: PA_ERR_UNSUPPORTED)
  *   scale         > 0 and finite (normally 1/sqrt(head_dim))
  *   variant       HOST pa_attn_variant, or NULL for plain attention.  The query
  *                 sits at position p = L_i - 1: a window W keeps t >= L_i - W
@@ -285,7 +286,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t he
  *   query_start   DEVICE int32 [num_seqs + 1], rising from 0 to num_tokens
  *   context_lens  DEVICE int32 [num_seqs], n_i <= L_i <= max_blocks_per_seq*block_size
  *                 (rows before position 0, n_i > L_i, get zeros)
- *   num_heads     ratio to num_kv_heads 1, 2, 4 or 8
+ *   num_heads     ratio G to num_kv_heads 1..8 or 16 (a workgroup tile holds
+ *                 floor(128 / G) tokens)
  *   out           DEVICE [num_tokens][num_heads][128] of out_dtype (PA_F32 or PA_BF16),
  *                 16-byte aligned; rows of sequences with n_i = 0 are not written
  *   variant       HOST pa_attn_variant, or NULL for plain causal attention

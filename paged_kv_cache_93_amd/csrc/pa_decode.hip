@@ -75,15 +75,18 @@ int prepare(const char* fn, const pa_cache* cache, const void* q, const int32_t*
     return fail(PA_ERR_SHAPE, "%s: num_heads (%d) is not a multiple of num_kv_heads (%d)", fn,
                 num_heads, cache->num_kv_heads);
   *group = num_heads / cache->num_kv_heads;
-  if (*group != 1 && *group != 2 && *group != 4 && *group != 8)
-    return fail(PA_ERR_UNSUPPORTED, "%s: query heads per KV head must be 1, 2, 4 or 8 (got %d)",
-                fn, *group);
   if (cache->head_dim != 64 && cache->head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "%s: head_dim must be 64 or 128 (got %d)", fn,
                 cache->head_dim);
   if (cache->block_size != 8 && cache->block_size != 16 && cache->block_size != 32)
     return fail(PA_ERR_UNSUPPORTED, "%s: block_size must be 8, 16 or 32 (got %d)", fn,
                 cache->block_size);
+  if (!decode_group_supported(elem_type(cache->dtype), cache->head_dim, cache->block_size,
+                              *group))
+    return fail(PA_ERR_UNSUPPORTED,
+                "%s: query heads per KV head must be 1..8, or 16 for a bf16 or 8-bit cache "
+                "with head_dim 128 (got %d)",
+                fn, *group);
   if (!(scale > 0.f) || !std::isfinite(scale))
     return fail(PA_ERR_SHAPE, "%s: scale must be positive and finite", fn);
   if (num_seqs > 65535 || cache->num_kv_heads > 65535)

@@ -346,7 +346,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   constexpr int RPI = 64 / LPR;                      // rows per load instruction
   constexpr bool MF = decode_uses_mfma(ET, D, BS);   // q.k on MFMA (16-row tiles)
   constexpr int QC = MF ? (16 * G + 63) / 64 : 1;    // query chunks a lane loads per tile
-  constexpr int TRW = MF ? 16 : (G >= 8 ? 2 : 4) * RPI;  // wide groups keep smaller tiles
+  constexpr int TRW = MF ? 16 : (G > 4 ? 2 : 4) * RPI;   // wide groups keep smaller tiles
   constexpr int TR = MF ? 16 : BS < TRW ? BS : TRW;  // rows per register tile
   constexpr int NI = TR / RPI;                       // load instructions per tile
   // A unit is BPT consecutive blocks of one sequence: one block, or on the
@@ -1349,7 +1349,23 @@ int decode_groups_per_cu_f32(int d, int bs, int g, int waves, size_t lds);
 int decode_groups_per_cu_bf16(int d, int bs, int g, int waves, size_t lds);
 int decode_groups_per_cu_fp8(int d, int bs, int g, int waves, size_t lds);
 
-// Instantiation table: D in {64, 128}, block size in {16, 32}, G in {1, 2, 4, 8}.
+// Query heads per KV head the kernels take: 1..8, and 16 on the MFMA path
+// (whose score tile has 16 head columns).
+constexpr bool decode_group_supported(int et, int d, int bs, int g) {
+  return (g >= 1 && g <= 8) || (g == 16 && decode_uses_mfma(et, d, bs));
+}
+
+// Instantiation table: D in {64, 128}, block size in {8, 16, 32}, G in 1..8,
+// and G = 16 where the MFMA path runs.
+#define PA_DECODE_GROUPS(CASE, D_, BS_)                                                  \
+  CASE(D_, BS_, 1) CASE(D_, BS_, 2) CASE(D_, BS_, 3) CASE(D_, BS_, 4) CASE(D_, BS_, 5)  \
+  CASE(D_, BS_, 6) CASE(D_, BS_, 7) CASE(D_, BS_, 8)                                    \
+  if constexpr (decode_uses_mfma(ET, D_, BS_)) { CASE(D_, BS_, 16) }
+#define PA_DECODE_SHAPES(CASE)                                                           \
+  PA_DECODE_GROUPS(CASE, 64, 8) PA_DECODE_GROUPS(CASE, 64, 16)                          \
+  PA_DECODE_GROUPS(CASE, 64, 32) PA_DECODE_GROUPS(CASE, 128, 8)                         \
+  PA_DECODE_GROUPS(CASE, 128, 16) PA_DECODE_GROUPS(CASE, 128, 32)
+
 template <int ET>
 bool launch_decode_impl(int d, int bs, int g, const DecodeArgs& a, dim3 grid, int waves,
                         size_t lds, hipStream_t s) {
@@ -1360,15 +1376,7 @@ bool launch_decode_impl(int d, int bs, int g, const DecodeArgs& a, dim3 grid, in
         grid, dim3(waves * 64), lds, s, a);                                              \
     return true;                                                                         \
   }
-#define PA_DECODE_G(D_, BS_) \
-  PA_DECODE_CASE(D_, BS_, 1) PA_DECODE_CASE(D_, BS_, 2) PA_DECODE_CASE(D_, BS_, 4) PA_DECODE_CASE(D_, BS_, 8)
-  PA_DECODE_G(64, 8)
-  PA_DECODE_G(64, 16)
-  PA_DECODE_G(64, 32)
-  PA_DECODE_G(128, 8)
-  PA_DECODE_G(128, 16)
-  PA_DECODE_G(128, 32)
-#undef PA_DECODE_G
+  PA_DECODE_SHAPES(PA_DECODE_CASE)
 #undef PA_DECODE_CASE
   return false;
 }
@@ -1389,14 +1397,7 @@ int decode_groups_per_cu_impl(int d, int bs, int g, int waves, size_t lds) {
       n = 0;                                                                                \
     return n;                                                                               \
   }
-#define PA_OCC_G(D_, BS_) PA_OCC_CASE(D_, BS_, 1) PA_OCC_CASE(D_, BS_, 2) PA_OCC_CASE(D_, BS_, 4) PA_OCC_CASE(D_, BS_, 8)
-  PA_OCC_G(64, 8)
-  PA_OCC_G(64, 16)
-  PA_OCC_G(64, 32)
-  PA_OCC_G(128, 8)
-  PA_OCC_G(128, 16)
-  PA_OCC_G(128, 32)
-#undef PA_OCC_G
+  PA_DECODE_SHAPES(PA_OCC_CASE)
 #undef PA_OCC_CASE
   return 0;
 }

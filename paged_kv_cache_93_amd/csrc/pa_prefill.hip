@@ -1,95 +1,10 @@
-// Mixed-batch (prefill) attention over the paged cache, for gfx950.
-//
-// What it computes ("How Paged Attention and Continuous Batching Actually
-// Work", section "Continuous batching: schedule steps, not batches": every
-// scheduled token of the batch flattened into one sequence, metadata saying
-// where each request's tokens begin and end and what they may see;
-// "PagedAttention and continuous batching", section "Attention kernel
-// modification": causal attention of position t over K_{0:t}, V_{0:t} loaded
-// block by block through the table, with a running softmax): sequence i owns
-// query rows query_start[i] .. query_start[i+1]-1, its n_i tokens are its last
-// n_i positions, and token j at position p = L_i - n_i + j attends to
-// positions 0..p.  A decode row is n_i = 1.
-//
-// Mapping onto CDNA4:
-// * A workgroup (4 waves) takes a tile of 128 query rows of one sequence and
-//   one KV head: 128/G tokens times the G query heads that share the KV head,
-//   so every K/V row the tile loads serves all of them.  Each wave owns 32
-//   rows (two 16-row MFMA tiles).
-// * The tile walks its keys 32 at a time (positions 0 .. its last row's
-//   position).  The workgroup stages each 32-key K/V tile in LDS (double
-//   buffered, the next tile's global loads in flight during the current one's
-//   math): K row-major (the MFMA A operand of S^T = K Q^T reads 16-byte row
-//   pieces), V transposed (the A operand of O^T = V^T P^T needs keys
-//   contiguous per dimension).  8-bit codes become bf16 on the way into LDS
-//   (exact; the scales are folded into the score scale and the output).
-// * Scores come out as S^T, so lane 16g + r holds keys 4g..4g+3 (and 16 +
-//   4g..) of query row r: the softmax weights P are already the B operand of
-//   O^T = V^T P^T in that lane (the k order of the two operands is permuted
-//   alike), and the output O^T lands in the lane that owns the row's running
-//   max and sum - no shuffles except two lane swaps for the row maximum.
-// * Weights are rounded to bf16 for the matrix product, and the running sum
-//   adds the rounded weights, so the output is an exact convex combination of
-//   V rows with weights within 2^-9 (relative) of the true ones.
-#include <type_traits>
-
-#include "pa_decode_kernel.h"
-#include "pa_internal.h"
+// pa_prefill: validation, the tile map, and the launch of the attention
+// kernel (pa_prefill_kernel.h) for the cache type.
+#include "pa_prefill_kernel.h"
 
 namespace pa {
+namespace pf {
 namespace {
-
-using namespace dev;
-
-constexpr int kD = 128;           // head dim
-constexpr int kRows = 128;        // query rows per workgroup tile
-constexpr int kWaves = 4;
-constexpr int kKeys = 32;         // keys per K/V tile
-constexpr int kKStride = 17;      // 16-byte chunks per K row in LDS (16 + 1 pad)
-constexpr int kVStride = 36;      // bf16 per transposed V row in LDS (32 + 4 pad)
-constexpr int kKBytes = kKeys * kKStride * 16;
-constexpr int kVBytes = kD * kVStride * 2;
-constexpr int kBufBytes = kKBytes + kVBytes;
-
-#ifndef PA_PREFILL_ROW_TILES
-#define PA_PREFILL_ROW_TILES 2  // 16-row tiles per wave of the LDS-DMA kernel: 2 or 4
-#endif
-
-#ifndef PA_PREFILL_DMA
-#define PA_PREFILL_DMA 1  // 0: bf16 caches take the register-staged kernel too (for comparison)
-#endif
-
-// Key-pair slot swizzle of the transposed V tile: dims 32x..32x+31 XOR their
-// pair slot with 4x (an even number, so the two pairs a fragment read takes
-// stay adjacent).  With 72-byte rows, the transposed writes of a wave (16 dim
-// chunks x 4 key pairs) then land in 64 distinct banks.
-__device__ __forceinline__ int vswz(int dim) { return 4 * ((dim >> 5) & 3); }
-
-constexpr bf16x2 kOnes = {__bf16(1.0f), __bf16(1.0f)};
-
-struct PrefillArgs {
-  const uint8_t* q;
-  const uint8_t* k_pool;
-  const uint8_t* v_pool;
-  const int32_t* block_tables;
-  const int32_t* query_start;
-  const int32_t* context_lens;
-  const int32_t* tiles;  // [0] tile count; then (sequence, tile index) pairs
-  void* out;
-  int64_t num_blocks;
-  int32_t num_seqs;
-  int32_t num_tokens;
-  int32_t num_kv_heads;
-  int32_t num_heads;
-  int32_t max_blocks;
-  int32_t max_tiles;
-  float scale_log2;  // score scale * log2(e), times the K pool's scale (8-bit cache)
-  float v_scale;     // the V pool's scale (8-bit cache), else 1
-  const float* k_scales;  // 8-bit cache with one scale per KV head (then the two above
-  const float* v_scales;  //   leave them out), or NULL
-  int32_t window;    // sliding window in tokens (0: none)
-  const float* alibi;  // ALiBi slope per query head, or NULL
-};
 
 // The tile map: tile t of the grid -> (sequence, tile of that sequence), each
 // sequence's tiles from its last (longest context) to its first.  One
@@ -137,648 +52,6 @@ __global__ void __launch_bounds__(1024) prefill_tiles_kernel(const int32_t* qs, 
   if (tid == 0) tiles[0] = min(running, max_tiles);
 }
 
-// One 32-key tile of the online softmax for a wave's two 16-row tiles: scores
-// (S^T in the MFMA C layout: lane 16g + r holds keys 4g..4g+3 and 16+4g..
-// 16+4g+3 of row r) -> masked, exponentiated weights packed as the B operand
-// of O^T = V^T P^T in the k order [4g .. 4g+3, 16+4g .. 16+4g+3]; the running
-// max, sum and accumulators of the rows are updated.  Only tiles that reach
-// past the workgroup's first position (or, with a window, start before its
-// last row's window) need masks; without ALiBi the max is taken on raw
-// scores (the scale is positive) and the scale enters with the exponent's fma.
-template <bool AL, int NR = 2>
-__device__ __forceinline__ void softmax_step(f32x4 (&s)[NR][2], u32x4 (&pf)[NR], int k0,
-                                             const int (&pos)[NR], const int (&lo_row)[NR],
-                                             const float (&slope2)[NR], int min_pos, int max_pos,
-                                             int W, float sc, int grp, float (&m)[NR],
-                                             float (&lsum)[NR], f32x4 (&acc)[NR][8]) {
-  if constexpr (AL) {
-    // scores to log2 units plus slope * (key - position)
-#pragma unroll
-    for (int rt = 0; rt < NR; ++rt) {
-      const float sd = slope2[rt] * float(k0 + 4 * grp - pos[rt]);
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          s[rt][h][v] = fmaf(s[rt][h][v], sc, fmaf(slope2[rt], float(16 * h + v), sd));
-    }
-  }
-  if (k0 + kKeys - 1 > min_pos || (W > 0 && k0 < max_pos - W + 1)) {
-#pragma unroll
-    for (int rt = 0; rt < NR; ++rt)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int k = k0 + 16 * h + 4 * grp + v;
-          if (k > pos[rt] || k < lo_row[rt]) s[rt][h][v] = kNegInf;
-        }
-  }
-#pragma unroll
-  for (int rt = 0; rt < NR; ++rt) {
-    float mx = fmaxf(fmaxf(fmaxf(s[rt][0][0], s[rt][0][1]), fmaxf(s[rt][0][2], s[rt][0][3])),
-                     fmaxf(fmaxf(s[rt][1][0], s[rt][1][1]), fmaxf(s[rt][1][2], s[rt][1][3])));
-    mx = xor_max<16>(mx);
-    if constexpr (!AL) mx *= sc;
-    // The exponent base moves only when the row maximum passes it by more
-    // than 8 (log2 units): weights stay <= 2^8, the accumulators are
-    // rescaled rarely, and the result is the same softmax.
-    const bool move = mx > m[rt] + 8.f;
-    const float mnew = move ? mx : m[rt];
-    const float base = mnew == kNegInf ? 0.f : mnew;
-    const float alpha = move ? fast_exp2(m[rt] - base) : 1.f;
-    m[rt] = mnew;
-    float psum = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int h = w >> 1, v = 2 * (w & 1);
-      f32x2 pp;
-      if constexpr (AL)
-        pp = f32x2{fast_exp2(s[rt][h][v] - base), fast_exp2(s[rt][h][v + 1] - base)};
-      else
-        pp = f32x2{fast_exp2(fmaf(s[rt][h][v], sc, -base)),
-                   fast_exp2(fmaf(s[rt][h][v + 1], sc, -base))};
-      const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
-      pf[rt][w] = __builtin_bit_cast(uint32_t, pb);
-      psum = __builtin_amdgcn_fdot2_f32_bf16(pb, kOnes, psum, false);  // adds the rounded pair
-    }
-    lsum[rt] = fmaf(lsum[rt], alpha, psum);
-    if (__ballot(move) != 0) {
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) acc[rt][dt] *= alpha;
-    }
-  }
-}
-
-template <int ET, int BS, int G, bool OUT_F32, bool AL>
-__global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
-  constexpr int EB = ET == kFP8 ? 1 : 2;   // K/V element bytes
-  constexpr int TT = kRows / G;            // tokens per tile
-  using Raw = typename LaneChunk<8 * EB>::type;  // 8 elements of a row
-  extern __shared__ __attribute__((aligned(16))) uint8_t s_mem[];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Workgroups go to the 8 XCDs round-robin by linear id; renumber them so
-  // each XCD takes a contiguous run of (KV head, tile) items - the tiles of one
-  // sequence and head then share that XCD's L2.
-  const int nwg = gridDim.x * gridDim.y;
-  const int id = blockIdx.y * gridDim.x + blockIdx.x;
-  const int xcd = id % 8, slot = id / 8;
-  const int logical = xcd * (nwg / 8) + min(xcd, nwg % 8) + slot;
-  const int t = logical % gridDim.x;
-  const int g = logical / gridDim.x;
-  const float sl2 = a.k_scales ? a.scale_log2 * a.k_scales[g] : a.scale_log2;
-  const float vsc = a.v_scales ? a.v_scales[g] : a.v_scale;
-  if (t >= a.tiles[0]) return;
-  const int seq = a.tiles[1 + 2 * t];
-  const int tile = a.tiles[2 + 2 * t];
-  if (seq < 0 || seq >= a.num_seqs) return;
-
-  const int32_t qs0 = min(max(a.query_start[seq], 0), a.num_tokens);
-  const int32_t qs1 = min(max(a.query_start[seq + 1], 0), a.num_tokens);
-  const int32_t n = qs1 - qs0;
-  const int32_t max_len = a.max_blocks * BS;
-  const int32_t L = min(max(a.context_lens[seq], 0), max_len);
-  const int32_t c = L - n;  // position of query token 0 (negative: caller error)
-  const int32_t j0 = tile * TT;
-  const int32_t j1 = min(j0 + TT, n);
-  if (j1 <= j0) return;
-  const int32_t kend = c + j1;  // keys 0 .. kend-1 are needed (kend <= L)
-  const int32_t* table = a.block_tables + int64_t(seq) * a.max_blocks;
-
-  // ---- this lane's query rows and their fragments (B operand of S^T) --------
-  const int r16 = lane & 15, grp = lane >> 4;
-  int pos[2];
-  bool valid[2];
-  int64_t row_index[2];  // output row (token * Hq + head)
-  u32x4 qf[2][4];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int row = wave * 32 + rt * 16 + r16;
-    const int tok = j0 + row / G;
-    valid[rt] = tok < j1;
-    const int tq = min(tok, j1 - 1);
-    pos[rt] = c + tok;
-    const int head = g * G + row % G;
-    row_index[rt] = int64_t(qs0 + tq) * a.num_heads + head;
-    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + row_index[rt] * kD * 2);
-#pragma unroll
-    for (int mm = 0; mm < 4; ++mm) qf[rt][mm] = qp[4 * mm + grp];
-  }
-
-  // ---- K/V tile staging -------------------------------------------------------
-  // Thread tid loads dims [8*dc, 8*dc+8) of keys 2kp and 2kp+1 of a tile (one
-  // block: block sizes are even).  Loads run two tiles ahead of the math (two
-  // register sets), block-table entries three tiles ahead.
-  const int dc = tid & 15, kp = tid >> 4;
-  Raw kr[2][2], vr[2][2];
-  // key 2kp of a tile sits at row (2kp) % BS of its block (tiles start at
-  // multiples of 32, a multiple of BS), so a lane's offset inside a block is fixed
-  constexpr int kRowBytes = kD * EB;
-  const int64_t blk_stride = int64_t(a.num_kv_heads) * BS * kRowBytes;
-  const int64_t lane_off = (int64_t(g) * BS + (2 * kp) % BS) * kRowBytes + dc * 8 * EB;
-  auto table_entry = [&](int k0) -> int {
-    const int key = k0 + 2 * kp;
-    return key < kend ? table[key / BS] : -1;
-  };
-  auto load_tile = [&](int set, int k0, int phys) {
-    const bool ok = phys >= 0 && int64_t(phys) < a.num_blocks;
-    if (k0 + kKeys <= kend && __ballot(!ok) == 0) {
-      // whole tile inside the context, every block in the pool: no conditions
-      const uint8_t* kb = a.k_pool + int64_t(phys) * blk_stride + lane_off;
-      const uint8_t* vb = a.v_pool + int64_t(phys) * blk_stride + lane_off;
-      kr[set][0] = *reinterpret_cast<const Raw*>(kb);
-      kr[set][1] = *reinterpret_cast<const Raw*>(kb + kRowBytes);
-      vr[set][0] = *reinterpret_cast<const Raw*>(vb);
-      vr[set][1] = *reinterpret_cast<const Raw*>(vb + kRowBytes);
-      return;
-    }
-    // the context's last tile, or a block id outside the pool: those rows are zero
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int key = k0 + 2 * kp + e;
-      kr[set][e] = Raw{};
-      vr[set][e] = Raw{};
-      if (key < kend && ok) {
-        const int64_t off = int64_t(phys) * blk_stride + lane_off + e * kRowBytes;
-        kr[set][e] = *reinterpret_cast<const Raw*>(a.k_pool + off);
-        vr[set][e] = *reinterpret_cast<const Raw*>(a.v_pool + off);
-      }
-    }
-  };
-  auto store_tile = [&](int set, int buf) {
-    u32x4* lk = reinterpret_cast<u32x4*>(s_mem + buf * kBufBytes);
-    uint32_t* lv = reinterpret_cast<uint32_t*>(s_mem + buf * kBufBytes + kKBytes);
-    u32x4 kb[2], vb[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      kb[e] = score_chunk<ET>(kr[set][e]);
-      vb[e] = score_chunk<ET>(vr[set][e]);
-      lk[(2 * kp + e) * kKStride + dc] = kb[e];
-    }
-    // V transposed: dim 8dc + x gets the pair (key 2kp, key 2kp+1) as one word,
-    // at pair slot kp ^ vswz(dim) (a wave's 64 writes hit 64 distinct banks)
-    const int kps = kp ^ vswz(8 * dc);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t a0 = vb[0][w], a1 = vb[1][w];  // dims 8dc+2w, 8dc+2w+1 of each key
-      // low halves of both words, then high halves (v_perm byte selects)
-      lv[((8 * dc + 2 * w) * kVStride) / 2 + kps] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-      lv[((8 * dc + 2 * w + 1) * kVStride) / 2 + kps] =
-          __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-    }
-  };
-
-  // A wave whose 32 rows all lie past the tile's last token (a short slice or a
-  // decode row in a 128-row tile) still stages its share of every key tile but
-  // computes nothing.
-  const bool busy = j0 + (wave * 32) / G < j1;
-
-  // ---- running state: lane 16g + r owns query row r of each 16-row tile -----
-  f32x4 acc[2][8];
-  float m[2], lsum[2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    m[rt] = kNegInf;
-    lsum[rt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  const int min_pos = c + j0;
-  const int max_pos = kend - 1;
-  const int ntiles = kend > 0 ? (kend + kKeys - 1) / kKeys : 0;
-  // Sliding window: a row at position p sees p-W+1 .. p, so the walk starts at
-  // the tile holding the earliest key any row of this tile sees.
-  const int W = a.window;
-  const int kt0 = W > 0 ? max(0, min_pos - W + 1) / kKeys : 0;
-  int lo_row[2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) lo_row[rt] = W > 0 ? pos[rt] - W + 1 : INT32_MIN;
-  // ALiBi: slope * log2(e) of each row's query head (the scores are in log2 units)
-  float slope2[2] = {0.f, 0.f};
-  if constexpr (AL) {
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int row = wave * 32 + rt * 16 + r16;
-      slope2[rt] = a.alibi[g * G + row % G] * 1.4426950408889634f;
-    }
-  }
-
-  // prologue: tile kt0 in LDS, tile kt0+1 in flight, the table entry of kt0+2 in flight
-  int next_phys = -1;
-  if (ntiles > kt0) {
-    load_tile(0, kt0 * kKeys, table_entry(kt0 * kKeys));
-    if (ntiles > kt0 + 1) load_tile(1, (kt0 + 1) * kKeys, table_entry((kt0 + 1) * kKeys));
-    if (ntiles > kt0 + 2) next_phys = table_entry((kt0 + 2) * kKeys);
-    store_tile(0, 0);
-  }
-  __syncthreads();
-  // one key tile; BUF (= (kt - kt0) & 1) is a constant, so every register set is static
-  auto iteration = [&](int kt, auto buf_c) {
-    constexpr int buf = decltype(buf_c)::value;
-    const int k0 = kt * kKeys;
-    // tile kt+2 into the register set tile kt used (it is in LDS already)
-    if (kt + 2 < ntiles) {
-      load_tile(buf, k0 + 2 * kKeys, next_phys);
-      if (kt + 3 < ntiles) next_phys = table_entry(k0 + 3 * kKeys);
-    }
-    const u32x4* lk = reinterpret_cast<const u32x4*>(s_mem + buf * kBufBytes);
-    const uint8_t* lv = s_mem + buf * kBufBytes + kKBytes;
-
-    if (busy) {
-    // S^T = K Q^T for both 16-key halves and both row tiles
-    f32x4 s[2][2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) s[rt][h] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
-        const u32x4 kf = lk[(16 * h + r16) * kKStride + 4 * mm + grp];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-          s[rt][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, kf), __builtin_bit_cast(bf16x8, qf[rt][mm]), s[rt][h],
-              0, 0, 0);
-      }
-    }
-
-    u32x4 pf[2];
-    softmax_step<AL>(s, pf, k0, pos, lo_row, slope2, min_pos, max_pos, W, sl2, grp, m,
-                     lsum, acc);
-
-    // O^T += V^T P^T: A = dims 16dt + r, keys in the permuted k order
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int dim = 16 * dt + r16;
-      const uint8_t* row = lv + dim * kVStride * 2;
-      const int sw = vswz(dim);
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(row + 4 * ((2 * grp) ^ sw));
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 4 * ((8 + 2 * grp) ^ sw));
-      const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-        acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, vf), __builtin_bit_cast(bf16x8, pf[rt]), acc[rt][dt], 0,
-            0, 0);
-    }
-    }  // busy
-
-    if (kt + 1 < ntiles) store_tile(buf ^ 1, buf ^ 1);
-    __syncthreads();
-  };
-  for (int kt = kt0; kt < ntiles; kt += 2) {
-    iteration(kt, std::integral_constant<int, 0>{});
-    if (kt + 1 < ntiles) iteration(kt + 1, std::integral_constant<int, 1>{});
-  }
-
-  // ---- finalise: lane 16g + r holds dims 16dt + 4g + v of row r -------------
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const float l = xor_sum<16>(lsum[rt]);
-    const float inv = l > 0.f ? vsc / l : 0.f;
-    if (!valid[rt]) continue;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int d0 = 16 * dt + 4 * grp;
-      const f32x4 o = acc[rt][dt] * inv;
-      if constexpr (OUT_F32) {
-        float* dst = static_cast<float*>(a.out) + row_index[rt] * kD + d0;
-        *reinterpret_cast<f32x4*>(dst) = o;
-      } else {
-        uint16_t* dst = static_cast<uint16_t*>(a.out) + row_index[rt] * kD + d0;
-        const bf16x2 lo = __builtin_convertvector((f32x2{o[0], o[1]}), bf16x2);
-        const bf16x2 hi = __builtin_convertvector((f32x2{o[2], o[3]}), bf16x2);
-        const u32x2 w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-        *reinterpret_cast<u32x2*>(dst) = w;
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// bf16 caches: K/V tiles go from the pool straight into LDS
-// ---------------------------------------------------------------------------
-//
-// gfx950's LDS DMA (global_load_lds_dwordx4: lane l's 16 bytes land at the
-// instruction's LDS base + 16 l) fills a ring of kStages 32-key stages, each
-// a K tile and a V tile of 32 rows x 256 bytes, row-major as in the pool.
-// No registers hold tiles in flight and no VALU repacks them.  A lane picks
-// which 16-byte piece of its row it fetches, so the pieces are stored with an
-// XOR swizzle: K rows at piece c ^ (row % 8) (the 8 rows an 8-lane read phase
-// touches fall in 8 distinct bank groups), V rows at piece c ^ 2(row % 4).
-// The V^T operand of O^T = V^T P^T comes from ds_read_b64_tr_b16: within a
-// 16-lane group, lane s addresses 4 dims of key row 4g + s/4 and lane i gets
-// dim i of the 4 rows the group addressed - 4 keys of one dimension, in the
-// k order the P^T operand already has.  V rows past the context (or of a block
-// id outside the pool) are zeroed in LDS before the tile is used, so that a
-// zero weight never meets a NaN.
-
-constexpr int kStages = 3;
-constexpr int kStageBytes = 2 * kKeys * kD * 2;  // K and V tiles, 16 KiB
-
-typedef short v4s __attribute__((ext_vector_type(4)));
-#define PA_LDS(T) __attribute__((address_space(3))) T
-
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm() {
-  // s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding; expcnt left at its maximum)
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
-}
-
-template <int BS, int G, bool OUT_F32, bool AL, int NRT>
-__global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
-    prefill_dma_kernel(PrefillArgs a) {
-  constexpr int TT = kRows / G;  // tokens per tile
-  constexpr int NW = 8 / NRT;    // waves; each owns 16 NRT query rows
-  static_assert(NRT == 2 || NRT == 4, "16-row tiles per wave");
-  extern __shared__ __attribute__((aligned(1024))) uint8_t s_mem[];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nwg = gridDim.x * gridDim.y;
-  const int id = blockIdx.y * gridDim.x + blockIdx.x;
-  const int xcd = id % 8, slot = id / 8;
-  const int logical = xcd * (nwg / 8) + min(xcd, nwg % 8) + slot;
-  const int t = logical % gridDim.x;
-  const int g = logical / gridDim.x;
-  const float sl2 = a.k_scales ? a.scale_log2 * a.k_scales[g] : a.scale_log2;
-  const float vsc = a.v_scales ? a.v_scales[g] : a.v_scale;
-  if (t >= a.tiles[0]) return;
-  const int seq = a.tiles[1 + 2 * t];
-  const int tile = a.tiles[2 + 2 * t];
-  if (seq < 0 || seq >= a.num_seqs) return;
-
-  const int32_t qs0 = min(max(a.query_start[seq], 0), a.num_tokens);
-  const int32_t qs1 = min(max(a.query_start[seq + 1], 0), a.num_tokens);
-  const int32_t n = qs1 - qs0;
-  const int32_t max_len = a.max_blocks * BS;
-  const int32_t L = min(max(a.context_lens[seq], 0), max_len);
-  const int32_t c = L - n;
-  const int32_t j0 = tile * TT;
-  const int32_t j1 = min(j0 + TT, n);
-  if (j1 <= j0) return;
-  const int32_t kend = c + j1;
-  const int32_t* table = a.block_tables + int64_t(seq) * a.max_blocks;
-
-  const int r16 = lane & 15, grp = lane >> 4;
-  int pos[NRT];
-  bool valid[NRT];
-  int64_t row_index[NRT];
-  u32x4 qf[NRT][4];
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    const int row = wave * 16 * NRT + rt * 16 + r16;
-    const int tok = j0 + row / G;
-    valid[rt] = tok < j1;
-    const int tq = min(tok, j1 - 1);
-    pos[rt] = c + tok;
-    const int head = g * G + row % G;
-    row_index[rt] = int64_t(qs0 + tq) * a.num_heads + head;
-    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + row_index[rt] * kD * 2);
-#pragma unroll
-    for (int mm = 0; mm < 4; ++mm) qf[rt][mm] = qp[4 * mm + grp];
-  }
-
-  // a wave with no row before the tile's last token stages its share of every
-  // key tile and computes nothing
-  const bool busy = j0 + (wave * 16 * NRT) / G < j1;
-
-  f32x4 acc[NRT][8];
-  float m[NRT], lsum[NRT];
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    m[rt] = kNegInf;
-    lsum[rt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  const int min_pos = c + j0;
-  const int max_pos = kend - 1;
-  const int ntiles = kend > 0 ? (kend + kKeys - 1) / kKeys : 0;
-  const int W = a.window;
-  const int kt0 = W > 0 ? max(0, min_pos - W + 1) / kKeys : 0;
-  int lo_row[NRT];
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) lo_row[rt] = W > 0 ? pos[rt] - W + 1 : INT32_MIN;
-  float slope2[NRT] = {};
-  if constexpr (AL) {
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      const int row = wave * 16 * NRT + rt * 16 + r16;
-      slope2[rt] = a.alibi[g * G + row % G] * 1.4426950408889634f;
-    }
-  }
-
-  // ---- the DMA side ---------------------------------------------------------
-  constexpr int kRowBytes = kD * 2;
-  const int64_t blk_stride = int64_t(a.num_kv_heads) * BS * kRowBytes;
-  const int64_t head_off = int64_t(g) * BS * kRowBytes;
-  const int rr = lane >> 4, piece = lane & 15;  // row within a 4-row group, LDS piece
-  // Wave w moves rows 4NRT w .. 4NRT (w+1) - 1 of both tiles: NRT 4-row groups,
-  // each one DMA instruction (1 KiB) per tensor - 2 NRT instructions per wave
-  // per tile.
-  auto issue = [&](int kt, int stage) {
-    const int k0 = kt * kKeys;
-#pragma unroll
-    for (int i = 0; i < NRT; ++i) {
-      const int r0 = 4 * NRT * wave + 4 * i;  // first row of the group (wave-uniform)
-      // rows past the context read the context's last aligned group instead
-      // (in bounds; their V rows are zeroed before use)
-      const int key0 = __builtin_amdgcn_readfirstlane(min(k0 + r0, (kend - 1) & ~3));
-      int phys = __builtin_amdgcn_readfirstlane(table[key0 / BS]);
-      if (phys < 0 || int64_t(phys) >= a.num_blocks) phys = 0;
-      const int row = r0 + rr;
-      const int64_t base = int64_t(phys) * blk_stride + head_off + int64_t(key0 % BS + rr) * kRowBytes;
-      const uint8_t* kp = a.k_pool + base + ((piece ^ (row & 7)) << 4);
-      const uint8_t* vp = a.v_pool + base + ((piece ^ (2 * (row & 3))) << 4);
-      uint8_t* lk = s_mem + stage * kStageBytes + r0 * kRowBytes;
-      uint8_t* lv = lk + kKeys * kRowBytes;
-      __builtin_amdgcn_global_load_lds(kp, (PA_LDS(void)*)lk, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vp, (PA_LDS(void)*)lv, 16, 0, 0);
-    }
-  };
-  // V rows that must read as zero: past the context, or in a block outside the pool
-  auto fix_needed = [&](int kt) -> bool {
-    const int k0 = kt * kKeys;
-    if (k0 + kKeys > kend) return true;
-    bool bad = false;
-#pragma unroll
-    for (int b = 0; b < kKeys / BS; ++b) {
-      const int phys = __builtin_amdgcn_readfirstlane(table[k0 / BS + b]);
-      bad |= phys < 0 || int64_t(phys) >= a.num_blocks;
-    }
-    return bad;
-  };
-  auto fix = [&](int kt, int stage) {
-    const int k0 = kt * kKeys;
-    constexpr int PPT = 512 / (64 * NW);        // 16-byte pieces per thread (32 rows x 16)
-    const int row = tid / (16 / PPT);
-    const int key = k0 + row;
-    bool zero = key >= kend;
-    if (!zero) {
-      const int phys = table[key / BS];
-      zero = phys < 0 || int64_t(phys) >= a.num_blocks;
-    }
-    if (zero) {
-      u32x4* dst = reinterpret_cast<u32x4*>(s_mem + stage * kStageBytes + kKeys * kRowBytes +
-                                            row * kRowBytes) + PPT * (tid % (16 / PPT));
-#pragma unroll
-      for (int e = 0; e < PPT; ++e) dst[e] = u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-
-  // prologue: kStages-1 tiles in flight
-#pragma unroll
-  for (int p = 0; p < kStages - 1; ++p)
-    if (kt0 + p < ntiles) issue(kt0 + p, p);
-
-  int stage = 0;
-  for (int kt = kt0; kt < ntiles; ++kt) {
-    // this wave's DMAs of tile kt have landed once at most 2 NRT per later tile remain
-    const int later = min(kStages - 2, ntiles - 1 - kt);
-    if (later >= 1)
-      wait_vm_lgkm<2 * NRT>();
-    else
-      wait_vm_lgkm<0>();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (fix_needed(kt)) {
-      fix(kt, stage);
-      wait_vm_lgkm<63>();  // lgkmcnt(0): the zeros are written before the barrier
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    }
-    // the stage tile kt-1 used is free: refill it with tile kt+kStages-1
-    if (kt + kStages - 1 < ntiles) {
-      const int free_stage = stage == 0 ? kStages - 1 : stage - 1;
-      issue(kt + kStages - 1, free_stage);
-    }
-    const int k0 = kt * kKeys;
-    const uint8_t* lk = s_mem + stage * kStageBytes;
-    const uint8_t* lv = lk + kKeys * kRowBytes;
-
-    if (busy) {
-    // S^T = K Q^T: A = key rows (16h + r16), pieces (4mm + grp) ^ (row % 8)
-    f32x4 sc4[NRT][2];
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) sc4[rt][h] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int row = 16 * h + r16;
-#pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(
-            lk + row * kRowBytes + (((4 * mm + grp) ^ (row & 7)) << 4));
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt)
-          sc4[rt][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, kf), __builtin_bit_cast(bf16x8, qf[rt][mm]),
-              sc4[rt][h], 0, 0, 0);
-      }
-    }
-
-    u32x4 pf[NRT];
-    softmax_step<AL, NRT>(sc4, pf, k0, pos, lo_row, slope2, min_pos, max_pos, W, sl2,
-                          grp, m, lsum, acc);
-
-    // O^T += V^T P^T: two transposed reads give keys 4g..4g+3 and 16+4g..16+4g+3
-    // of dim 16dt + (lane % 16)
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      v4s half[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int row = 16 * hh + 4 * grp + (r16 >> 2);
-        const int lc = 2 * dt + ((r16 & 3) >> 1);            // logical 16-byte piece
-        const int off = row * kRowBytes + ((lc ^ (2 * (row & 3))) << 4) + ((r16 & 1) << 3);
-        half[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (PA_LDS(v4s)*)((PA_LDS(uint8_t)*)lv + off));
-      }
-      const u32x4 vf = {__builtin_bit_cast(uint32_t, __builtin_shufflevector(half[0], half[0], 0, 1)),
-                        __builtin_bit_cast(uint32_t, __builtin_shufflevector(half[0], half[0], 2, 3)),
-                        __builtin_bit_cast(uint32_t, __builtin_shufflevector(half[1], half[1], 0, 1)),
-                        __builtin_bit_cast(uint32_t, __builtin_shufflevector(half[1], half[1], 2, 3))};
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
-        acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, vf), __builtin_bit_cast(bf16x8, pf[rt]), acc[rt][dt], 0,
-            0, 0);
-    }
-    }  // busy
-    stage = stage == kStages - 1 ? 0 : stage + 1;
-  }
-
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    const float l = xor_sum<16>(lsum[rt]);
-    const float inv = l > 0.f ? vsc / l : 0.f;
-    if (!valid[rt]) continue;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int d0 = 16 * dt + 4 * grp;
-      const f32x4 o = acc[rt][dt] * inv;
-      if constexpr (OUT_F32) {
-        float* dst = static_cast<float*>(a.out) + row_index[rt] * kD + d0;
-        *reinterpret_cast<f32x4*>(dst) = o;
-      } else {
-        uint16_t* dst = static_cast<uint16_t*>(a.out) + row_index[rt] * kD + d0;
-        const bf16x2 lo = __builtin_convertvector((f32x2{o[0], o[1]}), bf16x2);
-        const bf16x2 hi = __builtin_convertvector((f32x2{o[2], o[3]}), bf16x2);
-        const u32x2 w = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-        *reinterpret_cast<u32x2*>(dst) = w;
-      }
-    }
-  }
-}
-
-template <int ET, int BS, int G>
-int launch_g(const PrefillArgs& a, bool out_f32, dim3 grid, hipStream_t stream) {
-  const bool al = a.alibi != nullptr;
-  if constexpr (ET == kBF16 && PA_PREFILL_DMA) {
-    constexpr int NRT = PA_PREFILL_ROW_TILES;
-    const size_t lds = size_t(kStages) * kStageBytes;
-    const dim3 block(64 * (8 / NRT));
-    if (out_f32 && al)
-      hipLaunchKernelGGL((prefill_dma_kernel<BS, G, true, true, NRT>), grid, block, lds, stream, a);
-    else if (out_f32)
-      hipLaunchKernelGGL((prefill_dma_kernel<BS, G, true, false, NRT>), grid, block, lds, stream, a);
-    else if (al)
-      hipLaunchKernelGGL((prefill_dma_kernel<BS, G, false, true, NRT>), grid, block, lds, stream, a);
-    else
-      hipLaunchKernelGGL((prefill_dma_kernel<BS, G, false, false, NRT>), grid, block, lds, stream, a);
-    return launch_result("pa_prefill");
-  }
-  const size_t lds = 2 * kBufBytes;
-  if (out_f32 && al)
-    hipLaunchKernelGGL((prefill_kernel<ET, BS, G, true, true>), grid, dim3(256), lds, stream, a);
-  else if (out_f32)
-    hipLaunchKernelGGL((prefill_kernel<ET, BS, G, true, false>), grid, dim3(256), lds, stream, a);
-  else if (al)
-    hipLaunchKernelGGL((prefill_kernel<ET, BS, G, false, true>), grid, dim3(256), lds, stream, a);
-  else
-    hipLaunchKernelGGL((prefill_kernel<ET, BS, G, false, false>), grid, dim3(256), lds, stream, a);
-  return launch_result("pa_prefill");
-}
-
-template <int ET, int BS>
-int launch_bs(const PrefillArgs& a, int group, bool out_f32, dim3 grid, hipStream_t stream) {
-  switch (group) {
-    case 1: return launch_g<ET, BS, 1>(a, out_f32, grid, stream);
-    case 2: return launch_g<ET, BS, 2>(a, out_f32, grid, stream);
-    case 4: return launch_g<ET, BS, 4>(a, out_f32, grid, stream);
-    default: return launch_g<ET, BS, 8>(a, out_f32, grid, stream);
-  }
-}
-
 int32_t tokens_per_tile(int32_t group) { return kRows / group; }
 
 int64_t max_tiles_for(int32_t num_seqs, int32_t num_tokens, int32_t group) {
@@ -787,6 +60,7 @@ int64_t max_tiles_for(int32_t num_seqs, int32_t num_tokens, int32_t group) {
 }
 
 }  // namespace
+}  // namespace pf
 }  // namespace pa
 
 PA_API size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
@@ -795,8 +69,8 @@ PA_API size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_tokens, i
       num_heads % num_kv_heads != 0)
     return 0;
   const int32_t group = num_heads / num_kv_heads;
-  if (group != 1 && group != 2 && group != 4 && group != 8) return 0;
-  return size_t(1 + 2 * pa::max_tiles_for(num_seqs, num_tokens, group)) * sizeof(int32_t);
+  if (!pa::pf::prefill_group_supported(group)) return 0;
+  return size_t(1 + 2 * pa::pf::max_tiles_for(num_seqs, num_tokens, group)) * sizeof(int32_t);
 }
 
 PA_API int pa_prefill(const pa_cache* cache, const void* q, const int32_t* block_tables,
@@ -805,6 +79,7 @@ PA_API int pa_prefill(const pa_cache* cache, const void* q, const int32_t* block
                       float scale, const pa_attn_variant* variant, void* out,
                       int32_t out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   using namespace pa;
+  using namespace pa::pf;
   if (int st = check_cache(cache, "pa_prefill")) return st;
   const int32_t window = variant ? variant->sliding_window : 0;
   const float* alibi = variant ? variant->alibi_slopes : nullptr;
@@ -822,8 +97,8 @@ PA_API int pa_prefill(const pa_cache* cache, const void* q, const int32_t* block
   if (num_heads % cache->num_kv_heads != 0)
     return fail(PA_ERR_SHAPE, "pa_prefill: num_heads must be a multiple of num_kv_heads");
   const int32_t group = num_heads / cache->num_kv_heads;
-  if (group != 1 && group != 2 && group != 4 && group != 8)
-    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: heads per KV head must be 1, 2, 4 or 8");
+  if (!prefill_group_supported(group))
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: heads per KV head must be 1..8 or 16");
   if (!(scale > 0.f) || !(scale < 3.4e38f))
     return fail(PA_ERR_SHAPE, "pa_prefill: scale must be positive and finite");
   if (out_dtype != PA_F32 && out_dtype != PA_BF16)
@@ -879,12 +154,6 @@ PA_API int pa_prefill(const pa_cache* cache, const void* q, const int32_t* block
   a.alibi = alibi;
   const dim3 grid(unsigned(max_tiles), unsigned(cache->num_kv_heads));
   const bool f32 = out_dtype == PA_F32;
-  switch (cache->block_size) {
-    case 8: return fp8 ? launch_bs<kFP8, 8>(a, group, f32, grid, s)
-                       : launch_bs<kBF16, 8>(a, group, f32, grid, s);
-    case 16: return fp8 ? launch_bs<kFP8, 16>(a, group, f32, grid, s)
-                        : launch_bs<kBF16, 16>(a, group, f32, grid, s);
-    default: return fp8 ? launch_bs<kFP8, 32>(a, group, f32, grid, s)
-                        : launch_bs<kBF16, 32>(a, group, f32, grid, s);
-  }
+  return fp8 ? launch_prefill_fp8(a, cache->block_size, group, f32, grid, s)
+             : launch_prefill_bf16(a, cache->block_size, group, f32, grid, s);
 }

@@ -146,7 +146,10 @@ def _partitions(cache, **kw):
     (dict(block_size=4), {}, 3),
     (dict(k_pool=8), {}, 2),                       # misaligned pool
     ({}, dict(num_heads=3), 2),                    # not a multiple of num_kv_heads
-    ({}, dict(num_heads=32), 3),                   # 16 query heads per KV head
+    ({}, dict(num_heads=18), 3),                   # 9 query heads per KV head
+    ({}, dict(num_heads=64), 3),                   # 32 query heads per KV head
+    (dict(dtype=lib.PA_F32), dict(num_heads=32, out_dtype=lib.PA_F32), 3),  # 16: MFMA path only
+    (dict(head_dim=64), dict(num_heads=32), 3),    # 16 with 64-dim heads
     ({}, dict(scale=0.0), 2),
     ({}, dict(scale=float("inf")), 2),
     ({}, dict(num_seqs=-1), 2),
@@ -268,7 +271,9 @@ def test_prefill_workspace_bytes():
     # 1 count + 2 ints per tile; tiles <= ceil(tokens / (128 / G)) + sequences
     assert lib.prefill_workspace_bytes(3, 100, 8, 2) == 4 * (1 + 2 * (math.ceil(100 / 32) + 3))
     assert lib.prefill_workspace_bytes(3, 100, 8, 3) == 0       # not a multiple
-    assert lib.prefill_workspace_bytes(3, 100, 48, 3) == 0      # ratio 16
+    assert lib.prefill_workspace_bytes(3, 100, 48, 3) == 4 * (1 + 2 * (math.ceil(100 / 8) + 3))
+    assert lib.prefill_workspace_bytes(3, 100, 6, 2) == 4 * (1 + 2 * (math.ceil(100 / 42) + 3))
+    assert lib.prefill_workspace_bytes(3, 100, 36, 3) == 0      # ratio 12
     assert lib.prefill_workspace_bytes(-1, 100, 8, 2) == 0
 
 
@@ -284,7 +289,9 @@ def test_prefill_rejects_bad_arguments():
     assert pf(cache=_cache(dtype=lib.PA_F32, head_dim=128, block_size=16, num_kv_heads=2)) == 3
     assert pf(cache=_cache(dtype=lib.PA_BF16, head_dim=64, block_size=16, num_kv_heads=2)) == 3
     assert pf(cache=_cache(dtype=lib.PA_BF16, head_dim=128, block_size=4, num_kv_heads=2)) == 3
-    assert pf(H=6) == 3          # ratio 3
+    assert pf(H=18) == 3         # ratio 9
+    assert pf(H=24) == 3         # ratio 12
+    assert pf(H=64) == 3         # ratio 32
     assert pf(H=7) == 2          # not a multiple
     assert pf(scale=0.0) == 2
     assert pf(od=7) == 3

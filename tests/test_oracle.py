@@ -163,7 +163,7 @@ def test_decode_matches_torch_sdpa(seed):
     rng = np.random.default_rng(1000 + seed)
     num_seqs = int(rng.integers(1, 4))
     hkv = int(rng.choice([1, 2, 3]))
-    group = int(rng.choice([1, 2, 4]))
+    group = int(rng.choice([1, 2, 3, 4, 5, 7, 16]))
     d = int(rng.choice([4, 8, 16, 64]))
     bs = int(rng.choice([1, 2, 4, 16]))
     lens = [int(x) for x in rng.integers(1, 41, size=num_seqs)]
