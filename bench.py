@@ -19,6 +19,9 @@ model's layers each read their own cache once per step.
 Two timed regions, each bracketed by HIP events on the launch stream with no
 event inside: ``--steps`` whole steps (``value``, ``ms_per_step``), then
 ``--steps`` decode launches back to back (``decode_us`` and the roofline).
+Each timed region follows at least ``--warmup`` untimed calls of what it
+times, and at least WARM_SECONDS of them: the GPU's clocks ramp up over the
+first milliseconds of work, which a handful of 60-90 us steps does not cover.
 
 Prints one JSON line.  ``value`` is the KV bytes the step's decode must read
 divided by the step time (GB/s).
@@ -281,8 +284,7 @@ def bench_swap(args) -> dict:
     res = {}
     for name, fn in (("swap_out", swap_out), ("swap_in", swap_in), ("bulk_out", bulk_out),
                      ("bulk_in", bulk_in)):
-        for _ in range(args.warmup):
-            fn()
+        warm_up(lambda i: fn(), args.warmup)
         ms = timed(fn, args.steps)
         res[name] = dict(us=round(ms * 1e3, 1), gbps=round(nbytes / (ms * 1e-3) / 1e9, 2))
     return {
@@ -297,6 +299,25 @@ def bench_swap(args) -> dict:
                      "frac_out": round(res["swap_out"]["gbps"] / PCIE_PEAK_GBPS, 3),
                      "frac_in": round(res["swap_in"]["gbps"] / PCIE_PEAK_GBPS, 3)},
     }
+
+
+# Untimed work before each timed region: at least --warmup calls and at least
+# this long (GPU clocks ramp up over the first milliseconds of activity).
+WARM_SECONDS = 0.2
+
+
+def warm_up(fn, calls: int, rotate: int = 1) -> int:
+    """Call fn(i % rotate) at least `calls` times and for at least WARM_SECONDS;
+    returns the number of calls."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < calls or time.perf_counter() - t0 < WARM_SECONDS:
+        fn(i % rotate)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()  # keep the host from running far ahead of the GPU
+    torch.cuda.synchronize()
+    return i
 
 
 def bench_prefill(args) -> dict:
@@ -326,9 +347,7 @@ def bench_prefill(args) -> dict:
                            k_scale=w.k_scale, v_scale=w.v_scale, window=args.window,
                            alibi_slopes=slopes)
 
-        for _ in range(args.warmup):
-            call()
-        torch.cuda.synchronize()
+        warm_up(lambda i: call(), args.warmup)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(args.steps):
@@ -642,14 +661,15 @@ def main() -> int:
               file=sys.stderr, flush=True)
         return 0
 
-    for i in range(args.warmup):
-        step(i % args.rotate)
+    warm_steps = warm_up(step, args.warmup, args.rotate)
     # timed region 1: whole steps (value, ms_per_step)
     ms_step = timed(step, args.steps)
     # timed region 2: the decode launches alone, back to back (roofline)
-    for i in range(args.warmup):
-        decode(i % args.rotate)
+    warm_decode = warm_up(decode, args.warmup, args.rotate)
     dec_avg = timed(decode, args.steps)
+    # (a kernel trace of this run splits its dispatches by these counts)
+    print(f"# regions: steps {warm_steps} warm-up + {args.steps} timed; decode {warm_decode} "
+          f"warm-up + {args.steps} timed", file=sys.stderr, flush=True)
 
     kernels = ("decode_kernel + merge_kernel" if mode == "balanced" else
                "decode_kernel" if mode == "single" else "decode_kernel + reduce_kernel")
