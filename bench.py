@@ -111,23 +111,26 @@ def cpu_baseline(w: W.Workload, budget_s: float, window: int = 0, alibi: bool = 
     slopes = None
     if alibi:
         slopes = paper_alibi_slopes(w.num_heads).cpu().numpy().astype(np.float64)
+    # sequences one at a time, cycling over the batch until the time budget is spent
     done = 0
     kv = 0
     t0 = time.perf_counter()
-    while done < w.num_seqs and time.perf_counter() - t0 < budget_s:
-        sl = slice(done, done + 1)
+    while time.perf_counter() - t0 < budget_s:
+        i = done % w.num_seqs
+        sl = slice(i, i + 1)
         oracle.decode(w.q[sl], kp, vp, w.block_tables[sl], w.context_lens[sl], scale, w.dtype,
                       k_scale=w.k_scale, v_scale=w.v_scale, window=window, alibi_slopes=slopes)
-        n = int(w.context_lens[done])
+        n = int(w.context_lens[i])
         n = min(n, window) if window > 0 else n
         kv += n * w.num_kv_heads * w.head_dim * 2 * W.element_bytes(w.dtype)
         done += 1
     dt = time.perf_counter() - t0
     return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"float64 NumPy oracle decode (gather + two-pass softmax) of sequences "
-                      f"0..{done - 1} of the same workload ({done} of {w.num_seqs}, "
-                      f"{kv / 1e6:.1f} MB of KV) in {dt:.1f} s; host has {os.cpu_count()} CPUs",
+            "sample": f"float64 NumPy oracle decode (gather + two-pass softmax), one sequence at "
+                      f"a time, cycling over the workload's {w.num_seqs} sequences: {done} "
+                      f"sequence decodes ({done / w.num_seqs:.1f} passes, {kv / 1e6:.1f} MB of "
+                      f"KV) in {dt:.1f} s; host has {os.cpu_count()} CPUs",
             "seqs_per_s": round(done / dt, 3)}
 
 
