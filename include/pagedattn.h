@@ -278,8 +278,9 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t he
  *     out[row][h] = sum_{t <= p} softmax_t(scale * q[row][h] . K_t) V_t
  * The K/V of all of a sequence's context_lens[i] positions (this step's tokens
  * included, written by pa_kv_append) must be in the cache.  The softmax
- * weights are rounded to bf16 for the matrix product (each within 2^-9 of
- * its value, relative) and normalised by the sum of the rounded weights.
+ * weights are rounded to bf16 for the matrix product (round to nearest even,
+ * each within 2^-8 of its value, relative) and normalised by the sum of the
+ * rounded weights.
  *
  *   q             DEVICE [num_tokens][num_heads][128] bfloat16
  *   block_tables  DEVICE int32 [num_seqs][max_blocks_per_seq]

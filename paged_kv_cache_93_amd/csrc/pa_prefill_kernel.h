@@ -30,7 +30,8 @@
 //   max and sum - no shuffles except two lane swaps for the row maximum.
 // * Weights are rounded to bf16 for the matrix product, and the running sum
 //   adds the rounded weights, so the output is an exact convex combination of
-//   V rows with weights within 2^-9 (relative) of the true ones.
+//   V rows; each weight is rounded to nearest even (within 2^-8 of its value,
+//   relative), so after the normalisation the weights are within about 2^-7.
 #pragma once
 
 #include <type_traits>

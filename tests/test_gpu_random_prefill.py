@@ -1,0 +1,95 @@
+"""A seeded sweep of random prefill (mixed-batch) configurations against the oracle.
+
+Each case draws everything at once: cache type (bf16 or 8-bit), block size, KV
+heads, query heads per KV head (1..8 or 16), a batch mixing whole prompts,
+slices over computed prefixes, decode rows and sequences with no rows, a sliding
+window, ALiBi slopes, one 8-bit scale per pool or per KV head, and the output
+type.  Bar: the prefill kernel rounds each softmax weight to bf16 (round to
+nearest even, relative error at most u = 2^-8) and divides by the sum of the
+rounded weights, so each output row is a convex combination of V rows whose
+weights are within about 1 +- 2^-7 of the exact ones: |out - exact| <=
+2^-7 max|v| (times 1.01), plus the output's own rounding (2^-8 relative for a
+bf16 output).  Per-head scales can make |v| larger than the seeded N(0,1)
+cases of the other prefill tests, so each case takes the worst-case bound from
+its own largest value.  Every case prints its draw before it runs.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import to_device
+from paged_kv_cache_93_amd import lib
+from paged_kv_cache_93_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw(seed):
+    rng = np.random.default_rng(7000 + seed)
+    S = int(rng.integers(1, 9))
+    lens, nq = [], []
+    for _ in range(S):
+        L = int(rng.integers(1, 401))
+        kind = int(rng.integers(0, 4))
+        n = L if kind == 0 else 1 if kind == 1 else 0 if kind == 2 else int(rng.integers(1, L + 1))
+        lens.append(L)
+        nq.append(n)
+    if sum(nq) == 0:
+        nq[0] = lens[0]
+    return dict(dtype=str(rng.choice(["bf16", "fp8"])), bs=int(rng.choice([8, 16, 32])),
+                hkv=int(rng.choice([1, 2, 4, 8])), g=int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 16])),
+                lens=lens, nq=nq, window=int(rng.choice([0, 0, 1, 50, 129])),
+                alibi=bool(rng.integers(0, 2)), per_head=bool(rng.integers(0, 2)),
+                out_f32=bool(rng.integers(0, 2)), rng=rng)
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_random_prefill(seed):
+    c = _draw(seed)
+    desc = {k: v for k, v in c.items() if k != "rng"}
+    print(f"case {seed}: {desc}", flush=True)
+    rng, dtype = c["rng"], c["dtype"]
+    H = c["hkv"] * c["g"]
+    w = W.prefill_batch("random", 8000 + seed, c["lens"], c["nq"], num_heads=H,
+                        num_kv_heads=c["hkv"], block_size=c["bs"], dtype=dtype)
+    ks = vs = None
+    k_arg, v_arg = w.k_scale, w.v_scale
+    if dtype == "fp8" and c["per_head"]:
+        ks = rng.uniform(0.004, 0.03, c["hkv"]).astype(np.float32)
+        vs = rng.uniform(0.004, 0.03, c["hkv"]).astype(np.float32)
+        k_arg, v_arg = torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda()
+    o_ks = ks.astype(np.float64) if ks is not None else w.k_scale
+    o_vs = vs.astype(np.float64) if vs is not None else w.v_scale
+    slopes = rng.uniform(0.01, 0.5, H).astype(np.float32) if c["alibi"] else None
+    scale = 1 / math.sqrt(128)
+    ref = oracle.prefill(w.q, w.k_pool, w.v_pool, w.block_tables, w.query_start, w.context_lens,
+                         scale, dtype, k_scale=o_ks, v_scale=o_vs, window=c["window"],
+                         alibi_slopes=slopes)
+    out = torch.empty((w.num_tokens, H, 128), device="cuda",
+                      dtype=torch.float32 if c["out_f32"] else torch.bfloat16)
+    lib.pa_prefill(to_device(w.k_pool, dtype), to_device(w.v_pool, dtype), to_device(w.q, "bf16"),
+                   torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(w.query_start).cuda(),
+                   torch.from_numpy(w.context_lens).cuda(), scale, out, k_scale=k_arg,
+                   v_scale=v_arg, window=c["window"],
+                   alibi_slopes=None if slopes is None else torch.from_numpy(slopes).cuda())
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    assert np.abs(got - ref).max() <= value_bound(w, vs, c["out_f32"], ref)
+
+
+def value_bound(w, vs, out_f32, ref):
+    """The worst case 1.01 * 2^-7 max|v| over the pool's finite values, plus the
+    output rounding (2^-8 relative for bf16) and the float32 accumulation."""
+    if w.dtype == "fp8":
+        head_scale = np.full(w.num_kv_heads, w.v_scale) if vs is None else vs.astype(np.float64)
+        v = oracle.fp8_to_f64(w.v_pool) * head_scale[None, :, None, None]
+    else:
+        v = oracle.to_f64(w.v_pool, w.dtype)
+    vmax = float(np.nanmax(np.abs(v)))
+    rounding = 0.0 if out_f32 else 2.0 ** -8 * (float(np.abs(ref).max()) + 2.0 ** -7 * vmax)
+    return 1.01 * 2.0 ** -7 * vmax + rounding + 1e-5
