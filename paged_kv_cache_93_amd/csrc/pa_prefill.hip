@@ -8,12 +8,17 @@ namespace {
 
 // The tile map: tile t of the grid -> (sequence, tile of that sequence), each
 // sequence's tiles from its last (longest context) to its first.  One
-// workgroup of 1024 threads scans the per-sequence tile counts.
+// workgroup of 1024 threads takes 1024 sequences at a time: it scans their
+// tile counts, then all threads write the chunk's (sequence, tile) pairs
+// together, each finding the sequence of its tile by binary search over the
+// chunk's running ends (a thread per sequence writing its own pairs would
+// leave a long prompt's hundreds of pairs to one thread).
 __global__ void __launch_bounds__(1024) prefill_tiles_kernel(const int32_t* qs, int32_t S,
                                                              int32_t T, int32_t tt,
                                                              int32_t* tiles, int32_t max_tiles) {
   __shared__ int32_t s_wave[16];
   __shared__ int32_t s_total;
+  __shared__ int32_t s_end[1024];  // end (exclusive) of sequence base + j's tiles in the chunk
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   int32_t running = 0;
@@ -38,15 +43,24 @@ __global__ void __launch_bounds__(1024) prefill_tiles_kernel(const int32_t* qs, 
       s_total = acc;
     }
     __syncthreads();
-    const int32_t off = running + s_wave[wave] + incl - cnt;
-    for (int32_t k = 0; k < cnt; ++k) {
-      const int32_t t = off + k;
-      if (t < max_tiles) {
-        tiles[1 + 2 * t] = i;
-        tiles[2 + 2 * t] = cnt - 1 - k;
+    s_end[tid] = s_wave[wave] + incl;
+    __syncthreads();
+    const int32_t total = s_total;
+    for (int32_t t = tid; t < total; t += 1024) {
+      int lo = 0, hi = 1023;  // first j with s_end[j] > t (s_end[1023] == total > t)
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_end[mid] > t) hi = mid; else lo = mid + 1;
+      }
+      const int32_t start = lo > 0 ? s_end[lo - 1] : 0;
+      const int32_t seq_cnt = s_end[lo] - start;
+      const int32_t gt = running + t;
+      if (gt < max_tiles) {
+        tiles[1 + 2 * gt] = base + lo;
+        tiles[2 + 2 * gt] = seq_cnt - 1 - (t - start);
       }
     }
-    running += s_total;
+    running += total;
     __syncthreads();
   }
   if (tid == 0) tiles[0] = min(running, max_tiles);
