@@ -213,7 +213,7 @@ typedef struct pa_attn_variant {
  *                 ceil(L_i / block_size) are not read
  *   context_lens  DEVICE int32 [num_seqs], 0 <= L_i <= max_blocks_per_seq*block_size
  *   num_heads     multiple of num_kv_heads; ratio G = 1..8, or 16 for a bf16 or
- *                 8-bit cache with head_dim 128 (other ratios: PA_ERR_UNSUPPORTED)
+ *                 8-bit cache (other ratios: PA_ERR_UNSUPPORTED)
  *   scale         > 0 and finite (normally 1/sqrt(head_dim))
  *   variant       HOST pa_attn_variant, or NULL for plain attention.  The query
  *                 sits at position p = L_i - 1: a window W keeps t >= L_i - W

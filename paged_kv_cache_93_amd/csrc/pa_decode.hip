@@ -85,7 +85,7 @@ int prepare(const char* fn, const pa_cache* cache, const void* q, const int32_t*
                               *group))
     return fail(PA_ERR_UNSUPPORTED,
                 "%s: query heads per KV head must be 1..8, or 16 for a bf16 or 8-bit cache "
-                "with head_dim 128 (got %d)",
+                "(got %d)",
                 fn, *group);
   if (!(scale > 0.f) || !std::isfinite(scale))
     return fail(PA_ERR_SHAPE, "%s: scale must be positive and finite", fn);

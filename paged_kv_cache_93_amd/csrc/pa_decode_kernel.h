@@ -25,15 +25,15 @@
 //   ones write the output, pieces write partials merged by merge_kernel).
 // * Rows are loaded in 16-byte chunks with non-temporal loads (the cache is
 //   streamed once); one load instruction covers 1 KiB of contiguous rows.
-// * q.k, bf16 and 8-bit caches with 128-dim heads (blocks of 8, 16 or 32): a
-//   16-row K tile goes through LDS into the MFMA A layout and four
+// * q.k, bf16 and 8-bit caches with 64- or 128-dim heads (blocks of 8, 16 or 32): a
+//   16-row K tile goes through LDS into the MFMA A layout and D/32
 //   v_mfma_f32_16x16x32_bf16 score it against the G query heads (the B
 //   operand; columns past G are ignored).  P.V then runs on MFMA too: the
 //   weights, in lane 16g + h for rows 4g..4g+3 of head h, are already the B
 //   operand of O^T += V^T P, and the V tile goes through the same LDS area and
 //   comes back transposed (ds_read_b64_tr_b16) as the A operand; each weight
-//   enters as three bf16 terms, so the product keeps it to 2^-23.  Other
-//   cases (float32 caches, 64-dim heads): each lane dots its
+//   enters as three bf16 terms, so the product keeps it to 2^-23.  Float32
+//   caches: each lane dots its
 //   16-byte chunk against the same chunk of each query head (v_dot2 for bf16
 //   pairs, f32 accumulation), the lanes of a row add up their partial sums
 //   with DPP row rotations, and the V rows are accumulated on the VALU in f32.
@@ -317,7 +317,8 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 // Scores on the matrix cores: bf16 and 8-bit caches with 128-dim heads and
 // blocks of at least 16 rows (an MFMA tile is 16 rows of one block).
 constexpr bool decode_uses_mfma(int et, int d, int bs) {
-  return PA_MFMA_SCORES && et != kF32 && d == 128 && bs >= 8;
+  return PA_MFMA_SCORES && et != kF32 && (d == 128 || (d == 64 && PA_DECODE_MFMA_PV)) &&
+         bs >= 8;
 }
 
 // LDS bytes each wave of the MFMA path uses: a 16-row K tile padded to 17
@@ -325,7 +326,8 @@ constexpr bool decode_uses_mfma(int et, int d, int bs) {
 // [4 row groups][G heads][4 rows], the rescale factors [4][G], and the G
 // query rows of the sequence being scored (16 chunks of 16 bytes each).
 constexpr int decode_wave_lds_bytes(int et, int d, int g, int bs) {
-  return decode_uses_mfma(et, d, bs) ? 16 * 17 * 16 + 64 * g + 16 * g + 256 * g : 0;
+  return decode_uses_mfma(et, d, bs) ? 16 * (d / 8 + 1) * 16 + 64 * g + 16 * g + (d / 8) * 16 * g
+                                     : 0;
 }
 
 // Byte offset of the per-wave LDS areas behind the unit prefix (balanced mode).
@@ -345,7 +347,10 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   constexpr int LPR = D / VEC;                       // lanes per row
   constexpr int RPI = 64 / LPR;                      // rows per load instruction
   constexpr bool MF = decode_uses_mfma(ET, D, BS);   // q.k on MFMA (16-row tiles)
-  constexpr int QC = MF ? (16 * G + 63) / 64 : 1;    // query chunks a lane loads per tile
+  constexpr int QCH = D / 8;                         // 16-byte chunks of a bf16 query row
+  constexpr int KCH = D / 8 + 1;                     // 16-byte chunks of an LDS tile row (padded)
+  constexpr int MM = D / 32;                         // score MFMAs per tile
+  constexpr int QC = MF ? (QCH * G + 63) / 64 : 1;   // query chunks a lane loads per tile
   constexpr int TRW = MF ? 16 : (G > 4 ? 2 : 4) * RPI;   // wide groups keep smaller tiles
   constexpr int TR = MF ? 16 : BS < TRW ? BS : TRW;  // rows per register tile
   constexpr int NI = TR / RPI;                       // load instructions per tile
@@ -359,7 +364,8 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   static_assert(BPT == 1 ? BS % TR == 0 : (MF && BPT == 2), "a unit is one block or an MFMA pair");
   static_assert(RPI * D * EB == 64 * LB, "one load instruction covers whole rows");
   static_assert(!BF16 || VEC == 8, "bf16 query chunks hold 8 elements");
-  static_assert(!MF || (RPI == 4 && NI == 4 && TR == 16), "MFMA tiles are 16 rows of 4 groups");
+  static_assert(!MF || (TR == 16 && NI * RPI == 16 && MM % 2 == 0),
+                "MFMA tiles are 16 rows: NI consecutive rows per row group");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -440,8 +446,8 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   uint8_t* wave_lds = reinterpret_cast<uint8_t*>(s_prefix) +
                       decode_prefix_lds_bytes(a.num_seqs, a.mode == kModeBalanced) +
                       size_t(wave) * decode_wave_lds_bytes(ET, D, G, BS);
-  u32x4* lds_k = reinterpret_cast<u32x4*>(wave_lds);              // [16 rows][17 chunks]
-  float* lds_p = reinterpret_cast<float*>(wave_lds + 16 * 17 * 16);  // [4][G][4]
+  u32x4* lds_k = reinterpret_cast<u32x4*>(wave_lds);              // [16 rows][KCH chunks]
+  float* lds_p = reinterpret_cast<float*>(wave_lds + 16 * KCH * 16);  // [4][G][4]
   float* lds_a = lds_p + 16 * G;                                   // [4][G]
   u32x4* lds_q = reinterpret_cast<u32x4*>(lds_a + 4 * G);          // [G][16 chunks]
 
@@ -500,7 +506,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   f32x4 oacc[MFPV ? NB16 : 1];
   float mf_top = kNegInf;
   u32x4 qc[MF ? 1 : G];  // VALU path: chunk c of each head's query
-  u32x4 qf[MF ? 4 : 1];  // MFMA path: the current sequence's query as B operands
+  u32x4 qf[MF ? MM : 1];  // MFMA path: the current sequence's query as B operands
 
   // Emit the finished piece of sequence `seq`: the final output when the piece
   // is the whole sequence, else a partial row.
@@ -683,7 +689,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     if constexpr (MF) {
       const int h = (lane & 15) % G;
 #pragma unroll
-      for (int mm = 0; mm < 4; ++mm) dqf[mm] = qrow[h * LPR + 4 * mm + (lane >> 4)];
+      for (int mm = 0; mm < MM; ++mm) dqf[mm] = qrow[h * QCH + 4 * mm + (lane >> 4)];
     } else {
 #pragma unroll
       for (int h = 0; h < G; ++h) dqc[h] = qrow[h * LPR + c];
@@ -821,7 +827,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < QC; ++j) {
           const int ch = lane + 64 * j;
-          qr[j] = qrow[ch < 16 * G ? ch : ch % (16 * G)];  // lanes past the rows repeat one
+          qr[j] = qrow[ch < QCH * G ? ch : ch % (QCH * G)];  // lanes past the rows repeat one
         }
       }
     }
@@ -836,15 +842,15 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     // the MFMA operand layout instead - 64-byte pieces of 16 rows - was
     // measured slower than transposing it through LDS.)  With block pairs,
     // row groups 2 and 3 read rows 0..7 of the second block.
-    int lo = MF ? r * 64 + c : lane;
+    int lo = MF ? NI * LPR * r + c : lane;
     if constexpr (BPT > 1) {
       if (phys2 < 0 || int64_t(phys2) >= a.num_blocks) phys2 = 0;
-      if (r >= 2) {
+      if (NI * r >= 8) {
         off = size_t(phys2) * block_bytes;
-        lo -= 128;
+        lo -= 8 * LPR;
       }
     }
-    constexpr int step = MF ? 16 : 64;
+    constexpr int step = MF ? LPR : 64;
     const Raw* kp = reinterpret_cast<const Raw*>(kbase + off) + lo;
     const Raw* vp = reinterpret_cast<const Raw*>(vbase + off) + lo;
 #pragma unroll
@@ -884,11 +890,11 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
         q_staged = tseq;
 #pragma unroll
         for (int j = 0; j < QC; ++j)
-          if (lane + 64 * j < 16 * G) lds_q[lane + 64 * j] = qr[j];
+          if (lane + 64 * j < QCH * G) lds_q[lane + 64 * j] = qr[j];
         __builtin_amdgcn_wave_barrier();
         const int qh = (lane & 15) % G;
 #pragma unroll
-        for (int mm = 0; mm < 4; ++mm) qf[mm] = lds_q[qh * 16 + 4 * mm + (lane >> 4)];
+        for (int mm = 0; mm < MM; ++mm) qf[mm] = lds_q[qh * QCH + 4 * mm + (lane >> 4)];
       }
     }
     if (nvalid <= nskip) return;  // every row masked: the state would not change
@@ -899,13 +905,13 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
       // 16g + h holds the same dims of query head h as B (h < G; the other
       // lanes repeat a head whose score column is never used).
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lds_k[(4 * r + i) * 17 + c] = score_chunk<ET>(kr[i]);
+      for (int i = 0; i < NI; ++i) lds_k[(NI * r + i) * KCH + c] = score_chunk<ET>(kr[i]);
       // two independent accumulation chains of two MFMAs each
       f32x4 sc_even = {0.f, 0.f, 0.f, 0.f}, sc_odd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int mm = 0; mm < 4; mm += 2) {
-        const u32x4 ka = lds_k[(lane & 15) * 17 + 4 * mm + (lane >> 4)];
-        const u32x4 kb2 = lds_k[(lane & 15) * 17 + 4 * (mm + 1) + (lane >> 4)];
+      for (int mm = 0; mm < MM; mm += 2) {
+        const u32x4 ka = lds_k[(lane & 15) * KCH + 4 * mm + (lane >> 4)];
+        const u32x4 kb2 = lds_k[(lane & 15) * KCH + 4 * (mm + 1) + (lane >> 4)];
         sc_even = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             __builtin_bit_cast(bf16x8, ka), __builtin_bit_cast(bf16x8, qf[mm]), sc_even, 0, 0, 0);
         sc_odd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -965,14 +971,14 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
         // reads give lane 16g + s dim 16b + s of rows 4g..4g+3: the A operand.
         asm volatile("" ::: "memory");
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < NI; ++i) {
           u32x4 vc = score_chunk<ET>(vr[i]);
-          if (partial && (4 * r + i >= nvalid || 4 * r + i < nskip)) vc = u32x4{0u, 0u, 0u, 0u};
-          lds_k[(4 * r + i) * 17 + c] = vc;
+          if (partial && (NI * r + i >= nvalid || NI * r + i < nskip)) vc = u32x4{0u, 0u, 0u, 0u};
+          lds_k[(NI * r + i) * KCH + c] = vc;
         }
         asm volatile("" ::: "memory");
         PA_LDS_PTR(uint8_t) lv = (PA_LDS_PTR(uint8_t))lds_k;
-        const int voff = (4 * (lane >> 4) + ((lane & 15) >> 2)) * 272 + 8 * (lane & 3);
+        const int voff = (4 * (lane >> 4) + ((lane & 15) >> 2)) * (KCH * 16) + 8 * (lane & 3);
 #pragma unroll
         for (int b = 0; b < NB16; ++b) {
           const v4s vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS_PTR(v4s))(lv + voff + 32 * b));

@@ -149,7 +149,7 @@ def _partitions(cache, **kw):
     ({}, dict(num_heads=18), 3),                   # 9 query heads per KV head
     ({}, dict(num_heads=64), 3),                   # 32 query heads per KV head
     (dict(dtype=lib.PA_F32), dict(num_heads=32, out_dtype=lib.PA_F32), 3),  # 16: MFMA path only
-    (dict(head_dim=64), dict(num_heads=32), 3),    # 16 with 64-dim heads
+    (dict(dtype=lib.PA_F32, head_dim=64), dict(num_heads=32, out_dtype=lib.PA_F32), 3),
     ({}, dict(scale=0.0), 2),
     ({}, dict(scale=float("inf")), 2),
     ({}, dict(num_seqs=-1), 2),

@@ -35,7 +35,7 @@ def _draw(seed):
     d = int(rng.choice([64, 128]))
     bs = int(rng.choice([8, 16, 32]))
     hkv = int(rng.choice([1, 2, 3, 4, 8]))
-    groups = [1, 2, 3, 4, 5, 6, 7, 8] + ([16] if dtype != "f32" and d == 128 else [])
+    groups = [1, 2, 3, 4, 5, 6, 7, 8] + ([16] if dtype != "f32" else [])
     g = int(rng.choice(groups))
     S = int(rng.integers(1, 41))
     lens = [int(x) for x in rng.integers(1, 701, size=S)]
