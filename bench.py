@@ -518,6 +518,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--block-size", type=int, default=None)
+    ap.add_argument("--head-dim", type=int, default=None, choices=[64, 128],
+                    help="decode: the named workload with this head_dim (same seed)")
     ap.add_argument("--dtype", default=None, choices=["f32", "bf16", "fp8"],
                     help="cache element type (default: the workload's; fp8 = E4M3 codes)")
     ap.add_argument("--mode", default="balanced",
@@ -569,7 +571,8 @@ def main() -> int:
         print(json.dumps(bench_prefill(args)), flush=True)
         return 0
 
-    w = W.make_config(args.workload, dtype=args.dtype, block_size=args.block_size)
+    w = W.make_config(args.workload, dtype=args.dtype, block_size=args.block_size,
+                      head_dim=args.head_dim)
     qdt = W.query_dtype(w.dtype)
     sc = dict(k_scale=w.k_scale, v_scale=w.v_scale)
     mode = args.mode if args.mode in ("balanced", "single") else int(args.mode)

@@ -393,22 +393,26 @@ def _scatter_placement(rng, lens, bs, slack=1.25, extra_blocks=0, num_blocks=Non
 # ---------------------------------------------------------------------------
 
 def make_config(k: int, dtype: str | None = None, block_size: int | None = None,
-                num_seqs: int | None = None, context: int | None = None) -> Workload:
+                num_seqs: int | None = None, context: int | None = None,
+                head_dim: int | None = None) -> Workload:
     """Workload k (1..5) with master seed 9300 + k.
 
-    ``dtype``/``block_size``/``num_seqs``/``context`` override the named shape
-    (same seed), e.g. float32 copies of the bf16 shapes, block size 32 for
-    workload 5, or fewer sequences for quick tests.
+    ``dtype``/``block_size``/``num_seqs``/``context``/``head_dim`` override the
+    named shape (same seed), e.g. float32 copies of the bf16 shapes, block size
+    32 for workload 5, 64-dim heads, or fewer sequences for quick tests.
     """
     cfg = dict(CONFIGS[k])
     seed = 9300 + k
     if block_size is not None:
         cfg["block_size"] = int(block_size)
+    if head_dim is not None:
+        cfg["head_dim"] = int(head_dim)
     dt = dtype or cfg["dtype"]
     s = _streams(seed)
     bs = cfg["block_size"]
     name = cfg["name"] + ("" if dt == cfg["dtype"] else f"_{dt}") + (
-        "" if block_size in (None, CONFIGS[k]["block_size"]) else f"_bs{bs}")
+        "" if block_size in (None, CONFIGS[k]["block_size"]) else f"_bs{bs}") + (
+        "" if head_dim in (None, CONFIGS[k]["head_dim"]) else f"_d{cfg['head_dim']}")
 
     if k == 1:
         lens = [5, 37]

@@ -153,3 +153,12 @@ def test_fp8_workloads():
     ref = W.bf16_bits_to_f32(b.k_pool)[live] / W.FP8_SCALE
     assert np.max(np.abs(vals[live] - ref) / np.maximum(np.abs(ref), 2.0 ** -6)) < 2.0 ** -3
     assert w.kv_bytes() * 2 == b.kv_bytes()
+
+
+def test_head_dim_override_keeps_the_lengths():
+    base, d64 = W.make_config(2), W.make_config(2, head_dim=64)
+    assert d64.name == base.name + "_d64" and d64.head_dim == 64
+    assert np.array_equal(base.context_lens, d64.context_lens)
+    assert d64.k_pool.shape == base.k_pool.shape[:3] + (64,)
+    assert d64.q.shape == base.q.shape[:2] + (64,)
+    assert 2 * d64.kv_bytes() == base.kv_bytes()
