@@ -156,7 +156,7 @@ def test_fp8_workloads():
 
 
 def test_head_dim_override_keeps_the_lengths():
-    base, d64 = W.make_config(2), W.make_config(2, head_dim=64)
+    base, d64 = W.make_config(2, num_seqs=4), W.make_config(2, num_seqs=4, head_dim=64)
     assert d64.name == base.name + "_d64" and d64.head_dim == 64
     assert np.array_equal(base.context_lens, d64.context_lens)
     assert d64.k_pool.shape == base.k_pool.shape[:3] + (64,)
