@@ -70,6 +70,28 @@ int check_cache(const pa_cache* cache, const char* fn) {
   return PA_OK;
 }
 
+int check_device_memory(const char* fn, std::initializer_list<NamedPtr> ptrs) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PA_ERR_SHAPE, "%s: no HIP device is current", fn);
+  }
+  for (const NamedPtr& np : ptrs) {
+    if (np.ptr == nullptr) continue;
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, np.ptr) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(PA_ERR_SHAPE, "%s: %s is not memory the HIP runtime knows (a host pointer?)",
+                  fn, np.name);
+    }
+    const bool managed = attr.type == hipMemoryTypeManaged || attr.isManaged != 0;
+    if (!managed && !(attr.type == hipMemoryTypeDevice && attr.device == dev))
+      return fail(PA_ERR_SHAPE, "%s: %s is not device memory of the current device", fn,
+                  np.name);
+  }
+  return PA_OK;
+}
+
 }  // namespace pa
 
 PA_API int32_t pa_abi_version(void) { return PA_ABI_VERSION; }

@@ -183,6 +183,15 @@ int decode_call(const char* fn, const pa_cache* cache, const void* q, const void
                 "%s: out_dtype must be PA_F32, or PA_BF16 for a bf16 or 8-bit cache", fn);
   if (!aligned16(out)) return fail(PA_ERR_SHAPE, "%s: out must be 16-byte aligned", fn);
   if (num_seqs == 0) return PA_OK;
+  // (after every other check, right before anything is enqueued)
+  auto check_memory = [&]() {
+    return check_device_memory(
+        fn, {{"k_pool", cache->k_pool}, {"v_pool", cache->v_pool}, {"q", q},
+             {"block_tables", block_tables}, {"context_lens", context_lens}, {"out", out},
+             {"workspace", workspace}, {"k_new", k_new}, {"v_new", v_new},
+             {"alibi_slopes", a.alibi}, {"k_scales", cache->k_scales},
+             {"v_scales", cache->v_scales}});
+  };
   a.out = out;
   a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
   const int waves = waves_per_group(cache->num_kv_heads);
@@ -193,6 +202,7 @@ int decode_call(const char* fn, const pa_cache* cache, const void* q, const void
       size_t(waves) * decode_wave_lds_bytes(elem_type(cache->dtype), cache->head_dim, group, cache->block_size);
   if (workspace == nullptr || num_seqs > kMaxBalancedSeqs) {
     a.mode = kModeSingle;
+    if (int st = check_memory()) return st;
     return launch(fn, cache, group, a, dim3(unsigned(num_seqs), head_groups), waves, wave_lds, s);
   }
   const size_t lds = decode_prefix_lds_bytes(num_seqs, true) + wave_lds;
@@ -203,6 +213,7 @@ int decode_call(const char* fn, const pa_cache* cache, const void* q, const void
                 workspace_bytes, w.total);
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
     return fail(PA_ERR_SHAPE, "%s: workspace must be 256-byte aligned", fn);
+  if (int st = check_memory()) return st;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   a.mode = kModeBalanced;
   a.num_groups = groups;
@@ -274,6 +285,12 @@ PA_API int pa_decode_partitions(const pa_cache* cache, const void* q, const int3
     return fail(PA_ERR_WORKSPACE, "%s: part_out, part_max and part_sum are required", fn);
   if (!aligned16(part_out)) return fail(PA_ERR_SHAPE, "%s: part_out must be 16-byte aligned", fn);
   if (num_seqs == 0) return PA_OK;
+  if (int st = check_device_memory(
+          fn, {{"k_pool", cache->k_pool}, {"v_pool", cache->v_pool}, {"q", q},
+               {"block_tables", block_tables}, {"context_lens", context_lens},
+               {"part_out", part_out}, {"part_max", part_max}, {"part_sum", part_sum},
+               {"k_scales", cache->k_scales}, {"v_scales", cache->v_scales}}))
+    return st;
   a.mode = kModePartition;
   a.partition_blocks = partition_size / cache->block_size;
   a.max_parts = max_parts;

@@ -135,6 +135,13 @@ PA_API int pa_prefill(const pa_cache* cache, const void* q, const int32_t* block
     return fail(PA_ERR_SHAPE, "pa_prefill: workspace must be 256-byte aligned");
   if (cache->num_kv_heads > 65535)
     return fail(PA_ERR_SHAPE, "pa_prefill: too many KV heads");
+  if (int st = check_device_memory(
+          "pa_prefill", {{"k_pool", cache->k_pool}, {"v_pool", cache->v_pool}, {"q", q},
+                         {"block_tables", block_tables}, {"query_start", query_start},
+                         {"context_lens", context_lens}, {"out", out}, {"workspace", workspace},
+                         {"alibi_slopes", alibi}, {"k_scales", cache->k_scales},
+                         {"v_scales", cache->v_scales}}))
+    return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* tiles = static_cast<int32_t*>(workspace);

@@ -114,6 +114,10 @@ PA_API int pa_splitkv_reduce(const float* part_out, const float* part_max, const
   if (!part_out || !part_max || !part_sum)
     return fail(PA_ERR_WORKSPACE, "%s: part_out, part_max or part_sum is NULL", fn);
   if (!context_lens || !out) return fail(PA_ERR_NULL, "%s: context_lens or out is NULL", fn);
+  if (int st = check_device_memory(fn, {{"part_out", part_out}, {"part_max", part_max},
+                                        {"part_sum", part_sum}, {"context_lens", context_lens},
+                                        {"out", out}, {"lse", lse}}))
+    return st;
   ReduceArgs a;
   a.part_out = part_out;
   a.part_max = part_max;

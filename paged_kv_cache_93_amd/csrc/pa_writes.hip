@@ -124,6 +124,12 @@ PA_API int pa_kv_append(const pa_cache* cache, const void* k_new, const void* v_
   // (an 8-bit cache's rows are head_dim bytes; check_cache asks for a multiple of 16)
   if ((reinterpret_cast<uintptr_t>(slot_mapping) & 7u) != 0)
     return fail(PA_ERR_SHAPE, "pa_kv_append: slot_mapping must be 8-byte aligned");
+  if (int st = check_device_memory("pa_kv_append",
+                                   {{"k_pool", cache->k_pool}, {"v_pool", cache->v_pool},
+                                    {"k_new", k_new}, {"v_new", v_new},
+                                    {"slot_mapping", slot_mapping},
+                                    {"k_scales", cache->k_scales}, {"v_scales", cache->v_scales}}))
+    return st;
   AppendArgs a;
   a.k_pool = static_cast<uint8_t*>(cache->k_pool);
   a.v_pool = static_cast<uint8_t*>(cache->v_pool);
@@ -186,6 +192,10 @@ PA_API int pa_copy_blocks(const pa_cache* cache, const int64_t* block_pairs, int
   if (!block_pairs) return fail(PA_ERR_NULL, "pa_copy_blocks: block_pairs is NULL");
   if ((reinterpret_cast<uintptr_t>(block_pairs) & 7u) != 0)
     return fail(PA_ERR_SHAPE, "pa_copy_blocks: block_pairs must be 8-byte aligned");
+  if (int st = check_device_memory("pa_copy_blocks", {{"k_pool", cache->k_pool},
+                                                      {"v_pool", cache->v_pool},
+                                                      {"block_pairs", block_pairs}}))
+    return st;
   CopyArgs a;
   a.src_k = static_cast<const uint8_t*>(cache->k_pool);
   a.src_v = static_cast<const uint8_t*>(cache->v_pool);
@@ -212,6 +222,10 @@ PA_API int pa_swap_blocks(const pa_cache* cache, void* host_k_pool, void* host_v
     return fail(PA_ERR_SHAPE, "pa_swap_blocks: block_pairs must be 8-byte aligned");
   if (!aligned16(host_k_pool) || !aligned16(host_v_pool))
     return fail(PA_ERR_SHAPE, "pa_swap_blocks: host pools must be 16-byte aligned");
+  if (int st = check_device_memory("pa_swap_blocks", {{"k_pool", cache->k_pool},
+                                                      {"v_pool", cache->v_pool},
+                                                      {"block_pairs", block_pairs}}))
+    return st;
   void* hk = mapped_host(host_k_pool);
   void* hv = mapped_host(host_v_pool);
   if (!hk || !hv)

@@ -188,6 +188,13 @@ def _require(cond: bool, msg: str):
         raise ValueError(msg)
 
 
+def _on_device(**tensors):
+    """Every named tensor that is not None lives on a GPU (a host tensor's
+    pointer handed to a kernel would fault the device)."""
+    for name, t in tensors.items():
+        _require(t is None or t.device.type == "cuda", f"{name} must be a device tensor")
+
+
 def make_cache(k_pool: torch.Tensor, v_pool: torch.Tensor, k_scale: float = 1.0,
                v_scale: float = 1.0) -> PaCache:
     """pa_cache for two [num_blocks][num_kv_heads][block_size][head_dim] pools.
@@ -199,6 +206,7 @@ def make_cache(k_pool: torch.Tensor, v_pool: torch.Tensor, k_scale: float = 1.0,
     _require(k_pool.dim() == 4 and k_pool.shape == v_pool.shape and k_pool.dtype == v_pool.dtype,
              "k_pool and v_pool must be equal-shaped 4-D tensors")
     _require(k_pool.is_contiguous() and v_pool.is_contiguous(), "pools must be contiguous")
+    _on_device(k_pool=k_pool, v_pool=v_pool)
     nb, hkv, bs, d = k_pool.shape
     per_head = isinstance(k_scale, torch.Tensor) or isinstance(v_scale, torch.Tensor)
     if not per_head:
@@ -232,6 +240,7 @@ def pa_kv_append(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None, k_scal
     pools' scales.
     """
     cache = make_cache(k_pool, v_pool, k_scale, v_scale)
+    _on_device(k_new=k_new, v_new=v_new, slot_mapping=slot_mapping)
     _require(slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous(),
              "slot_mapping must be contiguous int64")
     n = slot_mapping.numel()
@@ -247,6 +256,7 @@ def pa_kv_append(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None, k_scal
 def pa_copy_blocks(k_pool, v_pool, block_pairs, stream=None) -> None:
     """Copy block src -> dst in both pools for each row of block_pairs (int64 [n][2])."""
     cache = make_cache(k_pool, v_pool, 1.0, 1.0)
+    _on_device(block_pairs=block_pairs)
     _require(block_pairs.dtype == torch.int64 and block_pairs.is_contiguous() and
              (block_pairs.numel() == 0 or block_pairs.shape[-1] == 2),
              "block_pairs must be contiguous int64 [n][2]")
@@ -294,6 +304,7 @@ def decode_workspace(num_seqs: int, num_heads: int, head_dim: int,
 
 def _decode_common(k_pool, v_pool, q, block_tables, context_lens, k_scale, v_scale):
     cache = make_cache(k_pool, v_pool, k_scale, v_scale)
+    _on_device(q=q, block_tables=block_tables, context_lens=context_lens)
     _require(q.dim() == 3 and q.is_contiguous() and q.dtype == _token_dtype(cache) and
              q.shape[2] == cache.head_dim,
              "q must be contiguous [num_seqs][num_heads][head_dim] of the pool dtype "
@@ -334,6 +345,7 @@ def pa_decode(k_pool, v_pool, q, block_tables, context_lens, scale: float, out, 
     _require(out is not None and out.is_contiguous() and
              tuple(out.shape) == (num_seqs, num_heads, cache.head_dim),
              "out must be contiguous [num_seqs][num_heads][head_dim]")
+    _on_device(out=out, workspace=workspace)
     ws_bytes = 0
     if workspace is not None:
         _require(workspace.is_contiguous(), "workspace must be contiguous")
@@ -355,6 +367,7 @@ def pa_decode_append(k_pool, v_pool, q, k_new, v_new, block_tables, context_lens
     """
     cache = _decode_common(k_pool, v_pool, q, block_tables, context_lens, k_scale, v_scale)
     num_seqs, num_heads = q.shape[0], q.shape[1]
+    _on_device(k_new=k_new, v_new=v_new)
     for t in (k_new, v_new):
         _require(t is not None and t.is_contiguous() and t.dtype == _token_dtype(cache) and
                  tuple(t.shape) == (num_seqs, cache.num_kv_heads, cache.head_dim),
@@ -363,6 +376,7 @@ def pa_decode_append(k_pool, v_pool, q, k_new, v_new, block_tables, context_lens
     _require(out is not None and out.is_contiguous() and
              tuple(out.shape) == (num_seqs, num_heads, cache.head_dim),
              "out must be contiguous [num_seqs][num_heads][head_dim]")
+    _on_device(out=out, workspace=workspace)
     ws_bytes = 0
     if workspace is not None:
         _require(workspace.is_contiguous(), "workspace must be contiguous")
@@ -391,6 +405,7 @@ def pa_decode_partitions(k_pool, v_pool, q, block_tables, context_lens, scale: f
         _require(t is not None and t.dtype == torch.float32 and t.is_contiguous() and
                  tuple(t.shape) == (num_seqs, num_heads, max_parts),
                  "part_max/part_sum must be contiguous float32 [num_seqs][num_heads][max_parts]")
+    _on_device(part_out=part_out, part_max=part_max, part_sum=part_sum)
     _check(load().pa_decode_partitions(ctypes.byref(cache), _ptr(q), _ptr(block_tables),
                                        _ptr(context_lens), num_seqs, num_heads,
                                        block_tables.shape[1], float(scale), int(partition_size),
@@ -419,19 +434,29 @@ def pa_prefill(k_pool, v_pool, q, block_tables, query_start, context_lens, scale
     ``alibi_slopes`` (device float32 [num_heads]) adds slope * (t - p) to scores.
     """
     cache = make_cache(k_pool, v_pool, k_scale, v_scale)
+    _on_device(q=q, out=out, block_tables=block_tables, query_start=query_start,
+               context_lens=context_lens, workspace=workspace)
+    _require(q.dtype == torch.bfloat16 and q.is_contiguous() and q.dim() == 3 and
+             q.shape[2] == cache.head_dim,
+             "q must be contiguous bf16 [num_tokens][num_heads][head_dim] with the pools' "
+             "head_dim")
     num_tokens, num_heads = q.shape[0], q.shape[1]
+    _require(context_lens.dtype == torch.int32 and context_lens.dim() == 1 and
+             context_lens.is_contiguous(), "context_lens must be contiguous int32 [num_seqs]")
     num_seqs = context_lens.shape[0]
-    _require(q.dtype == torch.bfloat16 and q.is_contiguous() and q.dim() == 3,
-             "q must be contiguous bf16 [num_tokens][num_heads][head_dim]")
-    _require(out.shape == q.shape and out.is_contiguous(), "out must match q's shape")
+    _require(out is not None and out.shape == q.shape and out.is_contiguous() and
+             out.dtype in (torch.float32, torch.bfloat16),
+             "out must be contiguous float32 or bfloat16 of q's shape")
     _require(block_tables.dtype == torch.int32 and block_tables.is_contiguous() and
              block_tables.dim() == 2 and block_tables.shape[0] == num_seqs,
              "block_tables must be contiguous int32 [num_seqs][max_blocks]")
-    _require(query_start.dtype == torch.int32 and query_start.numel() == num_seqs + 1 and
-             context_lens.dtype == torch.int32, "query_start int32 [S+1], context_lens int32 [S]")
+    _require(query_start.dtype == torch.int32 and query_start.is_contiguous() and
+             query_start.numel() == num_seqs + 1,
+             "query_start must be contiguous int32 [num_seqs + 1]")
     if workspace is None:
         workspace = prefill_workspace(num_seqs, num_tokens, num_heads, k_pool.shape[1],
                                       device=q.device)
+    _require(workspace.is_contiguous(), "workspace must be contiguous")
     variant = _variant(window, alibi_slopes, num_heads)
     _check(load().pa_prefill(ctypes.byref(cache), _ptr(q), _ptr(block_tables), _ptr(query_start),
                              _ptr(context_lens), num_seqs, num_tokens, num_heads,
@@ -455,6 +480,9 @@ def pa_splitkv_reduce(part_out, part_max, part_sum, context_lens, partition_size
              "context_lens must be int32 [num_seqs]")
     _require(out.is_contiguous() and tuple(out.shape) == (num_seqs, num_heads, head_dim),
              "out must be contiguous [num_seqs][num_heads][head_dim]")
+    _require(context_lens.is_contiguous(), "context_lens must be contiguous")
+    _on_device(part_out=part_out, part_max=part_max, part_sum=part_sum,
+               context_lens=context_lens, out=out, lse=lse)
     if lse is not None:
         _require(lse.dtype == torch.float32 and lse.is_contiguous() and
                  tuple(lse.shape) == (num_seqs, num_heads), "lse must be float32 [num_seqs][num_heads]")

@@ -308,3 +308,93 @@ def test_prefill_rejects_bad_arguments():
 
 def test_variant_struct_layout():
     assert ctypes.sizeof(lib.PaAttnVariant) == 16 and lib.PaAttnVariant.alibi_slopes.offset == 8
+
+
+# --- host memory is refused before anything reaches a kernel ---------------
+
+def _host_buffers(n=4, nbytes=1 << 16):
+    import numpy as np
+    bufs = [np.zeros(nbytes, np.uint8) for _ in range(n)]
+    return bufs, [b.ctypes.data + (-b.ctypes.data) % 256 for b in bufs]
+
+
+def test_c_abi_refuses_host_pointers():
+    """Arguments that pass every other check but point at ordinary host
+    memory: each entry point refuses them (PA_ERR_SHAPE) instead of handing
+    them to a kernel."""
+    bufs, (p0, p1, p2, p3) = _host_buffers()
+    c = _cache(k_pool=p0, v_pool=p1)
+    call = lib.raw_call
+    results = {
+        "pa_kv_append": call("pa_kv_append", ctypes.byref(c), p2, p3, p2, 1, None),
+        "pa_copy_blocks": call("pa_copy_blocks", ctypes.byref(c), p2, 1, None),
+        "pa_decode": _decode(c, q=p2, tables=p3, lens=p3, out=p2),
+        "pa_decode_append": _decode_append(c, q=p2, k_new=p3, v_new=p3, tables=p3, lens=p3,
+                                           out=p2),
+        "pa_decode_partitions": _partitions(c, q=p2, tables=p3, lens=p3, po=p2, pm=p3, ps=p3),
+        "pa_splitkv_reduce": call("pa_splitkv_reduce", p0, p1, p2, p3, 1, 4, 128, 2, 16, p0,
+                                  lib.PA_F32, None, None),
+    }
+    for name, status in results.items():
+        assert status == 2, (name, status)
+    msg = lib.load().pa_last_error().decode()
+    assert msg.startswith("pa_splitkv_reduce:") and "device" in msg or "HIP runtime" in msg
+    pf = call("pa_prefill", ctypes.byref(_cache(k_pool=p0, v_pool=p1, num_kv_heads=2)), p2, p3,
+              p3, p3, 2, 10, 8, 4, 0.1, None, p2, lib.PA_F32, p0, 4096, None)
+    assert pf == 2
+    del bufs
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    k = torch.zeros((4, 2, 16, 128), dtype=torch.bfloat16)
+    q = torch.zeros((1, 4, 128), dtype=torch.bfloat16)
+    tables = torch.zeros((1, 4), dtype=torch.int32)
+    lens = torch.ones(1, dtype=torch.int32)
+    with pytest.raises(ValueError, match="device tensor"):
+        lib.pa_decode(k, k.clone(), q, tables, lens, 0.1, torch.empty_like(q))
+    with pytest.raises(ValueError, match="device tensor"):
+        lib.pa_kv_append(k, k.clone(), torch.zeros((1, 2, 128), dtype=torch.bfloat16),
+                         torch.zeros((1, 2, 128), dtype=torch.bfloat16),
+                         torch.zeros(1, dtype=torch.int64))
+    with pytest.raises(ValueError, match="device tensor"):
+        lib.pa_copy_blocks(k, k.clone(), torch.zeros((1, 2), dtype=torch.int64))
+    with pytest.raises(ValueError, match="device tensor"):
+        lib.pa_prefill(k, k.clone(), q, tables, torch.tensor([0, 1], dtype=torch.int32), lens,
+                       0.1, torch.empty_like(q), workspace=torch.zeros(64, dtype=torch.uint8))
+    po = torch.zeros((1, 4, 2, 128))
+    with pytest.raises(ValueError, match="device tensor"):
+        lib.pa_splitkv_reduce(po, torch.zeros((1, 4, 2)), torch.zeros((1, 4, 2)), lens, 16,
+                              torch.zeros((1, 4, 128)))
+
+
+def test_prefill_binding_checks_shapes(monkeypatch):
+    """pa_prefill's binding checks q's head_dim against the pools, the output
+    type and the index arrays before any call (a 64-dim q over 128-dim pools
+    would be read and written past its end)."""
+    import torch
+    monkeypatch.setattr(lib, "_on_device", lambda **kw: None)
+
+    class NoCall:
+        def __getattr__(self, name):
+            raise AssertionError(f"{name} reached the library")
+    monkeypatch.setattr(lib, "load", lambda *a: NoCall())
+    k = torch.zeros((4, 2, 16, 128), dtype=torch.bfloat16)
+    tables = torch.zeros((1, 4), dtype=torch.int32)
+    lens = torch.ones(1, dtype=torch.int32)
+    qs = torch.tensor([0, 1], dtype=torch.int32)
+    ws = torch.zeros(64, dtype=torch.uint8)
+    q64 = torch.zeros((1, 4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="head_dim"):
+        lib.pa_prefill(k, k.clone(), q64, tables, qs, lens, 0.1, torch.empty_like(q64),
+                       workspace=ws)
+    q = torch.zeros((1, 4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="float32 or bfloat16"):
+        lib.pa_prefill(k, k.clone(), q, tables, qs, lens, 0.1,
+                       torch.zeros((1, 4, 128), dtype=torch.float16), workspace=ws)
+    with pytest.raises(ValueError, match="query_start"):
+        lib.pa_prefill(k, k.clone(), q, tables, torch.zeros((2, 2), dtype=torch.int32)[:, 0],
+                       lens, 0.1, torch.empty_like(q), workspace=ws)
+    with pytest.raises(ValueError, match="context_lens"):
+        lib.pa_prefill(k, k.clone(), q, tables, qs, torch.ones(1, dtype=torch.int64), 0.1,
+                       torch.empty_like(q), workspace=ws)
