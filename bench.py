@@ -381,6 +381,75 @@ def bench_prefill(args) -> dict:
     }
 
 
+def event_times(fn, n: int) -> list:
+    """Per-call durations (us) of n calls, each bracketed by its own pair of
+    HIP events on the current stream (for medians and percentiles; the mean
+    of back-to-back calls is timed without events in between)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in evs]
+
+
+def pct(xs, q: float) -> float:
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
+
+
+def bench_stream(args) -> dict:
+    """The streaming-read probe (pa_probe_stream_read): one read of a buffer
+    of --stream-mib MiB, the achievable HBM read rate the decode figures are
+    compared with.  Grids of 1, 2 and 4 workgroups of 512 lanes per CU; the
+    best is the ceiling.  With --xcd-masks, the same read by subsets of the
+    eight XCDs (does one XCD's share of bandwidth grow when others idle?)."""
+    nbytes = args.stream_mib * (1 << 20)
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.random_(0, 255)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rows, best = {}, None
+    masks = [0xFF] + [int(m, 0) for m in args.xcd_masks.split(",") if m] if args.xcd_masks else [0xFF]
+    for per_cu in (1, 2, 4):
+        groups = cus * per_cu
+        sink = torch.empty(groups * 16, dtype=torch.uint8, device="cuda")
+        for mask in masks:
+            call = lambda i, m=mask, g=groups, k=sink: lib.probe_stream_read(src, g, k, m)
+            warm_up(call, args.warmup)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(args.steps):
+                call(i)
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / args.steps * 1e3
+            per = event_times(call, min(args.steps, 100))
+            key = f"{per_cu}_per_cu" + ("" if mask == 0xFF else f"_xcd_{mask:#04x}")
+            rows[key] = dict(us=round(us, 2), gbps=round(nbytes / (us * 1e-6) / 1e9, 1),
+                             median_us=round(pct(per, 50), 2), p10_us=round(pct(per, 10), 2),
+                             p90_us=round(pct(per, 90), 2), workgroups=groups,
+                             xcds=bin(mask).count("1"))
+            print(f"# stream {key}: {us:.1f} us, {rows[key]['gbps']:.0f} GB/s", file=sys.stderr,
+                  flush=True)
+            if mask == 0xFF and (best is None or rows[key]["gbps"] > rows[best]["gbps"]):
+                best = key
+    return {
+        "metric": "streaming HBM read GB/s (pa_probe_stream_read), the ceiling decode is "
+                  "compared with",
+        "value": rows[best]["gbps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "vs_baseline": None, "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": f"one read of {args.stream_mib} MiB, 16-byte non-temporal "
+                               f"loads, 64 KiB slices per workgroup step", "best_grid": best},
+        "grids": rows,
+        "roofline": {"bound": "hbm", "kernel": "stream_read_kernel",
+                     "achieved": rows[best]["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(rows[best]["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None},
+    }
+
+
 class ServingTrace:
     """Seeded serving workload for the block manager at the batch-64 scale.
 
@@ -533,7 +602,14 @@ def main() -> int:
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from two --pmc-pass counter runs")
     ap.add_argument("--pmc-command", default="", help="command line recorded in the summary")
-    ap.add_argument("--part", default="decode", choices=["decode", "swap", "scheduler", "prefill"],
+    ap.add_argument("--ceiling", type=int, default=1,
+                    help="decode: also time the streaming-read probe (the read ceiling)")
+    ap.add_argument("--stream-mib", type=int, default=2048,
+                    help="stream: MiB read per probe call")
+    ap.add_argument("--xcd-masks", default="",
+                    help="stream: comma-separated XCD bit masks to time besides all eight")
+    ap.add_argument("--part", default="decode",
+                    choices=["decode", "swap", "scheduler", "prefill", "stream"],
                     help="decode: the decode step (default); swap: block swaps to pinned host "
                          "memory; scheduler: the host block manager (no GPU needed)")
     ap.add_argument("--swap-blocks", type=int, default=1024, help="blocks per swap launch")
@@ -569,6 +645,9 @@ def main() -> int:
         return 0
     if args.part == "prefill":
         print(json.dumps(bench_prefill(args)), flush=True)
+        return 0
+    if args.part == "stream":
+        print(json.dumps(bench_stream(args)), flush=True)
         return 0
 
     w = W.make_config(args.workload, dtype=args.dtype, block_size=args.block_size,
@@ -607,7 +686,7 @@ def main() -> int:
     ps = torch.empty_like(pm)
     ws = None
     if mode == "balanced":
-        ws = lib.decode_workspace(w.num_seqs, w.num_heads, w.head_dim)
+        ws = lib.decode_workspace(w.num_seqs, w.num_heads, w.head_dim, k_pool=k0, v_pool=v0)
 
     def decode(r):
         kp, vp = pools[r]
@@ -673,6 +752,19 @@ def main() -> int:
     # timed region 2: the decode launches alone, back to back (roofline)
     warm_decode = warm_up(decode, args.warmup, args.rotate)
     dec_avg = timed(decode, args.steps)
+    # per-launch spread: each launch between its own pair of events (these
+    # durations include an event's own cost, ~1-2 us; the mean above has none)
+    per_launch = event_times(lambda i: decode(i % args.rotate), min(args.steps, 200))
+    ceiling = None
+    if args.ceiling:
+        # the streaming-read probe on this GPU, over a 2 GiB buffer
+        src = torch.empty(1 << 31, dtype=torch.uint8, device="cuda")
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        sink = torch.empty(cus * 16, dtype=torch.uint8, device="cuda")
+        probe = lambda i: lib.probe_stream_read(src, cus, sink)
+        warm_up(probe, 5)
+        ceiling = round(float(src.numel()) / (timed(probe, 20) * 1e-3) / 1e9, 1)
+        del src
     # (a kernel trace of this run splits its dispatches by these counts)
     print(f"# regions: steps {warm_steps} warm-up + {args.steps} timed; decode {warm_decode} "
           f"warm-up + {args.steps} timed", file=sys.stderr, flush=True)
@@ -707,13 +799,24 @@ def main() -> int:
         "hbm_peak_frac_step": round(kv_gbps_step / HBM_PEAK_GBPS, 4),
         "kv_bytes": nbytes["kv"],
         "decode_us": round(dec_avg * 1e3, 2),
+        "decode_us_per_launch": {"median": round(pct(per_launch, 50), 2),
+                                 "p10": round(pct(per_launch, 10), 2),
+                                 "p90": round(pct(per_launch, 90), 2), "launches": len(per_launch)},
         "kv_gbps_decode": round(nbytes["kv"] / (dec_avg * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": kernels, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None if variant else read_traffic(w.name, str(mode)),
-                     "algorithmic_bytes_per_launch": decode_bytes},
+                     "algorithmic_bytes_per_launch": decode_bytes,
+                     "stream_ceiling_gbps": ceiling,
+                     "frac_of_ceiling": round(achieved / ceiling, 4) if ceiling else None},
     }
+    if w.info.get("shared_blocks") is not None:
+        # shared prefix: each shared block is read by every sequence's walk;
+        # the unique bytes are what a reader of every block once would move
+        uniq = w.unique_kv_bytes()
+        result["kv_bytes_unique"] = uniq
+        result["kv_gbps_decode_unique"] = round(uniq / (dec_avg * 1e-3) / 1e9, 1)
     if args.cpu_budget > 0:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, args.window, args.alibi)
     print(json.dumps(result), flush=True)

@@ -258,9 +258,17 @@ int pa_decode_append(const pa_cache *cache, const void *q, const void *k_new, co
                      const pa_attn_variant *variant, void *out, int32_t out_dtype,
                      void *workspace, size_t workspace_bytes, void *stream);
 
-/* Workspace bytes pa_decode needs on the current device for these sizes
- * (0 for a negative or zero size). */
+/* Workspace bytes pa_decode needs on the current device for these sizes,
+ * whatever the pools (0 for a negative or zero size): a bound over every
+ * element type, block size and KV-head count.  pa_decode_workspace_size gives
+ * the exact need for given pools. */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim);
+
+/* Workspace bytes pa_decode (and pa_decode_append) need on the current device
+ * for this cache and these sizes; 0 for sizes pa_decode refuses.  The
+ * workspace holds the split description and one partial row per (workgroup
+ * + sequence, query head) for the parts of split sequences. */
+size_t pa_decode_workspace_size(const pa_cache *cache, int32_t num_seqs, int32_t num_heads);
 
 /*
  * pa_prefill - causal attention of a mixed batch: many query tokens per

@@ -1,6 +1,8 @@
 // pa_decode, pa_decode_partitions, pa_decode_workspace_bytes: host-side
 // validation, work decomposition and launch of the decode kernels.
+#include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "pa_decode_kernel.h"
 #include "pa_internal.h"
@@ -40,6 +42,30 @@ int balanced_groups(const pa_cache* cache, int group, int waves, size_t lds) {
   if (per_cu < 1) per_cu = 1;
   if (per_cu > kMaxGroupsPerCu) per_cu = kMaxGroupsPerCu;
   return device_cus() * per_cu;
+}
+
+// The most one-wave workgroups any decode instantiation fits on a CU (its
+// smallest LDS), for the workspace bound that does not know the pools;
+// queried once.
+int max_groups_per_cu() {
+  static std::once_flag once;
+  static int best = 1;
+  std::call_once(once, [] {
+    for (int et : {kF32, kBF16, kFP8})
+      for (int d : {64, 128})
+        for (int bs : {8, 16, 32})
+          for (int g : {1, 2, 3, 4, 5, 6, 7, 8, 16}) {
+            if (!decode_group_supported(et, d, bs, g)) continue;
+            const size_t lds =
+                decode_prefix_lds_bytes(1, true) + decode_wave_lds_bytes(et, d, g, bs);
+            const int n = et == kBF16  ? decode_groups_per_cu_bf16(d, bs, g, 1, lds)
+                          : et == kFP8 ? decode_groups_per_cu_fp8(d, bs, g, 1, lds)
+                                       : decode_groups_per_cu_f32(d, bs, g, 1, lds);
+            best = std::max(best, n);
+          }
+    best = std::min(best, kMaxGroupsPerCu);
+  });
+  return best;
 }
 
 constexpr size_t kAlign = 256;
@@ -142,7 +168,26 @@ constexpr int kMaxBalancedSeqs = 16000;  // the unit prefix of all sequences liv
 PA_API size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim) {
   using namespace pa;
   if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0) return 0;
-  return layout_for(int64_t(device_cus()) * kMaxGroupsPerCu, num_seqs, num_heads, head_dim).total;
+  return layout_for(int64_t(device_cus()) * max_groups_per_cu(), num_seqs, num_heads, head_dim)
+      .total;
+}
+
+PA_API size_t pa_decode_workspace_size(const pa_cache* cache, int32_t num_seqs,
+                                       int32_t num_heads) {
+  using namespace pa;
+  if (!cache || num_seqs < 0 || num_heads <= 0 || cache->num_kv_heads <= 0 ||
+      num_heads % cache->num_kv_heads != 0 || cache->head_dim <= 0)
+    return 0;
+  const int group = num_heads / cache->num_kv_heads;
+  const int et = elem_type(cache->dtype);
+  if (!decode_group_supported(et, cache->head_dim, cache->block_size, group)) return 0;
+  const int waves = waves_per_group(cache->num_kv_heads);
+  const size_t lds =
+      decode_prefix_lds_bytes(num_seqs, true) +
+      size_t(waves) * decode_wave_lds_bytes(et, cache->head_dim, group, cache->block_size);
+  return layout_for(balanced_groups(cache, group, waves, lds), num_seqs, num_heads,
+                    cache->head_dim)
+      .total;
 }
 
 namespace pa {

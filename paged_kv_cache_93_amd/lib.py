@@ -29,9 +29,9 @@ STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSU
 # Every symbol include/pagedattn.h and include/pa_block_manager.h declare.
 EXPORTED = ("pa_abi_version", "pa_hip_runtime_version", "pa_last_error", "pa_kv_append",
             "pa_copy_blocks", "pa_swap_blocks", "pa_decode", "pa_decode_append",
-            "pa_decode_workspace_bytes",
+            "pa_decode_workspace_bytes", "pa_decode_workspace_size",
             "pa_decode_partitions", "pa_splitkv_reduce", "pa_partials_bytes", "pa_prefill",
-            "pa_prefill_workspace_bytes",
+            "pa_prefill_workspace_bytes", "pa_probe_stream_read",
             "pa_bm_create", "pa_bm_destroy", "pa_bm_add_request", "pa_bm_append_tokens",
             "pa_bm_append_batch",
             "pa_bm_fork", "pa_bm_finish", "pa_bm_schedule", "pa_bm_get_stats",
@@ -111,6 +111,7 @@ _SIGNATURES = {
                                         _i32, _i32, _f32, ctypes.POINTER(PaAttnVariant), _vp,
                                         _i32, _vp, ctypes.c_size_t, _vp]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32]),
+    "pa_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(PaCache), _i32, _i32]),
     "pa_decode_partitions": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _vp, _vp, _i32, _i32,
                                             _i32, _f32, _i32, _vp, _vp, _vp, _i32, _vp]),
     "pa_splitkv_reduce": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp,
@@ -120,6 +121,7 @@ _SIGNATURES = {
                                   _i32, _f32, ctypes.POINTER(PaAttnVariant), _vp, _i32, _vp,
                                   ctypes.c_size_t, _vp]),
     "pa_prefill_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32]),
+    "pa_probe_stream_read": (ctypes.c_int, [_vp, ctypes.c_size_t, _i32, _i32, _vp, _vp]),
     "pa_bm_create": (ctypes.c_int, [ctypes.POINTER(PaBmConfig), ctypes.POINTER(_vp)]),
     "pa_bm_destroy": (None, [_vp]),
     "pa_bm_add_request": (ctypes.c_int, [_vp, _i64, _vp, _i64]),
@@ -291,15 +293,26 @@ def pa_swap_blocks(k_pool, v_pool, host_k_pool, host_v_pool, block_pairs, direct
 
 
 def decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int) -> int:
-    """Bytes of workspace pa_decode needs on the current device."""
+    """Bytes of workspace pa_decode needs on the current device, for any pools."""
     return load().pa_decode_workspace_bytes(num_seqs, num_heads, head_dim)
 
 
-def decode_workspace(num_seqs: int, num_heads: int, head_dim: int,
-                     device="cuda") -> torch.Tensor:
-    """A workspace for pa_decode (allocated through torch; contents irrelevant)."""
-    return torch.empty(decode_workspace_bytes(num_seqs, num_heads, head_dim),
-                       dtype=torch.uint8, device=device)
+def decode_workspace_size(k_pool, v_pool, num_seqs: int, num_heads: int) -> int:
+    """Bytes of workspace pa_decode needs for these pools on the current device."""
+    cache = make_cache(k_pool, v_pool)
+    return load().pa_decode_workspace_size(ctypes.byref(cache), num_seqs, num_heads)
+
+
+def decode_workspace(num_seqs: int, num_heads: int, head_dim: int, device="cuda",
+                     k_pool=None, v_pool=None) -> torch.Tensor:
+    """A workspace for pa_decode (allocated through torch; contents irrelevant):
+    sized exactly for the pools when they are given, else for any pools."""
+    if k_pool is not None:
+        n = decode_workspace_size(k_pool, v_pool if v_pool is not None else k_pool, num_seqs,
+                                  num_heads)
+    else:
+        n = decode_workspace_bytes(num_seqs, num_heads, head_dim)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def _decode_common(k_pool, v_pool, q, block_tables, context_lens, k_scale, v_scale):
@@ -626,6 +639,19 @@ class BlockManager:
         out = np.zeros(self.num_gpu_blocks, dtype=np.int32)
         _check(load().pa_bm_refcounts(self._h, out.ctypes.data, out.size))
         return out.tolist()
+
+
+def probe_stream_read(src: torch.Tensor, workgroups: int, sink: torch.Tensor,
+                      xcd_mask: int = 0xFF, stream=None) -> None:
+    """Read all of src (device, contiguous, a multiple of 64 KiB) once with
+    the streaming-read probe; sink receives 16 bytes per workgroup."""
+    _on_device(src=src, sink=sink)
+    _require(src.is_contiguous() and sink.is_contiguous() and
+             sink.numel() * sink.element_size() >= 16 * workgroups,
+             "src contiguous; sink contiguous with 16 bytes per workgroup")
+    _check(load().pa_probe_stream_read(_ptr(src), src.numel() * src.element_size(),
+                                       int(workgroups), int(xcd_mask), _ptr(sink),
+                                       _stream(stream)))
 
 
 def raw_call(name: str, *args) -> int:

@@ -398,3 +398,31 @@ def test_prefill_binding_checks_shapes(monkeypatch):
     with pytest.raises(ValueError, match="context_lens"):
         lib.pa_prefill(k, k.clone(), q, tables, qs, torch.ones(1, dtype=torch.int64), 0.1,
                        torch.empty_like(q), workspace=ws)
+
+
+def test_workspace_size_for_pools():
+    call = lib.raw_call
+    c = _cache()
+    assert call("pa_decode_workspace_size", None, 4, 4) == 0
+    assert call("pa_decode_workspace_size", ctypes.byref(c), -1, 4) == 0
+    assert call("pa_decode_workspace_size", ctypes.byref(c), 4, 3) == 0     # not a multiple
+    assert call("pa_decode_workspace_size", ctypes.byref(c), 4, 18) == 0    # 9 per KV head
+    n = call("pa_decode_workspace_size", ctypes.byref(c), 64, 8)
+    assert 0 < n <= lib.decode_workspace_bytes(64, 8, 128)
+    # at least the piece rows of every sequence
+    assert n >= 64 * 8 * 130 * 4
+
+
+def test_probe_rejects_bad_arguments():
+    call = lib.raw_call
+    bufs, (p0, p1) = _host_buffers(2, 1 << 17)
+    assert call("pa_probe_stream_read", p0, 0, 8, 0xFF, p1, None) == 0       # nothing to read
+    assert call("pa_probe_stream_read", None, 65536, 8, 0xFF, p1, None) == 1
+    assert call("pa_probe_stream_read", p0, 65536, 8, 0xFF, None, None) == 1
+    assert call("pa_probe_stream_read", p0, 1000, 8, 0xFF, p1, None) == 2    # not 64 KiB slices
+    assert call("pa_probe_stream_read", p0 + 8, 65536, 8, 0xFF, p1, None) == 2
+    assert call("pa_probe_stream_read", p0, 65536, 4, 0xFF, p1, None) == 2   # < 8 workgroups
+    assert call("pa_probe_stream_read", p0, 65536, 8, 0x100, p1, None) == 2  # no XCD selected
+    assert call("pa_probe_stream_read", p0, 65536, 8, 0xFF, p1, None) == 2   # host memory
+    del bufs
+

@@ -355,3 +355,33 @@ def test_workspace_is_reusable_scratch():
                           t["context_lens"], 1 / math.sqrt(128), out, workspace=ws)
             torch.cuda.synchronize()
             assert max_abs_err(out, ref) <= 1e-5, (k, n, fill)
+
+
+@pytest.mark.parametrize("k,dtype", [(2, "bf16"), (4, "fp8"), (1, "f32")])
+def test_exact_workspace_size(k, dtype):
+    """pa_decode_workspace_size gives the exact need for the pools: a workspace
+    of that size serves the call (same bits as a larger one), one 256 bytes
+    smaller is refused with PA_ERR_WORKSPACE, and the pool-independent bound
+    is never smaller."""
+    w = W.make_config(k, dtype=dtype) if k == 1 else W.make_config(k, dtype=dtype, num_seqs=16)
+    t = upload(w)
+    run_writes(t)
+    need = lib.decode_workspace_size(t["k_pool"], t["v_pool"], w.num_seqs, w.num_heads)
+    bound = lib.decode_workspace_bytes(w.num_seqs, w.num_heads, w.head_dim)
+    assert 0 < need <= bound
+    scale = 1 / math.sqrt(w.head_dim)
+    outs = []
+    for n in (need, bound):
+        out = torch.empty((w.num_seqs, w.num_heads, w.head_dim), dtype=torch.float32,
+                          device="cuda")
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        lib.pa_decode(t["k_pool"], t["v_pool"], t["q"], t["block_tables"], t["context_lens"],
+                      scale, out, workspace=ws, k_scale=w.k_scale, v_scale=w.v_scale)
+        outs.append(out)
+    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(lib.PagedAttnError) as e:
+        lib.pa_decode(t["k_pool"], t["v_pool"], t["q"], t["block_tables"], t["context_lens"],
+                      scale, outs[0], workspace=small, k_scale=w.k_scale, v_scale=w.v_scale)
+    assert e.value.status == 4
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
