@@ -234,6 +234,29 @@ int pa_decode(const pa_cache *cache, const void *q, const int32_t *block_tables,
               void *stream);
 
 /*
+ * pa_decode_static - pa_decode with the balanced split, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).
+ *
+ * The same computation, kernels and results, bit for bit, as pa_decode with
+ * a workspace; the workspace is instead a 32 MiB array inside the library,
+ * one per device, allocated when the library's device code is loaded and
+ * held until the process ends.  The call allocates and frees nothing.  All
+ * calls on one device share that array: calls that overlap in time on one
+ * device (other streams, other host threads) race and give wrong results;
+ * calls on different devices do not.  Nothing in the array needs to start at
+ * any value.  Sizes whose split needs more than 32 MiB (roughly
+ * (1,024 + num_seqs) * num_heads rows of head_dim + 2 floats on a 256-CU
+ * device) return PA_ERR_WORKSPACE; more than 16,000 sequences take the
+ * single-pass walk, which needs no scratch.  Other arguments and errors are
+ * those of pa_decode.
+ */
+int pa_decode_static(const pa_cache *cache, const void *q, const int32_t *block_tables,
+                     const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+                     int32_t max_blocks_per_seq, float scale, const pa_attn_variant *variant,
+                     void *out, int32_t out_dtype, void *stream);
+
+/*
  * pa_decode_append - one decode step in one launch: the append of every
  * sequence's new token, then pa_decode.
  *

@@ -162,6 +162,39 @@ int launch(const char* fn, const pa_cache* cache, int group, const DecodeArgs& a
 
 constexpr int kMaxBalancedSeqs = 16000;  // the unit prefix of all sequences lives in LDS
 
+// The scratch of pa_decode_static: the balanced split's workspace in a
+// file-scope device array (each device holds its own copy until the process
+// ends), for callers that cannot allocate.  Host code uses the address
+// hipGetSymbolAddress gives on each device, never the array's name.
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, taken once per device
+// with that device current; nullptr (with the message set) on failure.
+void* scratch_address(const char* fn) {
+  static std::mutex lock;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    fail(PA_ERR_LAUNCH, "%s: no usable current HIP device", fn);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> guard(lock);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      fail(PA_ERR_LAUNCH, "%s: the static scratch has no address on device %d", fn, dev);
+      return nullptr;
+    }
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
 }  // namespace
 }  // namespace pa
 
@@ -193,12 +226,14 @@ PA_API size_t pa_decode_workspace_size(const pa_cache* cache, int32_t num_seqs,
 namespace pa {
 namespace {
 
-// pa_decode, and pa_decode_append when k_new / v_new are given.
+// pa_decode, pa_decode_append when k_new / v_new are given, and
+// pa_decode_static when static_scratch is set (the workspace is then the
+// file-scope scratch array, and `workspace` is ignored).
 int decode_call(const char* fn, const pa_cache* cache, const void* q, const void* k_new,
                 const void* v_new, const int32_t* block_tables, const int32_t* context_lens,
                 int32_t num_seqs, int32_t num_heads, int32_t max_blocks_per_seq, float scale,
                 const pa_attn_variant* variant, void* out, int32_t out_dtype, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                size_t workspace_bytes, void* stream, bool static_scratch = false) {
   DecodeArgs a;
   int group = 0;
   if (int st = prepare(fn, cache, q, block_tables, context_lens, num_seqs, num_heads,
@@ -233,7 +268,8 @@ int decode_call(const char* fn, const pa_cache* cache, const void* q, const void
     return check_device_memory(
         fn, {{"k_pool", cache->k_pool}, {"v_pool", cache->v_pool}, {"q", q},
              {"block_tables", block_tables}, {"context_lens", context_lens}, {"out", out},
-             {"workspace", workspace}, {"k_new", k_new}, {"v_new", v_new},
+             {"workspace", static_scratch ? nullptr : workspace}, {"k_new", k_new},
+             {"v_new", v_new},
              {"alibi_slopes", a.alibi}, {"k_scales", cache->k_scales},
              {"v_scales", cache->v_scales}});
   };
@@ -245,7 +281,8 @@ int decode_call(const char* fn, const pa_cache* cache, const void* q, const void
 
   const size_t wave_lds =
       size_t(waves) * decode_wave_lds_bytes(elem_type(cache->dtype), cache->head_dim, group, cache->block_size);
-  if (workspace == nullptr || num_seqs > kMaxBalancedSeqs) {
+  if (static_scratch) workspace = nullptr;
+  if ((workspace == nullptr && !static_scratch) || num_seqs > kMaxBalancedSeqs) {
     a.mode = kModeSingle;
     if (int st = check_memory()) return st;
     return launch(fn, cache, group, a, dim3(unsigned(num_seqs), head_groups), waves, wave_lds, s);
@@ -253,6 +290,15 @@ int decode_call(const char* fn, const pa_cache* cache, const void* q, const void
   const size_t lds = decode_prefix_lds_bytes(num_seqs, true) + wave_lds;
   const int groups = balanced_groups(cache, group, waves, lds);
   const WorkspaceLayout w = layout_for(groups, num_seqs, num_heads, cache->head_dim);
+  if (static_scratch) {
+    if (w.total > kStaticScratchBytes)
+      return fail(PA_ERR_WORKSPACE,
+                  "%s: these sizes need %zu bytes of scratch, more than the static %zu", fn,
+                  w.total, kStaticScratchBytes);
+    workspace = scratch_address(fn);
+    if (workspace == nullptr) return PA_ERR_LAUNCH;
+    workspace_bytes = kStaticScratchBytes;
+  }
   if (workspace_bytes < w.total)
     return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes is smaller than the %zu needed", fn,
                 workspace_bytes, w.total);
@@ -295,6 +341,16 @@ PA_API int pa_decode(const pa_cache* cache, const void* q, const int32_t* block_
   return pa::decode_call("pa_decode", cache, q, nullptr, nullptr, block_tables, context_lens,
                          num_seqs, num_heads, max_blocks_per_seq, scale, variant, out, out_dtype,
                          workspace, workspace_bytes, stream);
+}
+
+PA_API int pa_decode_static(const pa_cache* cache, const void* q, const int32_t* block_tables,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                            int32_t max_blocks_per_seq, float scale,
+                            const pa_attn_variant* variant, void* out, int32_t out_dtype,
+                            void* stream) {
+  return pa::decode_call("pa_decode_static", cache, q, nullptr, nullptr, block_tables,
+                         context_lens, num_seqs, num_heads, max_blocks_per_seq, scale, variant,
+                         out, out_dtype, nullptr, 0, stream, true);
 }
 
 PA_API int pa_decode_append(const pa_cache* cache, const void* q, const void* k_new,

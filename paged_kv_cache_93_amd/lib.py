@@ -29,6 +29,7 @@ STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSU
 # Every symbol include/pagedattn.h and include/pa_block_manager.h declare.
 EXPORTED = ("pa_abi_version", "pa_hip_runtime_version", "pa_last_error", "pa_kv_append",
             "pa_copy_blocks", "pa_swap_blocks", "pa_decode", "pa_decode_append",
+            "pa_decode_static",
             "pa_decode_workspace_bytes", "pa_decode_workspace_size",
             "pa_decode_partitions", "pa_splitkv_reduce", "pa_partials_bytes", "pa_prefill",
             "pa_prefill_workspace_bytes", "pa_probe_stream_read",
@@ -107,6 +108,9 @@ _SIGNATURES = {
     "pa_decode": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _vp, _vp, _i32, _i32, _i32, _f32,
                                  ctypes.POINTER(PaAttnVariant), _vp, _i32, _vp, ctypes.c_size_t,
                                  _vp]),
+    "pa_decode_static": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _vp, _vp, _i32, _i32,
+                                        _i32, _f32, ctypes.POINTER(PaAttnVariant), _vp, _i32,
+                                        _vp]),
     "pa_decode_append": (ctypes.c_int, [ctypes.POINTER(PaCache), _vp, _vp, _vp, _vp, _vp, _i32,
                                         _i32, _i32, _f32, ctypes.POINTER(PaAttnVariant), _vp,
                                         _i32, _vp, ctypes.c_size_t, _vp]),
@@ -367,6 +371,24 @@ def pa_decode(k_pool, v_pool, q, block_tables, context_lens, scale: float, out, 
                             num_seqs, num_heads, block_tables.shape[1], float(scale),
                             _variant(window, alibi_slopes, num_heads), _ptr(out),
                             _dtype_code(out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def pa_decode_static(k_pool, v_pool, q, block_tables, context_lens, scale: float, out,
+                     stream=None, k_scale=1.0, v_scale=1.0, window: int = 0,
+                     alibi_slopes=None) -> None:
+    """pa_decode's balanced split over the library's own device scratch (no
+    workspace argument, nothing allocated); see include/pagedattn.h."""
+    cache = _decode_common(k_pool, v_pool, q, block_tables, context_lens, k_scale, v_scale)
+    num_seqs, num_heads = q.shape[0], q.shape[1]
+    _require(out is not None and out.is_contiguous() and
+             tuple(out.shape) == (num_seqs, num_heads, cache.head_dim),
+             "out must be contiguous [num_seqs][num_heads][head_dim]")
+    _on_device(out=out)
+    _check(load().pa_decode_static(ctypes.byref(cache), _ptr(q), _ptr(block_tables),
+                                   _ptr(context_lens), num_seqs, num_heads,
+                                   block_tables.shape[1], float(scale),
+                                   _variant(window, alibi_slopes, num_heads), _ptr(out),
+                                   _dtype_code(out), _stream(stream)))
 
 
 def pa_decode_append(k_pool, v_pool, q, k_new, v_new, block_tables, context_lens, scale: float,

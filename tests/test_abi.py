@@ -426,3 +426,29 @@ def test_probe_rejects_bad_arguments():
     assert call("pa_probe_stream_read", p0, 65536, 8, 0xFF, p1, None) == 2   # host memory
     del bufs
 
+
+def _decode_static(cache, **kw):
+    a = dict(q=16, tables=16, lens=16, num_seqs=1, num_heads=4, max_blocks=4, scale=0.1,
+             variant=None, out=16, out_dtype=lib.PA_BF16)
+    a.update(kw)
+    return lib.raw_call("pa_decode_static", ctypes.byref(cache) if cache is not None else None,
+                        a["q"], a["tables"], a["lens"], a["num_seqs"], a["num_heads"],
+                        a["max_blocks"], a["scale"], a["variant"], a["out"], a["out_dtype"], None)
+
+
+@pytest.mark.parametrize("cache_kw,call_kw,status", [
+    (None, {}, 1),
+    ({}, dict(num_heads=3), 2),
+    ({}, dict(out=0), 1),
+    ({}, dict(q=8), 2),
+    ({}, dict(scale=0.0), 2),
+    (dict(num_kv_heads=8), dict(num_seqs=12000, num_heads=64), 4),  # past the 32 MiB scratch
+])
+def test_decode_static_rejects_bad_arguments(cache_kw, call_kw, status):
+    cache = None if cache_kw is None else _cache(**cache_kw)
+    assert _decode_static(cache, **call_kw) == status
+    assert lib.load().pa_last_error().decode().startswith("pa_decode_static:")
+
+
+def test_decode_static_with_no_sequences_is_a_no_op():
+    assert _decode_static(_cache(), num_seqs=0, q=0, tables=0, lens=0) == 0
