@@ -374,10 +374,14 @@ int pa_decode_partitions(const pa_cache *cache, const void *q, const int32_t *bl
  * Partitions past a sequence's last are not read.  L_i = 0 gives out = 0 and
  * lse = -inf.
  *
- *   part_out, part_max, part_sum  DEVICE, as written by pa_decode_partitions
+ * Partitions whose part_sum is 0 take no part (their rows are not used).
+ *
+ *   part_out, part_max, part_sum  DEVICE, as written by pa_decode_partitions;
+ *                 part_out 16-byte aligned
  *   context_lens  DEVICE int32 [num_seqs], the same lengths pa_decode_partitions saw
- *   out           DEVICE [num_seqs][num_heads][head_dim] of out_dtype
+ *   out           DEVICE [num_seqs][num_heads][head_dim] of out_dtype, 16-byte aligned
  *   lse           DEVICE float [num_seqs][num_heads], or NULL
+ * Misaligned part_out or out give PA_ERR_SHAPE.
  */
 int pa_splitkv_reduce(const float *part_out, const float *part_max, const float *part_sum,
                       const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
