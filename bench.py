@@ -173,70 +173,153 @@ def read_traffic(workload: str, mode: str):
     return int(fields["hbm_bytes_per_launch"])
 
 
-def pmc_summary(fetch_dir: str, write_dir: str, workload: str, block_bytes: int, mode: str,
-                command: str) -> str:
-    """Summarise two rocprofv3 --pmc runs of ``--pmc-pass`` (FETCH_SIZE, then
-    WRITE_SIZE) into profiles/traffic_decode_<workload>_<mode>.md.
+def _counter_rows(d: str):
+    """(kernel key, counter, value) of every dispatch in a rocprofv3 --pmc run."""
+    import csv
+    import glob
+
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            name = row["Kernel_Name"]
+            key = next((k for k in ("decode_kernel", "merge_kernel", "reduce_kernel",
+                                    "copy_kernel") if k in name), None)
+            if key:
+                yield key, row["Counter_Name"], float(row["Counter_Value"])
+
+
+def pmc_summary(dirs, workload: str, block_bytes: int, mode: str, command: str) -> str:
+    """Summarise the rocprofv3 --pmc runs of ``--pmc-pass`` into
+    profiles/traffic_decode_<workload>_<mode>.md: FETCH_SIZE, then WRITE_SIZE,
+    then (optional third run) TCC_HIT_sum, TCC_MISS_sum and
+    TCC_EA0_RDREQ_DRAM_sum.
 
     The calibration copy moves a known number of bytes each way; the ratio of
     those bytes to the counter's reading for it scales the decode kernels'
-    readings to bytes."""
-    import csv
-    import glob
+    readings to bytes.  The L2 (TCC) hit rate is HIT / (HIT + MISS) over the
+    kernel's requests; DRAM read requests are the L2's reads that went to
+    HBM rather than another cache."""
     from collections import defaultdict
 
-    def per_kernel(d, counter):
-        vals = defaultdict(list)
-        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            for row in csv.DictReader(open(f)):
-                if row["Counter_Name"] != counter:
-                    continue
-                name = row["Kernel_Name"]
-                key = next((k for k in ("decode_kernel", "merge_kernel", "reduce_kernel",
-                                        "copy_kernel") if k in name), None)
-                if key:
-                    vals[key].append(float(row["Counter_Value"]))
-        return vals
-
-    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    vals = defaultdict(list)  # (kernel, counter) -> per-dispatch values
+    for d in dirs:
+        for key, counter, v in _counter_rows(d):
+            vals[(key, counter)].append(v)
+    mean = lambda v: sum(v) / len(v) if v else float("nan")
     cal_bytes = 2 * (CAL_BLOCKS // 2) * block_bytes
-    mean = lambda v: sum(v) / len(v)
-    f_factor = cal_bytes / (mean(fetch["copy_kernel"]) * 1024)
-    w_factor = cal_bytes / (mean(write["copy_kernel"]) * 1024)
-    kernels = [k for k in ("decode_kernel", "merge_kernel", "reduce_kernel") if k in fetch]
+    f_cal, w_cal = mean(vals[("copy_kernel", "FETCH_SIZE")]), mean(vals[("copy_kernel", "WRITE_SIZE")])
+    f_factor = cal_bytes / (f_cal * 1024)
+    w_factor = cal_bytes / (w_cal * 1024)
+    kernels = [k for k in ("decode_kernel", "merge_kernel", "reduce_kernel")
+               if vals[(k, "FETCH_SIZE")]]
+    has_tcc = any(vals[(k, "TCC_HIT_sum")] for k in kernels)
     rows, total = [], 0.0
     for k in kernels:
-        fb = mean(fetch[k]) * 1024 * f_factor
-        wb = mean(write[k]) * 1024 * w_factor
+        fk, wk = vals[(k, "FETCH_SIZE")], vals[(k, "WRITE_SIZE")]
+        fb = mean(fk) * 1024 * f_factor
+        wb = mean(wk) * 1024 * w_factor
         total += fb + wb
-        rows.append(f"| {k} | {len(fetch[k])} | {mean(fetch[k]):.1f} | {fb / 1e6:.2f} | "
-                    f"{mean(write[k]):.1f} | {wb / 1e6:.2f} |")
+        row = (f"| {k} | {len(fk)} | {mean(fk):.1f} | {fb / 1e6:.2f} | {mean(wk):.1f} | "
+               f"{wb / 1e6:.2f} |")
+        if has_tcc:
+            hit, miss = mean(vals[(k, "TCC_HIT_sum")]), mean(vals[(k, "TCC_MISS_sum")])
+            dram = mean(vals[(k, "TCC_EA0_RDREQ_DRAM_sum")])
+            rate = hit / (hit + miss) if hit + miss > 0 else float("nan")
+            row += f" {100 * rate:.1f} | {hit:.0f} | {miss:.0f} | {dram:.0f} |"
+        rows.append(row)
+    head = ("| kernel | dispatches | FETCH_SIZE KiB | read MB (scaled) | WRITE_SIZE KiB | "
+            "written MB (scaled) |")
+    rule = "|---|---|---|---|---|---|"
+    if has_tcc:
+        head += " TCC hit % | TCC_HIT | TCC_MISS | TCC_EA0_RDREQ_DRAM |"
+        rule += "---|---|---|---|"
+    dk = "decode_kernel"
+    extra = []
+    if has_tcc:
+        hit, miss = mean(vals[(dk, "TCC_HIT_sum")]), mean(vals[(dk, "TCC_MISS_sum")])
+        dram = mean(vals[(dk, "TCC_EA0_RDREQ_DRAM_sum")])
+        fetched = mean(vals[(dk, "FETCH_SIZE")]) * 1024 * f_factor
+        extra = [f"- tcc_hit_rate_decode: {hit / (hit + miss):.4f}",
+                 f"- dram_read_requests_decode: {dram:.0f}",
+                 f"- dram_read_bytes_decode_at_128B: {int(dram * 128)} "
+                 f"({dram * 128 / fetched:.3f} of the scaled FETCH_SIZE)"]
     text = "\n".join([
         f"# HBM traffic of one decode launch: {workload}, mode {mode}",
         "",
-        "Two rocprofv3 counter runs of the same program (`bench.py --pmc-pass`), one per counter:",
+        "rocprofv3 counter runs of the same program (`bench.py --pmc-pass`), one per counter set:",
         "",
         "```",
         command,
         "```",
         "",
         f"Calibration: the copy kernel moves {cal_bytes} bytes each way "
-        f"({CAL_BLOCKS // 2} blocks, K and V pools); it read FETCH_SIZE "
-        f"{mean(fetch['copy_kernel']):.1f} KiB and WRITE_SIZE {mean(write['copy_kernel']):.1f} KiB "
-        f"per dispatch, so FETCH_SIZE is scaled by {f_factor:.4f} and WRITE_SIZE by {w_factor:.4f}.",
+        f"({CAL_BLOCKS // 2} blocks, K and V pools); it read FETCH_SIZE {f_cal:.1f} KiB and "
+        f"WRITE_SIZE {w_cal:.1f} KiB per dispatch, so FETCH_SIZE is scaled by {f_factor:.4f} and "
+        f"WRITE_SIZE by {w_factor:.4f}.  Counter values are means over the dispatches.",
         "",
-        "| kernel | dispatches | FETCH_SIZE KiB | read MB (scaled) | WRITE_SIZE KiB | written MB (scaled) |",
-        "|---|---|---|---|---|---|",
+        head,
+        rule,
         *rows,
         "",
         f"- hbm_bytes_per_launch: {int(round(total))}",
         f"- fetch_factor: {f_factor:.4f}",
         f"- write_factor: {w_factor:.4f}",
+        *extra,
         f"- kernel_digest: `{kernel_digest()}`",
         "",
     ])
     os.makedirs(PROFILES, exist_ok=True)
     with open(traffic_path(workload, mode), "w") as f:
+        f.write(text)
+    return text
+
+
+def ktrace_summary(trace_dir: str, workload: str, mode: str, steps: int, command: str,
+                   note: str = "") -> str:
+    """Summarise a rocprofv3 --kernel-trace run of bench.py into
+    profiles/kernels_<workload>_<mode>.md: per kernel, every dispatch, and the
+    last `steps` dispatches (the decode-only timed region, which runs last)."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    disp = defaultdict(list)
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            disp[row["Kernel_Name"]].append((int(row["Start_Timestamp"]),
+                                             int(row["End_Timestamp"])))
+    lines = []
+    decode_total = 0.0
+    for name in sorted(disp, key=lambda n: -len(disp[n])):
+        ds = sorted(disp[name])
+        us = [(e - b) / 1e3 for b, e in ds]
+        last = us[-steps:] if len(us) >= steps else us
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+        if any(k in name for k in ("decode_kernel", "merge_kernel", "reduce_kernel")):
+            decode_total += sum(last) / len(last)
+        lines.append(f"| `{short}` | {len(us)} | {sum(us) / len(us):.2f} | {len(last)} | "
+                     f"{sum(last) / len(last):.2f} | {pct(last, 50):.2f} | {pct(last, 10):.2f} | "
+                     f"{pct(last, 90):.2f} | {min(last):.2f} | {max(last):.2f} |")
+    text = "\n".join([
+        f"# Kernel durations: {workload}, decode mode {mode}",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "Durations are end minus start of each dispatch in the kernel trace (us). `last` = the "
+        f"last {steps} dispatches of a kernel: for the decode kernels, the bench's decode-only "
+        "timed region (the roofline's launches), which runs last.",
+        "",
+        "| kernel | dispatches | mean (all) | last | mean | median | p10 | p90 | min | max |",
+        "|---|---|---|---|---|---|---|---|---|---|",
+        *lines,
+        "",
+        f"- decode_launch_us (decode-path kernels, mean of the last {steps}): {decode_total:.2f}",
+        *( [note] if note else []),
+        "",
+    ])
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, f"kernels_{workload}_{mode}.md"), "w") as f:
         f.write(text)
     return text
 
@@ -599,8 +682,11 @@ def main() -> int:
     ap.add_argument("--pmc-pass", action="store_true",
                     help="run the calibration copy, then --steps decode launches, and exit "
                          "(the program to run under rocprofv3 --pmc)")
-    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write the traffic summary from two --pmc-pass counter runs")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
+                    help="write the traffic summary from --pmc-pass counter runs: FETCH_SIZE "
+                         "dir, WRITE_SIZE dir, [TCC hit/miss/DRAM dir]")
+    ap.add_argument("--ktrace-summary", metavar="DIR",
+                    help="write the kernel-duration summary of a --kernel-trace run of bench")
     ap.add_argument("--pmc-command", default="", help="command line recorded in the summary")
     ap.add_argument("--ceiling", type=int, default=1,
                     help="decode: also time the streaming-read probe (the read ceiling)")
@@ -629,7 +715,11 @@ def main() -> int:
 
     if args.pmc_summary:
         name, block_bytes = workload_shape(args.workload, args.block_size, args.dtype)
-        print(pmc_summary(*args.pmc_summary, name, block_bytes, args.mode, args.pmc_command))
+        print(pmc_summary(args.pmc_summary, name, block_bytes, args.mode, args.pmc_command))
+        return 0
+    if args.ktrace_summary:
+        name, _ = workload_shape(args.workload, args.block_size, args.dtype)
+        print(ktrace_summary(args.ktrace_summary, name, args.mode, args.steps, args.pmc_command))
         return 0
 
     if args.gpus != 1:
