@@ -67,25 +67,62 @@ def _run(cmd):
     return text
 
 
-def build(verbose: bool = False, jobs: int | None = None, defines=(), out: str = LIB_PATH,
-          build_dir: str = BUILD_DIR) -> str:
+# Host-side sanitizers for the CPU test build (build(sanitize=True)).  On a
+# hipcc line every -fsanitize= sits behind -Xarch_host: the device code is
+# built as usual, only its host side is instrumented.
+SAN_FLAGS = ["-fsanitize=address", "-fsanitize=undefined", "-fno-omit-frame-pointer",
+             "-fno-sanitize-recover=undefined", "-g"]
+SAN_LIB_PATH = os.path.join(BUILD_DIR, "san", "libpagedattn_san.so")
+
+
+def sanitizer_runtime() -> str:
+    """The clang address-sanitizer runtime (it carries the UBSan handlers too),
+    to LD_PRELOAD into a process that loads the sanitized library."""
+    paths = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(
+        hipcc()))), "lib", "llvm", "lib", "clang", "*", "lib", "linux",
+        "libclang_rt.asan-x86_64.so")))
+    if not paths:
+        raise RuntimeError("clang's address-sanitizer runtime was not found")
+    return paths[-1]
+
+
+def build(verbose: bool = False, jobs: int | None = None, defines=(), out: str | None = None,
+          build_dir: str | None = None, sanitize: bool = False) -> str:
     """Compile every csrc/*.hip and csrc/*.cpp and link a shared library; returns its path.
 
     ``defines`` are extra ``NAME=VALUE`` preprocessor definitions (tuning
     knobs); ``out`` is the library path (default: the in-tree libpagedattn.so).
+    ``sanitize`` builds the host code - the block manager, argument checks and
+    launch code - with AddressSanitizer and UndefinedBehaviorSanitizer into a
+    separate CPU test library (default ``_build/san/libpagedattn_san.so``), for
+    processes started with ``LD_PRELOAD`` of :func:`sanitizer_runtime`; the
+    device code is the same as in the product library.
     """
+    if out is None:
+        out = SAN_LIB_PATH if sanitize else LIB_PATH
+    if build_dir is None:
+        build_dir = os.path.join(BUILD_DIR, "san") if sanitize else BUILD_DIR
     os.makedirs(build_dir, exist_ok=True)
+    os.makedirs(os.path.dirname(out), exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not sources:
         raise RuntimeError("no HIP sources found")
     cc = hipcc()
     flags = [*COMMON_FLAGS, *(f"-D{d}" for d in defines)]
+    host_cc, host_flags = host_cxx(), HOST_FLAGS
+    if sanitize:
+        for f in SAN_FLAGS:
+            flags += ["-Xarch_host", f]
+        # the same compiler family as hipcc's host pass, so one runtime serves both
+        host_cc = os.path.join(os.path.dirname(os.path.realpath(cc)), "..", "lib", "llvm", "bin",
+                               "clang++")
+        host_flags = [*HOST_FLAGS, *SAN_FLAGS]
     objects = [os.path.join(build_dir, os.path.basename(s) + ".o") for s in sources]
     cmds = [[cc, *flags, "-c", src, "-o", obj] for src, obj in zip(sources, objects)]
     for src in sorted(glob.glob(os.path.join(CSRC, "*.cpp"))):
         obj = os.path.join(build_dir, os.path.basename(src) + ".o")
         objects.append(obj)
-        cmds.append([host_cxx(), *HOST_FLAGS, *(f"-D{d}" for d in defines), "-c", src, "-o", obj])
+        cmds.append([host_cc, *host_flags, *(f"-D{d}" for d in defines), "-c", src, "-o", obj])
     jobs = jobs or min(len(cmds), os.cpu_count() or 4, 16)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         for log in ex.map(_run, cmds):
