@@ -411,7 +411,7 @@ def bench_prefill(args) -> dict:
     8-bit cache): algorithmic flops per launch / average launch time."""
     import torch
 
-    names = ["cached_preamble", "long_prompts", "mixed_step"]
+    names = [args.prefill_workload] if args.prefill_workload else PREFILL_WORKLOADS
     dtype = args.dtype or "bf16"
     rows = {}
     for name in names:
@@ -447,21 +447,133 @@ def bench_prefill(args) -> dict:
                           tflops=round(tflops, 1), frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                           seqs=w.num_seqs, tokens=w.num_tokens)
         print(f"# prefill {name}: {us:.1f} us, {tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
-    head = rows["cached_preamble"]
+    head = rows[names[0]]
     return {
         "metric": "paged prefill attention TFLOP/s (pa_prefill, mixed batches)",
         "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "higher_is_better": True, "vs_baseline": None, "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": "cached_preamble: 16 x (304 new tokens over a 1,200-token "
-                               "context), 32 query / 8 KV heads, head_dim 128",
+        "config": {"workload": PREFILL_DESCRIPTIONS[names[0]],
                    "block_size": args.block_size or 16, "sliding_window": args.window,
                    "alibi": bool(args.alibi)},
         "workloads": rows,
-        "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": head["tflops"],
+        "roofline": {"bound": "mfma",
+                     "kernel": "prefill_dma_kernel" if dtype == "bf16" else "prefill_kernel",
+                     "achieved": head["tflops"],
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": head["frac"],
                      "traffic": None},
     }
+
+
+PREFILL_WORKLOADS = ["cached_preamble", "long_prompts", "mixed_step"]
+PREFILL_DESCRIPTIONS = {
+    "cached_preamble": "cached_preamble: 16 x (304 new tokens over a 1,200-token context), "
+                       "32 query / 8 KV heads, head_dim 128",
+    "long_prompts": "long_prompts: 4 x 4,096-token prompts from scratch, 32 query / 8 KV heads, "
+                    "head_dim 128",
+    "mixed_step": "mixed_step: 60 decode rows + a 2,048-token slice + a 1,024-token prompt, "
+                  "32 query / 8 KV heads, head_dim 128",
+}
+
+# SQ counter passes of the prefill attention kernel (each within one pass's
+# hardware limits: at most 8 SQ counters and 2 GRBM counters)
+SQ_PASSES = {
+    "mix": ["SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_VALU", "SQ_INSTS_SALU",
+            "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES",
+            "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE"],
+    "lds": ["SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_ADDR_CONFLICT",
+            "SQ_LDS_DATA_FIFO_FULL", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS",
+            "SQ_INSTS_LDS_LOAD_BANDWIDTH", "SQ_INSTS_VALU_TRANS_F32", "GRBM_GUI_ACTIVE"],
+}
+
+
+def sq_summary(root: str, dtype: str, command: str) -> str:
+    """Summarise rocprofv3 --pmc runs of ``--part prefill --prefill-workload W``
+    (directories root/<workload>/<pass>, one per SQ_PASSES entry) into
+    profiles/sq_prefill_<dtype>.md: per dispatch of the attention kernel, the
+    instruction mix and how busy the matrix cores, the VALU and the LDS were.
+
+    Utilisations follow rocprofv3's own derived metrics: MFMA busy cycles over
+    GPU-busy cycles times the 1,024 SIMDs; LDS active cycles over GPU-busy
+    cycles times the 256 CUs; VALU active cycles (summed over waves) over
+    GPU-busy cycles times the CUs; bank-conflict cycles over the LDS's
+    conflict-free active cycles."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    cus, simds = 256, 1024
+    lines = []
+    for wl in PREFILL_WORKLOADS:
+        vals = defaultdict(list)
+        for pname in SQ_PASSES:
+            d = os.path.join(root, wl, pname)
+            for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+                for row in csv.DictReader(open(f)):
+                    name = row["Kernel_Name"]
+                    if "prefill_dma_kernel" in name or "prefill_kernel" in name:
+                        vals[(pname, row["Counter_Name"])].append(float(row["Counter_Value"]))
+        if not vals:
+            continue
+        mean = lambda k: (sum(vals[k]) / len(vals[k])) if vals[k] else float("nan")
+        # GRBM_GUI_ACTIVE comes summed over the 8 XCDs: per XCD, the kernel's cycles
+        g1 = mean(("mix", "GRBM_GUI_ACTIVE")) / 8
+        g2 = mean(("lds", "GRBM_GUI_ACTIVE")) / 8
+        mfma = mean(("mix", "SQ_INSTS_MFMA"))
+        lds_i = mean(("mix", "SQ_INSTS_LDS"))
+        valu = mean(("mix", "SQ_INSTS_VALU"))
+        salu = mean(("mix", "SQ_INSTS_SALU"))
+        mfma_util = 100 * mean(("mix", "SQ_VALU_MFMA_BUSY_CYCLES")) / (g1 * simds)
+        valu_busy = 100 * mean(("mix", "SQ_ACTIVE_INST_VALU")) / (g1 * cus)
+        occ = 400 * mean(("mix", "SQ_WAVE_CYCLES")) / g1 / cus / 32
+        idx = mean(("lds", "SQ_LDS_IDX_ACTIVE"))
+        bank = mean(("lds", "SQ_LDS_BANK_CONFLICT"))
+        lds_util = 100 * idx / (g2 * cus)
+        bank_ratio = bank / (idx - bank) if idx > bank else float("nan")
+        lds_bytes = 64 * mean(("lds", "SQ_INSTS_LDS_LOAD_BANDWIDTH"))
+        trans = mean(("lds", "SQ_INSTS_VALU_TRANS_F32"))
+        lines.append(
+            f"| {wl} | {len(vals[('mix', 'SQ_INSTS_MFMA')])} | {g1:.0f} | {mfma:.0f} | "
+            f"{lds_i:.0f} | {lds_i / mfma:.2f} | {valu / mfma:.2f} | {salu / mfma:.2f} | "
+            f"{trans / mfma:.2f} | {lds_bytes / 1e6:.1f} | {lds_bytes / mfma:.0f} | "
+            f"{mfma_util:.1f} | {lds_util:.1f} | {100 * bank_ratio:.1f} | {valu_busy:.1f} | "
+            f"{occ:.1f} |")
+        lines.append(
+            f"| ↳ raw | | {g2:.0f} (lds pass) | | | | | | | | | "
+            f"addr-conflict {mean(('lds', 'SQ_LDS_ADDR_CONFLICT')):.0f}, "
+            f"data-FIFO-full {mean(('lds', 'SQ_LDS_DATA_FIFO_FULL')):.0f} | "
+            f"active-inst-LDS {mean(('lds', 'SQ_ACTIVE_INST_LDS')):.0f} | "
+            f"wait-inst-LDS {mean(('lds', 'SQ_WAIT_INST_LDS')):.0f} | | |")
+    text = "\n".join([
+        f"# SQ counters of the prefill attention kernel ({dtype} cache)",
+        "",
+        "rocprofv3 counter passes of `bench.py --part prefill` (one workload per run, one pass "
+        "per counter set):",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "Per dispatch of the attention kernel, means over the dispatches.  Columns: GPU-busy "
+        "cycles (GRBM_GUI_ACTIVE, which the counter run reports summed over the 8 XCDs, / 8); MFMA, LDS, VALU, SALU and 32-bit transcendental VALU "
+        "instructions (VALU/SALU/trans per MFMA); bytes the LDS returned to the waves "
+        "(SQ_INSTS_LDS_LOAD_BANDWIDTH x 64), in MB and per MFMA; MFMA util % "
+        "(SQ_VALU_MFMA_BUSY_CYCLES / (busy cycles x 1,024 SIMDs)); LDS util % "
+        "(SQ_LDS_IDX_ACTIVE / (busy cycles x 256 CUs)); bank conflicts % (conflict cycles / "
+        "conflict-free LDS active cycles); VALU busy % (SQ_ACTIVE_INST_VALU / (busy cycles x "
+        "256 CUs)); occupancy % of 32 wave slots per CU (SQ_WAVE_CYCLES).",
+        "",
+        "| workload | dispatches | busy cycles | MFMA | LDS inst | LDS/MFMA | VALU/MFMA | "
+        "SALU/MFMA | trans/MFMA | LDS read MB | LDS B/MFMA | MFMA util % | LDS util % | "
+        "bank confl % | VALU busy % | occupancy % |",
+        "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|",
+        *lines,
+        "",
+    ])
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, f"sq_prefill_{dtype}.md"), "w") as f:
+        f.write(text)
+    return text
 
 
 def event_times(fn, n: int) -> list:
@@ -688,6 +800,11 @@ def main() -> int:
     ap.add_argument("--ktrace-summary", metavar="DIR",
                     help="write the kernel-duration summary of a --kernel-trace run of bench")
     ap.add_argument("--pmc-command", default="", help="command line recorded in the summary")
+    ap.add_argument("--prefill-workload", default=None, choices=PREFILL_WORKLOADS,
+                    help="prefill: time only this workload")
+    ap.add_argument("--sq-summary", metavar="DIR",
+                    help="prefill: write the SQ counter summary of the runs under DIR "
+                         "(DIR/<workload>/<pass>)")
     ap.add_argument("--ceiling", type=int, default=1,
                     help="decode: also time the streaming-read probe (the read ceiling)")
     ap.add_argument("--stream-mib", type=int, default=2048,
@@ -716,6 +833,9 @@ def main() -> int:
     if args.pmc_summary:
         name, block_bytes = workload_shape(args.workload, args.block_size, args.dtype)
         print(pmc_summary(args.pmc_summary, name, block_bytes, args.mode, args.pmc_command))
+        return 0
+    if args.sq_summary:
+        print(sq_summary(args.sq_summary, args.dtype or "bf16", args.pmc_command))
         return 0
     if args.ktrace_summary:
         name, _ = workload_shape(args.workload, args.block_size, args.dtype)

@@ -426,8 +426,12 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 // a K tile and a V tile of 32 rows x 256 bytes, row-major as in the pool.
 // No registers hold tiles in flight and no VALU repacks them.  A lane picks
 // which 16-byte piece of its row it fetches, so the pieces are stored with an
-// XOR swizzle: K rows at piece c ^ (row % 8) (the 8 rows an 8-lane read phase
-// touches fall in 8 distinct bank groups), V rows at piece c ^ 2(row % 4).
+// XOR swizzle.  The LDS serves 256 bytes (64 banks) per cycle: a 16-byte read
+// goes in phases of 16 lanes, which read one piece of 16 consecutive K rows,
+// so K rows sit at piece c ^ (row % 16); an 8-byte transposed read goes in
+// phases of 32 lanes, which read two adjacent pieces of each of 8 consecutive
+// V rows, so V rows sit at piece c ^ 2(row % 8).  Each phase then touches all
+// 64 banks once.
 // The V^T operand of O^T = V^T P^T comes from ds_read_b64_tr_b16: within a
 // 16-lane group, lane s addresses 4 dims of key row 4g + s/4 and lane i gets
 // dim i of the 4 rows the group addressed - 4 keys of one dimension, in the
@@ -435,8 +439,19 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 // id outside the pool) are zeroed in LDS before the tile is used, so that a
 // zero weight never meets a NaN.
 
+#ifndef PA_PREFILL_KSWZ
+#define PA_PREFILL_KSWZ 16  // K rows whose pieces the swizzle spreads (16; 8 for comparison)
+#endif
+#ifndef PA_PREFILL_VSWZ
+#define PA_PREFILL_VSWZ 8   // V rows whose piece pairs the swizzle spreads (8; 4 for comparison)
+#endif
+
 constexpr int kStages = 3;
 constexpr int kStageBytes = 2 * kKeys * kD * 2;  // K and V tiles, 16 KiB
+// Block-table entries the LDS-DMA kernel keeps in LDS behind its ring (a
+// window of the walk's blocks, reloaded when the walk passes its end).
+constexpr int kTblWin = 1024;
+constexpr size_t kDmaLdsBytes = size_t(kStages) * kStageBytes + kTblWin * sizeof(int32_t);
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 #define PA_LDS(T) __attribute__((address_space(3))) T
@@ -533,6 +548,31 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
     }
   }
 
+  // ---- block-table entries in LDS -------------------------------------------
+  // Vector memory operations complete in order, so a table entry loaded from
+  // global memory inside the walk would wait for every tile DMA issued before
+  // it.  The walk reads its entries from a window of kTblWin of them in LDS
+  // instead (entries outside the pool stored as -1), loaded by the whole
+  // workgroup before the walk and again when the walk passes the window's end.
+  int32_t* s_tbl = reinterpret_cast<int32_t*>(s_mem + kStages * kStageBytes);
+  const int nblk = kend > 0 ? (kend + BS - 1) / BS : 0;
+  int tbl0 = 0;  // first block the window holds
+  auto load_tbl = [&](int first) {
+    tbl0 = first;
+    const int cnt = min(kTblWin, nblk - first);
+    for (int i = tid; i < cnt; i += 64 * NW) {
+      const int p = table[first + i];
+      s_tbl[i] = (p < 0 || int64_t(p) >= a.num_blocks) ? -1 : p;
+    }
+  };
+  // entry of block b, tbl0 <= b < min(tbl0 + kTblWin, nblk)
+  auto entry = [&](int b) { return s_tbl[b - tbl0]; };
+  load_tbl(kt0 * kKeys / BS);
+  // (the query rows and the entries have landed before the walk: the walk's
+  // waits then count only tile DMAs)
+  wait_vm_lgkm<0>();
+  __syncthreads();
+
   // ---- the DMA side ---------------------------------------------------------
   constexpr int kRowBytes = kD * 2;
   const int64_t blk_stride = int64_t(a.num_kv_heads) * BS * kRowBytes;
@@ -549,16 +589,18 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
       // rows past the context read the context's last aligned group instead
       // (in bounds; their V rows are zeroed before use)
       const int key0 = __builtin_amdgcn_readfirstlane(min(k0 + r0, (kend - 1) & ~3));
-      int phys = __builtin_amdgcn_readfirstlane(table[key0 / BS]);
-      if (phys < 0 || int64_t(phys) >= a.num_blocks) phys = 0;
+      int phys = __builtin_amdgcn_readfirstlane(entry(key0 / BS));
+      if (phys < 0) phys = 0;
+      // the group's base (scalar), then the lane's row and swizzled piece
+      const int64_t base = int64_t(phys) * blk_stride + head_off + int64_t(key0 % BS) * kRowBytes;
       const int row = r0 + rr;
-      const int64_t base = int64_t(phys) * blk_stride + head_off + int64_t(key0 % BS + rr) * kRowBytes;
-      const uint8_t* kp = a.k_pool + base + ((piece ^ (row & 7)) << 4);
-      const uint8_t* vp = a.v_pool + base + ((piece ^ (2 * (row & 3))) << 4);
+      const uint32_t ko = uint32_t(rr * kRowBytes + ((piece ^ (row & (PA_PREFILL_KSWZ - 1))) << 4));
+      const uint32_t vo =
+          uint32_t(rr * kRowBytes + ((piece ^ (2 * (row & (PA_PREFILL_VSWZ - 1)))) << 4));
       uint8_t* lk = s_mem + stage * kStageBytes + r0 * kRowBytes;
       uint8_t* lv = lk + kKeys * kRowBytes;
-      __builtin_amdgcn_global_load_lds(kp, (PA_LDS(void)*)lk, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vp, (PA_LDS(void)*)lv, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.k_pool + base + ko, (PA_LDS(void)*)lk, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.v_pool + base + vo, (PA_LDS(void)*)lv, 16, 0, 0);
     }
   };
   // V rows that must read as zero: past the context, or in a block outside the pool
@@ -567,10 +609,7 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
     if (k0 + kKeys > kend) return true;
     bool bad = false;
 #pragma unroll
-    for (int b = 0; b < kKeys / BS; ++b) {
-      const int phys = __builtin_amdgcn_readfirstlane(table[k0 / BS + b]);
-      bad |= phys < 0 || int64_t(phys) >= a.num_blocks;
-    }
+    for (int b = 0; b < kKeys / BS; ++b) bad |= __builtin_amdgcn_readfirstlane(entry(k0 / BS + b)) < 0;
     return bad;
   };
   auto fix = [&](int kt, int stage) {
@@ -578,11 +617,7 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
     constexpr int PPT = 512 / (64 * NW);        // 16-byte pieces per thread (32 rows x 16)
     const int row = tid / (16 / PPT);
     const int key = k0 + row;
-    bool zero = key >= kend;
-    if (!zero) {
-      const int phys = table[key / BS];
-      zero = phys < 0 || int64_t(phys) >= a.num_blocks;
-    }
+    const bool zero = key >= kend || entry(key / BS) < 0;
     if (zero) {
       u32x4* dst = reinterpret_cast<u32x4*>(s_mem + stage * kStageBytes + kKeys * kRowBytes +
                                             row * kRowBytes) + PPT * (tid % (16 / PPT));
@@ -614,15 +649,23 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
     }
     // the stage tile kt-1 used is free: refill it with tile kt+kStages-1
     if (kt + kStages - 1 < ntiles) {
+      const int tn = kt + kStages - 1;
+      // its last block past the window: move the window to tile kt+1's first
+      // block (tile kt no longer needs entries; every wave is past fix(kt))
+      if ((min(tn * kKeys + kKeys, kend) - 1) / BS >= tbl0 + kTblWin) {
+        __syncthreads();
+        load_tbl((kt + 1) * kKeys / BS);
+        __syncthreads();
+      }
       const int free_stage = stage == 0 ? kStages - 1 : stage - 1;
-      issue(kt + kStages - 1, free_stage);
+      issue(tn, free_stage);
     }
     const int k0 = kt * kKeys;
     const uint8_t* lk = s_mem + stage * kStageBytes;
     const uint8_t* lv = lk + kKeys * kRowBytes;
 
     if (busy) {
-    // S^T = K Q^T: A = key rows (16h + r16), pieces (4mm + grp) ^ (row % 8)
+    // S^T = K Q^T: A = key rows (16h + r16), pieces (4mm + grp) ^ (row % 16)
     f32x4 sc4[NRT][2];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
@@ -634,7 +677,7 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
 #pragma unroll
       for (int mm = 0; mm < 4; ++mm) {
         const u32x4 kf = *reinterpret_cast<const u32x4*>(
-            lk + row * kRowBytes + (((4 * mm + grp) ^ (row & 7)) << 4));
+            lk + row * kRowBytes + (((4 * mm + grp) ^ (row & (PA_PREFILL_KSWZ - 1))) << 4));
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
           sc4[rt][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -656,7 +699,8 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
       for (int hh = 0; hh < 2; ++hh) {
         const int row = 16 * hh + 4 * grp + (r16 >> 2);
         const int lc = 2 * dt + ((r16 & 3) >> 1);            // logical 16-byte piece
-        const int off = row * kRowBytes + ((lc ^ (2 * (row & 3))) << 4) + ((r16 & 1) << 3);
+        const int off =
+            row * kRowBytes + ((lc ^ (2 * (row & (PA_PREFILL_VSWZ - 1)))) << 4) + ((r16 & 1) << 3);
         half[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (PA_LDS(v4s)*)((PA_LDS(uint8_t)*)lv + off));
       }
@@ -702,7 +746,7 @@ int launch_g(const PrefillArgs& a, bool out_f32, dim3 grid, hipStream_t stream) 
   const bool al = a.alibi != nullptr;
   if constexpr (ET == kBF16 && PA_PREFILL_DMA) {
     constexpr int NRT = PA_PREFILL_ROW_TILES;
-    const size_t lds = size_t(kStages) * kStageBytes;
+    const size_t lds = kDmaLdsBytes;
     const dim3 block(64 * (8 / NRT));
     if (out_f32 && al)
       hipLaunchKernelGGL((prefill_dma_kernel<BS, G, true, true, NRT>), grid, block, lds, stream, a);
