@@ -53,6 +53,11 @@ constexpr int kVStride = 36;      // bf16 per transposed V row in LDS (32 + 4 pa
 constexpr int kKBytes = kKeys * kKStride * 16;
 constexpr int kVBytes = kD * kVStride * 2;
 constexpr int kBufBytes = kKBytes + kVBytes;
+// Block-table entries a workgroup keeps in LDS behind its tile buffers: a
+// window of the walk's blocks, reloaded when the walk passes its end.  (Vector
+// memory operations complete in order, so an entry loaded from global memory
+// inside the walk would wait for every tile load issued before it.)
+constexpr int kTblWin = 1024;
 
 #ifndef PA_PREFILL_ROW_TILES
 #define PA_PREFILL_ROW_TILES 2  // 16-row tiles per wave of the LDS-DMA kernel: 2 or 4
@@ -167,6 +172,13 @@ __device__ __forceinline__ void softmax_step(f32x4 (&s)[NR][2], u32x4 (&pf)[NR],
   }
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  // s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding; expcnt left at its maximum)
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
 template <int ET, int BS, int G, bool OUT_F32, bool AL>
 __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
   constexpr int EB = ET == kFP8 ? 1 : 2;   // K/V element bytes
@@ -228,42 +240,42 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
   // ---- K/V tile staging -------------------------------------------------------
   // Thread tid loads dims [8*dc, 8*dc+8) of keys 2kp and 2kp+1 of a tile (one
   // block: block sizes are even).  Loads run two tiles ahead of the math (two
-  // register sets), block-table entries three tiles ahead.
+  // register sets).  Every walk step issues the same four loads, so the
+  // compiler's wait before a register set is stored counts exactly the loads
+  // issued after it: keys past the context and blocks outside the pool read
+  // block 0 of the pool instead, and a per-set mask zeroes those rows when the
+  // set is stored.
   const int dc = tid & 15, kp = tid >> 4;
   Raw kr[2][2], vr[2][2];
+  int zmask[2] = {0, 0};  // bit e: key 2kp+e of the set's tile reads as zero
   // key 2kp of a tile sits at row (2kp) % BS of its block (tiles start at
   // multiples of 32, a multiple of BS), so a lane's offset inside a block is fixed
   constexpr int kRowBytes = kD * EB;
   const int64_t blk_stride = int64_t(a.num_kv_heads) * BS * kRowBytes;
   const int64_t lane_off = (int64_t(g) * BS + (2 * kp) % BS) * kRowBytes + dc * 8 * EB;
-  auto table_entry = [&](int k0) -> int {
-    const int key = k0 + 2 * kp;
-    return key < kend ? table[key / BS] : -1;
+
+  // the walk's table entries, a window of kTblWin of them in LDS (entries
+  // outside the pool stored as -1)
+  int32_t* s_tbl = reinterpret_cast<int32_t*>(s_mem + 2 * kBufBytes);
+  const int nblk = kend > 0 ? (kend + BS - 1) / BS : 0;
+  int tbl0 = 0;  // first block the window holds
+  auto load_tbl = [&](int first) {
+    tbl0 = first;
+    const int cnt = min(kTblWin, nblk - first);
+    for (int i = tid; i < cnt; i += 256) {
+      const int p = table[first + i];
+      s_tbl[i] = (p < 0 || int64_t(p) >= a.num_blocks) ? -1 : p;
+    }
   };
-  auto load_tile = [&](int set, int k0, int phys) {
-    const bool ok = phys >= 0 && int64_t(phys) < a.num_blocks;
-    if (k0 + kKeys <= kend && __ballot(!ok) == 0) {
-      // whole tile inside the context, every block in the pool: no conditions
-      const uint8_t* kb = a.k_pool + int64_t(phys) * blk_stride + lane_off;
-      const uint8_t* vb = a.v_pool + int64_t(phys) * blk_stride + lane_off;
-      kr[set][0] = *reinterpret_cast<const Raw*>(kb);
-      kr[set][1] = *reinterpret_cast<const Raw*>(kb + kRowBytes);
-      vr[set][0] = *reinterpret_cast<const Raw*>(vb);
-      vr[set][1] = *reinterpret_cast<const Raw*>(vb + kRowBytes);
-      return;
-    }
-    // the context's last tile, or a block id outside the pool: those rows are zero
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int key = k0 + 2 * kp + e;
-      kr[set][e] = Raw{};
-      vr[set][e] = Raw{};
-      if (key < kend && ok) {
-        const int64_t off = int64_t(phys) * blk_stride + lane_off + e * kRowBytes;
-        kr[set][e] = *reinterpret_cast<const Raw*>(a.k_pool + off);
-        vr[set][e] = *reinterpret_cast<const Raw*>(a.v_pool + off);
-      }
-    }
+  auto load_tile = [&](int set, int k0) {
+    const int key = k0 + 2 * kp;  // and key + 1, in the same block
+    const int phys = key < kend ? s_tbl[key / BS - tbl0] : -1;
+    zmask[set] = phys < 0 ? 3 : (key + 1 < kend ? 0 : 2);
+    const int64_t off = int64_t(phys < 0 ? 0 : phys) * blk_stride + lane_off;
+    kr[set][0] = *reinterpret_cast<const Raw*>(a.k_pool + off);
+    kr[set][1] = *reinterpret_cast<const Raw*>(a.k_pool + off + kRowBytes);
+    vr[set][0] = *reinterpret_cast<const Raw*>(a.v_pool + off);
+    vr[set][1] = *reinterpret_cast<const Raw*>(a.v_pool + off + kRowBytes);
   };
   auto store_tile = [&](int set, int buf) {
     u32x4* lk = reinterpret_cast<u32x4*>(s_mem + buf * kBufBytes);
@@ -271,8 +283,9 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     u32x4 kb[2], vb[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      kb[e] = score_chunk<ET>(kr[set][e]);
-      vb[e] = score_chunk<ET>(vr[set][e]);
+      const bool z = (zmask[set] >> e) & 1;
+      kb[e] = z ? u32x4{0u, 0u, 0u, 0u} : score_chunk<ET>(kr[set][e]);
+      vb[e] = z ? u32x4{0u, 0u, 0u, 0u} : score_chunk<ET>(vr[set][e]);
       lk[(2 * kp + e) * kKStride + dc] = kb[e];
     }
     // V transposed: dim 8dc + x gets the pair (key 2kp, key 2kp+1) as one word,
@@ -323,24 +336,33 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // prologue: tile kt0 in LDS, tile kt0+1 in flight, the table entry of kt0+2 in flight
-  int next_phys = -1;
+  // prologue: the table window, then tile kt0 in LDS and tile kt0+1 in flight
+  // (no tiles: rows before position 0, written as zeros below)
   if (ntiles > kt0) {
-    load_tile(0, kt0 * kKeys, table_entry(kt0 * kKeys));
-    if (ntiles > kt0 + 1) load_tile(1, (kt0 + 1) * kKeys, table_entry((kt0 + 1) * kKeys));
-    if (ntiles > kt0 + 2) next_phys = table_entry((kt0 + 2) * kKeys);
+    load_tbl(kt0 * kKeys / BS);
+    // (the query rows and the entries have landed before the walk: the walk's
+    // waits then count only tile loads)
+    wait_vm_lgkm<0>();
+    __syncthreads();
+    load_tile(0, kt0 * kKeys);
+    load_tile(1, min(kt0 + 1, ntiles - 1) * kKeys);
     store_tile(0, 0);
+    __syncthreads();
   }
-  __syncthreads();
   // one key tile; BUF (= (kt - kt0) & 1) is a constant, so every register set is static
   auto iteration = [&](int kt, auto buf_c) {
     constexpr int buf = decltype(buf_c)::value;
     const int k0 = kt * kKeys;
-    // tile kt+2 into the register set tile kt used (it is in LDS already)
-    if (kt + 2 < ntiles) {
-      load_tile(buf, k0 + 2 * kKeys, next_phys);
-      if (kt + 3 < ntiles) next_phys = table_entry(k0 + 3 * kKeys);
+    // tile kt+2 into the register set tile kt used (it is in LDS already);
+    // past the walk's end, its last tile again (never stored)
+    const int kn = min(kt + 2, ntiles - 1);
+    if ((min(kn * kKeys + kKeys, kend) - 1) / BS >= tbl0 + kTblWin) {
+      // the window ends before tile kn's last block: every thread is past its
+      // reads of the old one (the barrier that ended the previous step)
+      load_tbl(kn * kKeys / BS);
+      __syncthreads();
     }
+    load_tile(buf, kn * kKeys);
     const u32x4* lk = reinterpret_cast<const u32x4*>(s_mem + buf * kBufBytes);
     const uint8_t* lv = s_mem + buf * kBufBytes + kKBytes;
 
@@ -448,20 +470,11 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 
 constexpr int kStages = 3;
 constexpr int kStageBytes = 2 * kKeys * kD * 2;  // K and V tiles, 16 KiB
-// Block-table entries the LDS-DMA kernel keeps in LDS behind its ring (a
-// window of the walk's blocks, reloaded when the walk passes its end).
-constexpr int kTblWin = 1024;
 constexpr size_t kDmaLdsBytes = size_t(kStages) * kStageBytes + kTblWin * sizeof(int32_t);
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 #define PA_LDS(T) __attribute__((address_space(3))) T
 
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm() {
-  // s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding; expcnt left at its maximum)
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
-}
 
 template <int BS, int G, bool OUT_F32, bool AL, int NRT>
 __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
@@ -758,7 +771,7 @@ int launch_g(const PrefillArgs& a, bool out_f32, dim3 grid, hipStream_t stream) 
       hipLaunchKernelGGL((prefill_dma_kernel<BS, G, false, false, NRT>), grid, block, lds, stream, a);
     return launch_result("pa_prefill");
   } else {
-    const size_t lds = 2 * kBufBytes;
+    const size_t lds = 2 * kBufBytes + kTblWin * sizeof(int32_t);
     if (out_f32 && al)
       hipLaunchKernelGGL((prefill_kernel<ET, BS, G, true, true>), grid, dim3(256), lds, stream, a);
     else if (out_f32)
