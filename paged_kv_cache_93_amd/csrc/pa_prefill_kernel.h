@@ -599,13 +599,15 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
 #pragma unroll
     for (int i = 0; i < NRT; ++i) {
       const int r0 = 4 * NRT * wave + 4 * i;  // first row of the group (wave-uniform)
-      // rows past the context read the context's last aligned group instead
-      // (in bounds; their V rows are zeroed before use)
-      const int key0 = __builtin_amdgcn_readfirstlane(min(k0 + r0, (kend - 1) & ~3));
-      int phys = __builtin_amdgcn_readfirstlane(entry(key0 / BS));
-      if (phys < 0) phys = 0;
+      // The group's 4 keys share a block (block sizes are multiples of 4).
+      // Keys past the context read rows of the sequence's last block (in
+      // bounds; their scores are masked and their V rows zeroed before use).
+      const uint32_t key0 = uint32_t(k0 + r0);
+      int phys = __builtin_amdgcn_readfirstlane(entry(min(int(key0 / BS), nblk - 1)));
+      phys = phys < 0 ? 0 : phys;
       // the group's base (scalar), then the lane's row and swizzled piece
-      const int64_t base = int64_t(phys) * blk_stride + head_off + int64_t(key0 % BS) * kRowBytes;
+      const int64_t base =
+          int64_t(phys) * blk_stride + head_off + int64_t(key0 % BS) * kRowBytes;
       const int row = r0 + rr;
       const uint32_t ko = uint32_t(rr * kRowBytes + ((piece ^ (row & (PA_PREFILL_KSWZ - 1))) << 4));
       const uint32_t vo =
