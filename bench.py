@@ -576,6 +576,71 @@ def sq_summary(root: str, dtype: str, command: str) -> str:
     return text
 
 
+def prefill_ktrace_summary(root: str, dtype: str, steps: int, command: str) -> str:
+    """Summarise rocprofv3 --kernel-trace runs of ``--part prefill
+    --prefill-workload W`` (directories root/<workload>) into
+    profiles/kernels_prefill_<dtype>_three_workloads.md: per workload, the
+    attention kernel's last `steps` dispatches (the timed calls, which run
+    last) against the algorithmic flops, and the tile-map kernel."""
+    import csv
+    import glob
+
+    rows, prep = [], []
+    for wl in PREFILL_WORKLOADS:
+        attn, tiles = [], []
+        for f in glob.glob(os.path.join(root, wl, "**", "*kernel_trace.csv"), recursive=True):
+            for row in csv.DictReader(open(f)):
+                name = row["Kernel_Name"]
+                d = (int(row["Start_Timestamp"]), int(row["End_Timestamp"]))
+                if "prefill_tiles_kernel" in name:
+                    tiles.append(d)
+                elif "prefill_dma_kernel" in name or "prefill_kernel" in name:
+                    attn.append((d, name.replace("void ", "").split("(")[0]))
+        if not attn:
+            continue
+        attn.sort()
+        us = [(e - b) / 1e3 for (b, e), _ in attn][-steps:]
+        kname = attn[-1][1]
+        gflop = W.prefill_config(wl, dtype=dtype).flops() / 1e9
+        mean = sum(us) / len(us)
+        tf = gflop / (mean * 1e-6) / 1e3
+        rows.append(f"| `{kname}` | {wl} | {len(us)} | {mean:.1f} | {pct(us, 50):.1f} | "
+                    f"{pct(us, 10):.1f} | {pct(us, 90):.1f} | {min(us):.1f} | {max(us):.1f} | "
+                    f"{gflop:.2f} | {tf:.0f} | {tf / MFMA_BF16_PEAK_TFLOPS:.3f} |")
+        prep += [(e - b) / 1e3 for b, e in tiles]
+    text = "\n".join([
+        f"# Kernel durations: pa_prefill on three mixed-batch workloads ({dtype} cache)",
+        "",
+        "rocprofv3 kernel traces, one run per workload:",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "32 query / 8 KV heads, head_dim 128, 16-token blocks, bf16 output.  Every call is "
+        "`prefill_tiles_kernel` (the tile map, one workgroup) then the attention kernel; the "
+        f"table covers the attention kernel's last {steps} dispatches (the timed calls).  "
+        "Durations are end minus start of each dispatch (us); TFLOP/s = algorithmic flops "
+        "(4 x head_dim x query heads per (query token, visible key)) / mean duration, against "
+        f"the {MFMA_BF16_PEAK_TFLOPS:,.0f} TFLOP/s dense bf16 MFMA peak.",
+        "",
+        "Workloads: " + "; ".join(PREFILL_DESCRIPTIONS[w] for w in PREFILL_WORKLOADS) + ".",
+        "",
+        "| kernel | workload | calls | mean us | median | p10 | p90 | min | max | GFLOP | "
+        "TFLOP/s | of peak |",
+        "|---|---|---|---|---|---|---|---|---|---|---|---|",
+        *rows,
+        "",
+        f"- prefill_tiles_kernel: {len(prep)} dispatches, mean "
+        f"{(sum(prep) / len(prep)) if prep else float('nan'):.2f} us",
+        "",
+    ])
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, f"kernels_prefill_{dtype}_three_workloads.md"), "w") as f:
+        f.write(text)
+    return text
+
+
 def event_times(fn, n: int) -> list:
     """Per-call durations (us) of n calls, each bracketed by its own pair of
     HIP events on the current stream (for medians and percentiles; the mean
@@ -802,6 +867,9 @@ def main() -> int:
     ap.add_argument("--pmc-command", default="", help="command line recorded in the summary")
     ap.add_argument("--prefill-workload", default=None, choices=PREFILL_WORKLOADS,
                     help="prefill: time only this workload")
+    ap.add_argument("--prefill-ktrace-summary", metavar="DIR",
+                    help="prefill: write the kernel-trace summary of the runs under DIR "
+                         "(DIR/<workload>)")
     ap.add_argument("--sq-summary", metavar="DIR",
                     help="prefill: write the SQ counter summary of the runs under DIR "
                          "(DIR/<workload>/<pass>)")
@@ -836,6 +904,10 @@ def main() -> int:
         return 0
     if args.sq_summary:
         print(sq_summary(args.sq_summary, args.dtype or "bf16", args.pmc_command))
+        return 0
+    if args.prefill_ktrace_summary:
+        print(prefill_ktrace_summary(args.prefill_ktrace_summary, args.dtype or "bf16",
+                                     args.steps, args.pmc_command))
         return 0
     if args.ktrace_summary:
         name, _ = workload_shape(args.workload, args.block_size, args.dtype)
