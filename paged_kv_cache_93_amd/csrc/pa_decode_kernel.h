@@ -1331,13 +1331,22 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
 #ifndef PA_PREFETCH_FP8
 #define PA_PREFETCH_FP8 1     // 8-bit caches (tiles of half the bytes)
 #endif
+#ifndef PA_PREFETCH_D64
+#define PA_PREFETCH_D64 2     // 64-dim heads, bf16 and f32 caches (tiles of half the bytes)
+#endif
+#ifndef PA_PREFETCH_D64_FP8
+#define PA_PREFETCH_D64_FP8 1 // 64-dim heads, 8-bit caches
+#endif
 #ifndef PA_MAX_WAVES
 #define PA_MAX_WAVES 8        // KV heads (waves) per workgroup at most
 #endif
 
 // Tiles in flight ahead of the current one.
-constexpr int decode_prefetch(int et, int g) {
-  return et == kFP8 ? PA_PREFETCH_FP8 : g <= 4 ? PA_PREFETCH_NARROW : PA_PREFETCH_WIDE;
+constexpr int decode_prefetch(int et, int d, int g) {
+  return d == 64 ? (et == kFP8 ? PA_PREFETCH_D64_FP8 : PA_PREFETCH_D64)
+         : et == kFP8 ? PA_PREFETCH_FP8
+         : g <= 4     ? PA_PREFETCH_NARROW
+                      : PA_PREFETCH_WIDE;
 }
 
 // Launches decode_kernel for a runtime (D, BS, G) on a grid of `waves`-wave
@@ -1378,7 +1387,7 @@ bool launch_decode_impl(int d, int bs, int g, const DecodeArgs& a, dim3 grid, in
 #define PA_DECODE_CASE(D_, BS_, G_)                                                       \
   if (d == D_ && bs == BS_ && g == G_) {                                                 \
     hipLaunchKernelGGL(                                                                  \
-        (decode_kernel<ET, D_, BS_, G_, decode_prefetch(ET, G_), true>),                 \
+        (decode_kernel<ET, D_, BS_, G_, decode_prefetch(ET, D_, G_), true>),                 \
         grid, dim3(waves * 64), lds, s, a);                                              \
     return true;                                                                         \
   }
@@ -1398,7 +1407,7 @@ int decode_groups_per_cu_impl(int d, int bs, int g, int waves, size_t lds) {
   if (d == D_ && bs == BS_ && g == G_) {                                                    \
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(                                       \
             &n,                                                                             \
-            decode_kernel<ET, D_, BS_, G_, decode_prefetch(ET, G_), true>,                 \
+            decode_kernel<ET, D_, BS_, G_, decode_prefetch(ET, D_, G_), true>,                 \
             waves * 64, lds) != hipSuccess)                                                 \
       n = 0;                                                                                \
     return n;                                                                               \
