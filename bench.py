@@ -324,14 +324,16 @@ def ktrace_summary(trace_dir: str, workload: str, mode: str, steps: int, command
     return text
 
 
-def workload_shape(k: int, block_size=None, dtype=None):
+def workload_shape(k: int, block_size=None, dtype=None, head_dim=None):
     """(name, bytes of one block of one pool) of workload k, as make_config names it."""
     c = W.CONFIGS[k]
     bs = int(block_size or c["block_size"])
     dt = dtype or c["dtype"]
+    d = int(head_dim or c["head_dim"])
     name = (c["name"] + ("" if dt == c["dtype"] else f"_{dt}") +
-            ("" if bs == c["block_size"] else f"_bs{bs}"))
-    return name, c["num_kv_heads"] * bs * c["head_dim"] * W.element_bytes(dt)
+            ("" if bs == c["block_size"] else f"_bs{bs}") +
+            ("" if d == c["head_dim"] else f"_d{d}"))
+    return name, c["num_kv_heads"] * bs * d * W.element_bytes(dt)
 
 
 def bench_swap(args) -> dict:
@@ -899,7 +901,7 @@ def main() -> int:
         return 0
 
     if args.pmc_summary:
-        name, block_bytes = workload_shape(args.workload, args.block_size, args.dtype)
+        name, block_bytes = workload_shape(args.workload, args.block_size, args.dtype, args.head_dim)
         print(pmc_summary(args.pmc_summary, name, block_bytes, args.mode, args.pmc_command))
         return 0
     if args.sq_summary:
@@ -910,7 +912,7 @@ def main() -> int:
                                      args.steps, args.pmc_command))
         return 0
     if args.ktrace_summary:
-        name, _ = workload_shape(args.workload, args.block_size, args.dtype)
+        name, _ = workload_shape(args.workload, args.block_size, args.dtype, args.head_dim)
         print(ktrace_summary(args.ktrace_summary, name, args.mode, args.steps, args.pmc_command))
         return 0
 
