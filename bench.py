@@ -712,6 +712,54 @@ def bench_stream(args) -> dict:
     }
 
 
+def stream_ktrace_summary(trace_dir: str, mib: int, command: str) -> str:
+    """Summarise a rocprofv3 --kernel-trace run of ``--part stream`` into
+    profiles/kernels_stream_read_<mib>mib.md: per grid, every dispatch of the
+    probe kernel and the read rate it implies (bytes read / duration)."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    nbytes = mib * (1 << 20)
+    grids = defaultdict(list)
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if "stream_read" not in row["Kernel_Name"]:
+                continue
+            wgs = int(row["Grid_Size_X"]) // int(row["Workgroup_Size_X"])
+            grids[wgs].append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
+    lines = []
+    for wgs in sorted(grids):
+        us = grids[wgs]
+        gb = lambda t: nbytes / (t * 1e-6) / 1e9
+        lines.append(f"| {wgs} | {len(us)} | {sum(us) / len(us):.1f} | {pct(us, 50):.1f} | "
+                     f"{pct(us, 10):.1f} | {pct(us, 90):.1f} | {gb(sum(us) / len(us)):,.0f} | "
+                     f"{gb(pct(us, 50)):,.0f} | {gb(min(us)):,.0f} |")
+    text = "\n".join([
+        f"# Kernel durations: streaming-read probe, one read of {mib} MiB",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "`pa_probe_stream_read`: 512-lane workgroups read 64 KiB slices with 16-byte "
+        "non-temporal loads (8 per lane in flight) and fold them into a sink; grids of 1, 2 "
+        "and 4 workgroups per CU.  Durations are end minus start of each dispatch (us); GB/s "
+        "= bytes read / duration.  The best grid's rate is the read ceiling the decode "
+        "figures are compared with.",
+        "",
+        "| workgroups | dispatches | mean us | median | p10 | p90 | GB/s (mean) | GB/s (median) "
+        "| GB/s (fastest) |",
+        "|---|---|---|---|---|---|---|---|---|",
+        *lines,
+        "",
+    ])
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, f"kernels_stream_read_{mib}mib.md"), "w") as f:
+        f.write(text)
+    return text
+
+
 class ServingTrace:
     """Seeded serving workload for the block manager at the batch-64 scale.
 
@@ -869,6 +917,8 @@ def main() -> int:
     ap.add_argument("--pmc-command", default="", help="command line recorded in the summary")
     ap.add_argument("--prefill-workload", default=None, choices=PREFILL_WORKLOADS,
                     help="prefill: time only this workload")
+    ap.add_argument("--stream-ktrace-summary", metavar="DIR",
+                    help="stream: write the kernel-trace summary of a --part stream run")
     ap.add_argument("--prefill-ktrace-summary", metavar="DIR",
                     help="prefill: write the kernel-trace summary of the runs under DIR "
                          "(DIR/<workload>)")
@@ -906,6 +956,10 @@ def main() -> int:
         return 0
     if args.sq_summary:
         print(sq_summary(args.sq_summary, args.dtype or "bf16", args.pmc_command))
+        return 0
+    if args.stream_ktrace_summary:
+        print(stream_ktrace_summary(args.stream_ktrace_summary, args.stream_mib,
+                                    args.pmc_command))
         return 0
     if args.prefill_ktrace_summary:
         print(prefill_ktrace_summary(args.prefill_ktrace_summary, args.dtype or "bf16",
