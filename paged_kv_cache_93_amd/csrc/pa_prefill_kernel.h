@@ -646,8 +646,10 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
   for (int p = 0; p < kStages - 1; ++p)
     if (kt0 + p < ntiles) issue(kt0 + p, p);
 
-  int stage = 0;
-  for (int kt = kt0; kt < ntiles; ++kt) {
+  // One key tile in ring stage STAGE (= (kt - kt0) % kStages, a constant, so
+  // every LDS address is a fixed register plus an immediate offset).
+  auto step = [&](int kt, auto stage_c) {
+    constexpr int stage = decltype(stage_c)::value;
     // this wave's DMAs of tile kt have landed once at most 2 NRT per later tile remain
     const int later = min(kStages - 2, ntiles - 1 - kt);
     if (later >= 1)
@@ -672,7 +674,7 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
         load_tbl((kt + 1) * kKeys / BS);
         __syncthreads();
       }
-      const int free_stage = stage == 0 ? kStages - 1 : stage - 1;
+      constexpr int free_stage = stage == 0 ? kStages - 1 : stage - 1;
       issue(tn, free_stage);
     }
     const int k0 = kt * kKeys;
@@ -730,7 +732,12 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
             0, 0);
     }
     }  // busy
-    stage = stage == kStages - 1 ? 0 : stage + 1;
+  };
+  static_assert(kStages == 3, "the walk is unrolled by the ring's three stages");
+  for (int kt = kt0; kt < ntiles; kt += kStages) {
+    step(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < ntiles) step(kt + 1, std::integral_constant<int, 1>{});
+    if (kt + 2 < ntiles) step(kt + 2, std::integral_constant<int, 2>{});
   }
 
 #pragma unroll
