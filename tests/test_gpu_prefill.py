@@ -192,3 +192,17 @@ def test_decode_rows_with_variants_match_the_decode_oracle():
                         1.0 / math.sqrt(128), "bf16", window=256,
                         alibi_slopes=np.asarray(slopes, np.float32).astype(np.float64))
     assert np.abs(got - ref).max() <= 2e-2
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_walk_longer_than_the_table_window(dtype):
+    """A context of 2,500 eight-token blocks: the walk passes the end of the
+    kernels' window of 1,024 block-table entries twice and reloads it, while a
+    short prompt in the same batch never does."""
+    w = W.prefill_batch("long_walk", 700, [20000, 300], [70, 300], num_heads=8, num_kv_heads=2,
+                        block_size=8, dtype=dtype)
+    ref = reference(w)
+    got = run(w)
+    assert np.isfinite(got).all()
+    err = float(np.abs(got - ref).max())
+    assert err <= 2e-2, f"max abs error {err}"
