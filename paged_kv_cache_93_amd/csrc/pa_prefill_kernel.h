@@ -136,38 +136,56 @@ __device__ __forceinline__ void softmax_step(f32x4 (&s)[NR][2], u32x4 (&pf)[NR],
           if (k > pos[rt] || k < lo_row[rt]) s[rt][h][v] = kNegInf;
         }
   }
+  // The exponent base moves only when the row maximum passes it by more than 8
+  // (log2 units): weights stay <= 2^8, the accumulators are rescaled rarely,
+  // and the result is the same softmax.  A row's maximum passes its base only
+  // if one of its four lanes' maxima does, so the lanes test their own maxima
+  // first and the row maxima (two lane swaps each) and the new bases are
+  // taken only when some row of the wave moves.
+  float lmx[NR], base[NR], alpha[NR];
+  bool up = false;
 #pragma unroll
   for (int rt = 0; rt < NR; ++rt) {
-    float mx = fmaxf(fmaxf(fmaxf(s[rt][0][0], s[rt][0][1]), fmaxf(s[rt][0][2], s[rt][0][3])),
-                     fmaxf(fmaxf(s[rt][1][0], s[rt][1][1]), fmaxf(s[rt][1][2], s[rt][1][3])));
-    mx = xor_max<16>(mx);
-    if constexpr (!AL) mx *= sc;
-    // The exponent base moves only when the row maximum passes it by more
-    // than 8 (log2 units): weights stay <= 2^8, the accumulators are
-    // rescaled rarely, and the result is the same softmax.
-    const bool move = mx > m[rt] + 8.f;
-    const float mnew = move ? mx : m[rt];
-    const float base = mnew == kNegInf ? 0.f : mnew;
-    const float alpha = move ? fast_exp2(m[rt] - base) : 1.f;
-    m[rt] = mnew;
+    lmx[rt] = fmaxf(fmaxf(fmaxf(s[rt][0][0], s[rt][0][1]), fmaxf(s[rt][0][2], s[rt][0][3])),
+                    fmaxf(fmaxf(s[rt][1][0], s[rt][1][1]), fmaxf(s[rt][1][2], s[rt][1][3])));
+    up |= (AL ? lmx[rt] : lmx[rt] * sc) > m[rt] + 8.f;
+    base[rt] = m[rt] == kNegInf ? 0.f : m[rt];
+    alpha[rt] = 1.f;
+  }
+  bool moved[NR] = {};
+  if (__ballot(up) != 0) {
+#pragma unroll
+    for (int rt = 0; rt < NR; ++rt) {
+      float mx = xor_max<16>(lmx[rt]);
+      if constexpr (!AL) mx *= sc;
+      const bool move = mx > m[rt] + 8.f;
+      const float mnew = move ? mx : m[rt];
+      base[rt] = mnew == kNegInf ? 0.f : mnew;
+      alpha[rt] = move ? fast_exp2(m[rt] - base[rt]) : 1.f;
+      m[rt] = mnew;
+      moved[rt] = __ballot(move) != 0;
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < NR; ++rt) {
     float psum = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int h = w >> 1, v = 2 * (w & 1);
       f32x2 pp;
       if constexpr (AL)
-        pp = f32x2{fast_exp2(s[rt][h][v] - base), fast_exp2(s[rt][h][v + 1] - base)};
+        pp = f32x2{fast_exp2(s[rt][h][v] - base[rt]), fast_exp2(s[rt][h][v + 1] - base[rt])};
       else
-        pp = f32x2{fast_exp2(fmaf(s[rt][h][v], sc, -base)),
-                   fast_exp2(fmaf(s[rt][h][v + 1], sc, -base))};
+        pp = f32x2{fast_exp2(fmaf(s[rt][h][v], sc, -base[rt])),
+                   fast_exp2(fmaf(s[rt][h][v + 1], sc, -base[rt]))};
       const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
       pf[rt][w] = __builtin_bit_cast(uint32_t, pb);
       psum = __builtin_amdgcn_fdot2_f32_bf16(pb, kOnes, psum, false);  // adds the rounded pair
     }
-    lsum[rt] = fmaf(lsum[rt], alpha, psum);
-    if (__ballot(move) != 0) {
+    lsum[rt] = fmaf(lsum[rt], alpha[rt], psum);
+    if (moved[rt]) {
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) acc[rt][dt] *= alpha;
+      for (int dt = 0; dt < 8; ++dt) acc[rt][dt] *= alpha[rt];
     }
   }
 }
