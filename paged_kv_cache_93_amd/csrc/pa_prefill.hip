@@ -6,62 +6,127 @@ namespace pa {
 namespace pf {
 namespace {
 
-// The tile map: tile t of the grid -> (sequence, tile of that sequence), each
-// sequence's tiles from its last (longest context) to its first.  One
-// workgroup of 1024 threads takes 1024 sequences at a time: it scans their
-// tile counts, then all threads write the chunk's (sequence, tile) pairs
-// together, each finding the sequence of its tile by binary search over the
-// chunk's running ends (a thread per sequence writing its own pairs would
-// leave a long prompt's hundreds of pairs to one thread).
-__global__ void __launch_bounds__(1024) prefill_tiles_kernel(const int32_t* qs, int32_t S,
-                                                             int32_t T, int32_t tt,
+// The tile map: tile t of the grid -> (sequence, tile of that sequence),
+// longest walk first.  Workgroups start in grid order (and each XCD takes a
+// contiguous run of the map, see the kernels' id remap), so with the tiles
+// that walk the most key tiles dispatched first the run ends with short ones
+// - a longest-processing-time-first order, which keeps the last long walks
+// off the end of the launch and mixes walks that stream keys from memory (a
+// decode row's, a long context's) with ones that compute on few.  The order
+// does not change any output: every tile writes its own rows.
+//
+// One workgroup of 1024 threads.  It enumerates the tiles twice, 1024
+// sequences at a time: it scans their tile counts, and all threads take the
+// chunk's tiles together, each finding the sequence of its tile by binary
+// search over the chunk's running ends (a thread per sequence would leave a
+// long prompt's hundreds of tiles to one thread).  The first pass counts the
+// tiles per walk length (kBuckets buckets of equal width up to the longest
+// possible walk), the second places each tile after all tiles of longer
+// buckets (within a bucket, in the order the threads' slot claims land).
+constexpr int kBuckets = 512;
+
+__global__ void __launch_bounds__(1024) prefill_tiles_kernel(const int32_t* qs,
+                                                             const int32_t* context_lens,
+                                                             int32_t S, int32_t T, int32_t tt,
+                                                             int32_t max_len, int32_t window,
                                                              int32_t* tiles, int32_t max_tiles) {
   __shared__ int32_t s_wave[16];
   __shared__ int32_t s_total;
   __shared__ int32_t s_end[1024];  // end (exclusive) of sequence base + j's tiles in the chunk
+  __shared__ int32_t s_count[kBuckets];  // tiles per bucket, then the next free slot
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kBuckets; i += 1024) s_count[i] = 0;
+  // key tiles the walk of (sequence seq, tile j) takes, as the attention
+  // kernels count them, and its bucket (longest walks in bucket 0)
+  const int64_t max_walk = (int64_t(max_len) + kKeys - 1) / kKeys;
+  auto bucket = [&](int32_t seq, int32_t j) {
+    const int32_t a = min(max(qs[seq], 0), T), b = min(max(qs[seq + 1], 0), T);
+    const int32_t n = b - a;
+    const int32_t L = min(max(context_lens[seq], 0), max_len);
+    const int32_t c = L - n;
+    const int32_t j0 = j * tt, j1 = min(j0 + tt, n);
+    const int32_t kend = c + j1;
+    int64_t walk = 0;
+    if (kend > 0 && j1 > j0) {
+      const int32_t ntiles = (kend + kKeys - 1) / kKeys;
+      const int32_t kt0 = window > 0 ? max(0, c + j0 - window + 1) / kKeys : 0;
+      walk = max(ntiles - kt0, 0);
+    }
+    const int64_t q = walk * kBuckets / (max_walk + 1);
+    return kBuckets - 1 - int(min<int64_t>(q, kBuckets - 1));
+  };
   int32_t running = 0;
-  for (int32_t base = 0; base < S; base += 1024) {
-    const int32_t i = base + tid;
-    int32_t n = 0;
-    if (i < S) {
-      const int32_t a = min(max(qs[i], 0), T), b = min(max(qs[i + 1], 0), T);
-      n = max(b - a, 0);
-    }
-    const int32_t cnt = (n + tt - 1) / tt;
-    const int32_t incl = wave_inclusive_sum(cnt);
-    if (lane == 63) s_wave[wave] = incl;
-    __syncthreads();
-    if (tid == 0) {
-      int32_t acc = 0;
-      for (int w = 0; w < 16; ++w) {
-        const int32_t v = s_wave[w];
-        s_wave[w] = acc;
-        acc += v;
+  for (int pass = 0; pass < 2; ++pass) {
+    running = 0;
+    for (int32_t base = 0; base < S; base += 1024) {
+      const int32_t i = base + tid;
+      int32_t n = 0;
+      if (i < S) {
+        const int32_t a = min(max(qs[i], 0), T), b = min(max(qs[i + 1], 0), T);
+        n = max(b - a, 0);
       }
-      s_total = acc;
-    }
-    __syncthreads();
-    s_end[tid] = s_wave[wave] + incl;
-    __syncthreads();
-    const int32_t total = s_total;
-    for (int32_t t = tid; t < total; t += 1024) {
-      int lo = 0, hi = 1023;  // first j with s_end[j] > t (s_end[1023] == total > t)
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (s_end[mid] > t) hi = mid; else lo = mid + 1;
+      const int32_t cnt = (n + tt - 1) / tt;
+      const int32_t incl = wave_inclusive_sum(cnt);
+      if (lane == 63) s_wave[wave] = incl;
+      __syncthreads();
+      if (tid == 0) {
+        int32_t acc = 0;
+        for (int w = 0; w < 16; ++w) {
+          const int32_t v = s_wave[w];
+          s_wave[w] = acc;
+          acc += v;
+        }
+        s_total = acc;
       }
-      const int32_t start = lo > 0 ? s_end[lo - 1] : 0;
-      const int32_t seq_cnt = s_end[lo] - start;
-      const int32_t gt = running + t;
-      if (gt < max_tiles) {
-        tiles[1 + 2 * gt] = base + lo;
-        tiles[2 + 2 * gt] = seq_cnt - 1 - (t - start);
+      __syncthreads();
+      s_end[tid] = s_wave[wave] + incl;
+      __syncthreads();
+      const int32_t total = s_total;
+      for (int32_t t = tid; t < total; t += 1024) {
+        int lo = 0, hi = 1023;  // first j with s_end[j] > t (s_end[1023] == total > t)
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (s_end[mid] > t) hi = mid; else lo = mid + 1;
+        }
+        const int32_t start = lo > 0 ? s_end[lo - 1] : 0;
+        const int32_t seq_cnt = s_end[lo] - start;
+        const int32_t seq = base + lo;
+        const int32_t j = seq_cnt - 1 - (t - start);  // the sequence's last tile first
+        if (running + t >= max_tiles) continue;
+        const int k = bucket(seq, j);
+        if (pass == 0) {
+          atomicAdd(&s_count[k], 1);
+        } else {
+          const int32_t slot = atomicAdd(&s_count[k], 1);
+          if (slot < max_tiles) {
+            tiles[1 + 2 * slot] = seq;
+            tiles[2 + 2 * slot] = j;
+          }
+        }
       }
+      running += total;
+      __syncthreads();
     }
-    running += total;
-    __syncthreads();
+    if (pass == 0) {
+      // bucket counts -> first slot of each bucket (exclusive prefix sum)
+      static_assert(kBuckets <= 1024, "one bucket per thread");
+      const int32_t v = tid < kBuckets ? s_count[tid] : 0;
+      const int32_t incl = wave_inclusive_sum(v);
+      if (lane == 63) s_wave[wave] = incl;
+      __syncthreads();
+      if (tid == 0) {
+        int32_t acc = 0;
+        for (int w = 0; w < 16; ++w) {
+          const int32_t x = s_wave[w];
+          s_wave[w] = acc;
+          acc += x;
+        }
+      }
+      __syncthreads();
+      if (tid < kBuckets) s_count[tid] = s_wave[wave] + incl - v;
+      __syncthreads();
+    }
   }
   if (tid == 0) tiles[0] = min(running, max_tiles);
 }
@@ -145,8 +210,10 @@ PA_API int pa_prefill(const pa_cache* cache, const void* q, const int32_t* block
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* tiles = static_cast<int32_t*>(workspace);
-  hipLaunchKernelGGL(prefill_tiles_kernel, dim3(1), dim3(1024), 0, s, query_start, num_seqs,
-                     num_tokens, tokens_per_tile(group), tiles, int32_t(max_tiles));
+  hipLaunchKernelGGL(prefill_tiles_kernel, dim3(1), dim3(1024), 0, s, query_start, context_lens,
+                     num_seqs, num_tokens, tokens_per_tile(group),
+                     int32_t(int64_t(max_blocks_per_seq) * cache->block_size), window, tiles,
+                     int32_t(max_tiles));
   if (int st = launch_result("pa_prefill")) return st;
 
   PrefillArgs a;
