@@ -49,9 +49,8 @@ constexpr int kRows = 128;        // query rows per workgroup tile
 constexpr int kWaves = 4;
 constexpr int kKeys = 32;         // keys per K/V tile
 constexpr int kKStride = 17;      // 16-byte chunks per K row in LDS (16 + 1 pad)
-constexpr int kVStride = 36;      // bf16 per transposed V row in LDS (32 + 4 pad)
 constexpr int kKBytes = kKeys * kKStride * 16;
-constexpr int kVBytes = kD * kVStride * 2;
+constexpr int kVBytes = kKeys * kD * 2;  // V rows of 256 bytes, pieces swizzled
 constexpr int kBufBytes = kKBytes + kVBytes;
 // Block-table entries a workgroup keeps in LDS behind its tile buffers: a
 // window of the walk's blocks, reloaded when the walk passes its end.  (Vector
@@ -67,11 +66,15 @@ constexpr int kTblWin = 1024;
 #define PA_PREFILL_DMA 1  // 0: bf16 caches take the register-staged kernel too (for comparison)
 #endif
 
-// Key-pair slot swizzle of the transposed V tile: dims 32x..32x+31 XOR their
-// pair slot with 4x (an even number, so the two pairs a fragment read takes
-// stay adjacent).  With 72-byte rows, the transposed writes of a wave (16 dim
-// chunks x 4 key pairs) then land in 64 distinct banks.
-__device__ __forceinline__ int vswz(int dim) { return 4 * ((dim >> 5) & 3); }
+#ifndef PA_PREFILL_KSWZ
+#define PA_PREFILL_KSWZ 16  // K rows whose pieces the swizzle spreads (16; 8 for comparison)
+#endif
+#ifndef PA_PREFILL_VSWZ
+#define PA_PREFILL_VSWZ 8   // V rows whose piece pairs the swizzle spreads (8; 4 for comparison)
+#endif
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+#define PA_LDS(T) __attribute__((address_space(3))) T
 
 constexpr bf16x2 kOnes = {__bf16(1.0f), __bf16(1.0f)};
 
@@ -257,15 +260,19 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 
   // ---- K/V tile staging -------------------------------------------------------
   // Thread tid loads dims [8*dc, 8*dc+8) of keys 2kp and 2kp+1 of a tile (one
-  // block: block sizes are even).  Loads run two tiles ahead of the math (two
+  // block: block sizes are even), into its register pair e = 0, 1 as keys
+  // 2kp + (e ^ par), par = kp % 2: a 16-byte LDS store of register e then
+  // writes rows of both parities in each half-wave (rows 256 bytes apart fall
+  // in different bank halves), where keys in order would put two rows of one
+  // parity on the same banks.  Loads run two tiles ahead of the math (two
   // register sets).  Every walk step issues the same four loads, so the
   // compiler's wait before a register set is stored counts exactly the loads
   // issued after it: keys past the context and blocks outside the pool read
   // block 0 of the pool instead, and a per-set mask zeroes those rows when the
   // set is stored.
-  const int dc = tid & 15, kp = tid >> 4;
+  const int dc = tid & 15, kp = tid >> 4, par = kp & 1;
   Raw kr[2][2], vr[2][2];
-  int zmask[2] = {0, 0};  // bit e: key 2kp+e of the set's tile reads as zero
+  int zmask[2] = {0, 0};  // bit e: key 2kp + (e ^ par) of the set's tile reads as zero
   // key 2kp of a tile sits at row (2kp) % BS of its block (tiles start at
   // multiples of 32, a multiple of BS), so a lane's offset inside a block is fixed
   constexpr int kRowBytes = kD * EB;
@@ -288,34 +295,27 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
   auto load_tile = [&](int set, int k0) {
     const int key = k0 + 2 * kp;  // and key + 1, in the same block
     const int phys = key < kend ? s_tbl[key / BS - tbl0] : -1;
-    zmask[set] = phys < 0 ? 3 : (key + 1 < kend ? 0 : 2);
+    zmask[set] = phys < 0 ? 3 : (key + 1 < kend ? 0 : (par ? 1 : 2));
     const int64_t off = int64_t(phys < 0 ? 0 : phys) * blk_stride + lane_off;
-    kr[set][0] = *reinterpret_cast<const Raw*>(a.k_pool + off);
-    kr[set][1] = *reinterpret_cast<const Raw*>(a.k_pool + off + kRowBytes);
-    vr[set][0] = *reinterpret_cast<const Raw*>(a.v_pool + off);
-    vr[set][1] = *reinterpret_cast<const Raw*>(a.v_pool + off + kRowBytes);
+    const int64_t o0 = off + par * kRowBytes, o1 = off + (par ^ 1) * kRowBytes;
+    kr[set][0] = *reinterpret_cast<const Raw*>(a.k_pool + o0);
+    kr[set][1] = *reinterpret_cast<const Raw*>(a.k_pool + o1);
+    vr[set][0] = *reinterpret_cast<const Raw*>(a.v_pool + o0);
+    vr[set][1] = *reinterpret_cast<const Raw*>(a.v_pool + o1);
   };
   auto store_tile = [&](int set, int buf) {
     u32x4* lk = reinterpret_cast<u32x4*>(s_mem + buf * kBufBytes);
-    uint32_t* lv = reinterpret_cast<uint32_t*>(s_mem + buf * kBufBytes + kKBytes);
-    u32x4 kb[2], vb[2];
+    uint8_t* lv = s_mem + buf * kBufBytes + kKBytes;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
+      const int row = 2 * kp + (e ^ par);
       const bool z = (zmask[set] >> e) & 1;
-      kb[e] = z ? u32x4{0u, 0u, 0u, 0u} : score_chunk<ET>(kr[set][e]);
-      vb[e] = z ? u32x4{0u, 0u, 0u, 0u} : score_chunk<ET>(vr[set][e]);
-      lk[(2 * kp + e) * kKStride + dc] = kb[e];
-    }
-    // V transposed: dim 8dc + x gets the pair (key 2kp, key 2kp+1) as one word,
-    // at pair slot kp ^ vswz(dim) (a wave's 64 writes hit 64 distinct banks)
-    const int kps = kp ^ vswz(8 * dc);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t a0 = vb[0][w], a1 = vb[1][w];  // dims 8dc+2w, 8dc+2w+1 of each key
-      // low halves of both words, then high halves (v_perm byte selects)
-      lv[((8 * dc + 2 * w) * kVStride) / 2 + kps] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-      lv[((8 * dc + 2 * w + 1) * kVStride) / 2 + kps] =
-          __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+      const u32x4 kb = z ? u32x4{0u, 0u, 0u, 0u} : score_chunk<ET>(kr[set][e]);
+      const u32x4 vb = z ? u32x4{0u, 0u, 0u, 0u} : score_chunk<ET>(vr[set][e]);
+      lk[row * kKStride + dc] = kb;
+      // V row-major as in the bf16 kernel's ring: piece dc at dc ^ 2(row % 8)
+      *reinterpret_cast<u32x4*>(lv + row * (kD * 2) +
+                                ((dc ^ (2 * (row & (PA_PREFILL_VSWZ - 1)))) << 4)) = vb;
     }
   };
 
@@ -408,15 +408,25 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     softmax_step<AL>(s, pf, k0, pos, lo_row, slope2, min_pos, max_pos, W, sl2, grp, m,
                      lsum, acc);
 
-    // O^T += V^T P^T: A = dims 16dt + r, keys in the permuted k order
+    // O^T += V^T P^T: two transposed reads give keys 4g..4g+3 and 16+4g..16+4g+3
+    // of dim 16dt + (lane % 16) (the layout and reads of the bf16 kernel)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const int dim = 16 * dt + r16;
-      const uint8_t* row = lv + dim * kVStride * 2;
-      const int sw = vswz(dim);
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(row + 4 * ((2 * grp) ^ sw));
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 4 * ((8 + 2 * grp) ^ sw));
-      const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+      v4s half[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int row = 16 * hh + 4 * grp + (r16 >> 2);
+        const int lc = 2 * dt + ((r16 & 3) >> 1);  // logical 16-byte piece
+        const int off = row * (kD * 2) + ((lc ^ (2 * (row & (PA_PREFILL_VSWZ - 1)))) << 4) +
+                        ((r16 & 1) << 3);
+        half[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (PA_LDS(v4s)*)((PA_LDS(uint8_t)*)lv + off));
+      }
+      const u32x4 vf = {
+          __builtin_bit_cast(uint32_t, __builtin_shufflevector(half[0], half[0], 0, 1)),
+          __builtin_bit_cast(uint32_t, __builtin_shufflevector(half[0], half[0], 2, 3)),
+          __builtin_bit_cast(uint32_t, __builtin_shufflevector(half[1], half[1], 0, 1)),
+          __builtin_bit_cast(uint32_t, __builtin_shufflevector(half[1], half[1], 2, 3))};
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
         acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -479,20 +489,9 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
 // id outside the pool) are zeroed in LDS before the tile is used, so that a
 // zero weight never meets a NaN.
 
-#ifndef PA_PREFILL_KSWZ
-#define PA_PREFILL_KSWZ 16  // K rows whose pieces the swizzle spreads (16; 8 for comparison)
-#endif
-#ifndef PA_PREFILL_VSWZ
-#define PA_PREFILL_VSWZ 8   // V rows whose piece pairs the swizzle spreads (8; 4 for comparison)
-#endif
-
 constexpr int kStages = 3;
 constexpr int kStageBytes = 2 * kKeys * kD * 2;  // K and V tiles, 16 KiB
 constexpr size_t kDmaLdsBytes = size_t(kStages) * kStageBytes + kTblWin * sizeof(int32_t);
-
-typedef short v4s __attribute__((ext_vector_type(4)));
-#define PA_LDS(T) __attribute__((address_space(3))) T
-
 
 template <int BS, int G, bool OUT_F32, bool AL, int NRT>
 __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
