@@ -17,12 +17,12 @@
 //   KV head (rows past those tokens are idle), so every K/V row the tile
 //   loads serves all of them.  Each wave owns 32 rows (two 16-row MFMA tiles).
 // * The tile walks its keys 32 at a time (positions 0 .. its last row's
-//   position).  The workgroup stages each 32-key K/V tile in LDS (double
-//   buffered, the next tile's global loads in flight during the current one's
-//   math): K row-major (the MFMA A operand of S^T = K Q^T reads 16-byte row
-//   pieces), V transposed (the A operand of O^T = V^T P^T needs keys
-//   contiguous per dimension).  8-bit codes become bf16 on the way into LDS
-//   (exact; the scales are folded into the score scale and the output).
+//   position).  The workgroup stages each 32-key K/V tile in LDS, row-major
+//   with XOR-swizzled 16-byte pieces: the MFMA A operand of S^T = K Q^T reads
+//   16-byte K row pieces, and the A operand of O^T = V^T P^T (keys contiguous
+//   per dimension) comes from the transposed LDS read.  bf16 tiles go in by
+//   LDS DMA; 8-bit codes become bf16 in registers on the way in (exact; the
+//   scales are folded into the score scale and the output).
 // * Scores come out as S^T, so lane 16g + r holds keys 4g..4g+3 (and 16 +
 //   4g..) of query row r: the softmax weights P are already the B operand of
 //   O^T = V^T P^T in that lane (the k order of the two operands is permuted
@@ -48,9 +48,10 @@ constexpr int kD = 128;           // head dim
 constexpr int kRows = 128;        // query rows per workgroup tile
 constexpr int kWaves = 4;
 constexpr int kKeys = 32;         // keys per K/V tile
-constexpr int kKStride = 17;      // 16-byte chunks per K row in LDS (16 + 1 pad)
-constexpr int kKBytes = kKeys * kKStride * 16;
-constexpr int kVBytes = kKeys * kD * 2;  // V rows of 256 bytes, pieces swizzled
+// The register-staged kernel's K and V tiles in LDS: bf16 rows of 256 bytes
+// with the bf16 ring's piece swizzles
+constexpr int kKBytes = kKeys * kD * 2;
+constexpr int kVBytes = kKeys * kD * 2;
 constexpr int kBufBytes = kKBytes + kVBytes;
 // Block-table entries a workgroup keeps in LDS behind its tile buffers: a
 // window of the walk's blocks, reloaded when the walk passes its end.  (Vector
@@ -312,7 +313,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
       const bool z = (zmask[set] >> e) & 1;
       const u32x4 kb = z ? u32x4{0u, 0u, 0u, 0u} : score_chunk<ET>(kr[set][e]);
       const u32x4 vb = z ? u32x4{0u, 0u, 0u, 0u} : score_chunk<ET>(vr[set][e]);
-      lk[row * kKStride + dc] = kb;
+      // K row-major as in the bf16 kernel's ring: piece dc at dc ^ (row % 16)
+      lk[row * 16 + (dc ^ (row & (PA_PREFILL_KSWZ - 1)))] = kb;
       // V row-major as in the bf16 kernel's ring: piece dc at dc ^ 2(row % 8)
       *reinterpret_cast<u32x4*>(lv + row * (kD * 2) +
                                 ((dc ^ (2 * (row & (PA_PREFILL_VSWZ - 1)))) << 4)) = vb;
@@ -395,7 +397,8 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int mm = 0; mm < 4; ++mm) {
-        const u32x4 kf = lk[(16 * h + r16) * kKStride + 4 * mm + grp];
+        const int row = 16 * h + r16;
+        const u32x4 kf = lk[row * 16 + ((4 * mm + grp) ^ (row & (PA_PREFILL_KSWZ - 1)))];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
           s[rt][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
