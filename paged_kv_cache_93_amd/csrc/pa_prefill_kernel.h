@@ -28,10 +28,12 @@
 //   O^T = V^T P^T in that lane (the k order of the two operands is permuted
 //   alike), and the output O^T lands in the lane that owns the row's running
 //   max and sum - no shuffles except two lane swaps for the row maximum.
-// * Weights are rounded to bf16 for the matrix product, and the running sum
-//   adds the rounded weights, so the output is an exact convex combination of
-//   V rows; each weight is rounded to nearest even (within 2^-8 of its value,
-//   relative), so after the normalisation the weights are within about 2^-7.
+// * For a bf16 output, weights are rounded to bf16 for the matrix product, and
+//   the running sum adds the rounded weights, so the output is an exact convex
+//   combination of V rows; each weight is rounded to nearest even (within 2^-8
+//   of its value, relative), so after the normalisation the weights are within
+//   about 2^-7.  For a float32 output each weight enters the product as three
+//   bf16 terms (within 2^-24 of it) and the sum adds the float32 weights.
 #pragma once
 
 #include <type_traits>
@@ -111,12 +113,21 @@ struct PrefillArgs {
 // past the workgroup's first position (or, with a window, start before its
 // last row's window) need masks; without ALiBi the max is taken on raw
 // scores (the scale is positive) and the scale enters with the exponent's fma.
-template <bool AL, int NR = 2>
-__device__ __forceinline__ void softmax_step(f32x4 (&s)[NR][2], u32x4 (&pf)[NR], int k0,
+//
+// PT: bf16 terms per weight.  With one, each weight is rounded to bf16 and
+// the running sum adds the rounded weights (the output is an exact convex
+// combination of V rows with weights within about 2^-7 of the true ones).
+// With three (float32 outputs), weight p goes in as hi + mid + lo, hi its
+// bf16 rounding, mid that of p - hi, lo that of the rest (both differences
+// exact in float32), which leaves p within 2^-24 of its value; the running
+// sum adds the float32 weights.  pf[t][rt] is term t.
+template <bool AL, int NR = 2, int PT = 1>
+__device__ __forceinline__ void softmax_step(f32x4 (&s)[NR][2], u32x4 (&pf)[PT][NR], int k0,
                                              const int (&pos)[NR], const int (&lo_row)[NR],
                                              const float (&slope2)[NR], int min_pos, int max_pos,
                                              int W, float sc, int grp, float (&m)[NR],
                                              float (&lsum)[NR], f32x4 (&acc)[NR][8]) {
+  static_assert(PT == 1 || PT == 3, "one or three bf16 terms per weight");
   if constexpr (AL) {
     // scores to log2 units plus slope * (key - position)
 #pragma unroll
@@ -183,8 +194,17 @@ __device__ __forceinline__ void softmax_step(f32x4 (&s)[NR][2], u32x4 (&pf)[NR],
         pp = f32x2{fast_exp2(fmaf(s[rt][h][v], sc, -base[rt])),
                    fast_exp2(fmaf(s[rt][h][v + 1], sc, -base[rt]))};
       const bf16x2 pb = __builtin_convertvector(pp, bf16x2);
-      pf[rt][w] = __builtin_bit_cast(uint32_t, pb);
-      psum = __builtin_amdgcn_fdot2_f32_bf16(pb, kOnes, psum, false);  // adds the rounded pair
+      pf[0][rt][w] = __builtin_bit_cast(uint32_t, pb);
+      if constexpr (PT == 1) {
+        psum = __builtin_amdgcn_fdot2_f32_bf16(pb, kOnes, psum, false);  // adds the rounded pair
+      } else {
+        const f32x2 r1 = pp - __builtin_convertvector(pb, f32x2);
+        const bf16x2 pm = __builtin_convertvector(r1, bf16x2);
+        const f32x2 r2 = r1 - __builtin_convertvector(pm, f32x2);
+        pf[1][rt][w] = __builtin_bit_cast(uint32_t, pm);
+        pf[2][rt][w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, bf16x2));
+        psum += pp[0] + pp[1];
+      }
     }
     lsum[rt] = fmaf(lsum[rt], alpha[rt], psum);
     if (moved[rt]) {
@@ -407,9 +427,10 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
       }
     }
 
-    u32x4 pf[2];
-    softmax_step<AL>(s, pf, k0, pos, lo_row, slope2, min_pos, max_pos, W, sl2, grp, m,
-                     lsum, acc);
+    constexpr int PT = OUT_F32 ? 3 : 1;  // bf16 terms per weight
+    u32x4 pf[PT][2];
+    softmax_step<AL, 2, PT>(s, pf, k0, pos, lo_row, slope2, min_pos, max_pos, W, sl2, grp, m,
+                            lsum, acc);
 
     // O^T += V^T P^T: two transposed reads give keys 4g..4g+3 and 16+4g..16+4g+3
     // of dim 16dt + (lane % 16) (the layout and reads of the bf16 kernel)
@@ -431,10 +452,12 @@ __global__ void __launch_bounds__(256, 2) prefill_kernel(PrefillArgs a) {
           __builtin_bit_cast(uint32_t, __builtin_shufflevector(half[1], half[1], 0, 1)),
           __builtin_bit_cast(uint32_t, __builtin_shufflevector(half[1], half[1], 2, 3))};
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-        acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, vf), __builtin_bit_cast(bf16x8, pf[rt]), acc[rt][dt], 0,
-            0, 0);
+      for (int t = 0; t < PT; ++t)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, vf), __builtin_bit_cast(bf16x8, pf[t][rt]), acc[rt][dt],
+              0, 0, 0);
     }
     }  // busy
 
@@ -723,9 +746,10 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
       }
     }
 
-    u32x4 pf[NRT];
-    softmax_step<AL, NRT>(sc4, pf, k0, pos, lo_row, slope2, min_pos, max_pos, W, sl2,
-                          grp, m, lsum, acc);
+    constexpr int PT = OUT_F32 ? 3 : 1;  // bf16 terms per weight
+    u32x4 pf[PT][NRT];
+    softmax_step<AL, NRT, PT>(sc4, pf, k0, pos, lo_row, slope2, min_pos, max_pos, W, sl2,
+                              grp, m, lsum, acc);
 
     // O^T += V^T P^T: two transposed reads give keys 4g..4g+3 and 16+4g..16+4g+3
     // of dim 16dt + (lane % 16)
@@ -746,10 +770,12 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
                         __builtin_bit_cast(uint32_t, __builtin_shufflevector(half[1], half[1], 0, 1)),
                         __builtin_bit_cast(uint32_t, __builtin_shufflevector(half[1], half[1], 2, 3))};
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
-        acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, vf), __builtin_bit_cast(bf16x8, pf[rt]), acc[rt][dt], 0,
-            0, 0);
+      for (int t = 0; t < PT; ++t)
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, vf), __builtin_bit_cast(bf16x8, pf[t][rt]), acc[rt][dt],
+              0, 0, 0);
     }
     }  // busy
   };

@@ -136,7 +136,7 @@ def test_engine_loop_matches_the_oracle(dtype, mode):
                                          np.array(po.context_lens, np.int32), 1.0 / math.sqrt(D),
                                          dtype, k_scale=k_scale, v_scale=v_scale)
                 err_all = float(np.abs(out_all.cpu().numpy().astype(np.float64) - ref_all).max())
-                assert err_all <= 2e-2, f"step {state['steps']}: prefill max abs error {err_all}"
+                assert err_all <= 1e-5, f"step {state['steps']}: prefill max abs error {err_all}"
                 state["worst_prefill"] = max(state["worst_prefill"], err_all)
                 state["prompt_rows"] += len(idents) - S
         state["steps"] += 1

@@ -121,4 +121,4 @@ def test_prefill_mixed_batch(group):
     for i in range(len(lens)):
         if w.context_lens[i] >= nq[i]:
             rows[w.query_start[i]:w.query_start[i + 1]] = True
-    assert np.abs(got[rows] - ref[rows]).max() <= 2e-2
+    assert np.abs(got[rows] - ref[rows]).max() <= 1e-5  # float32 output

@@ -1,15 +1,19 @@
 """pa_prefill (mixed-batch causal attention) on the GPU against oracle.prefill.
 
-Tolerance.  The kernel rounds each softmax weight to bf16 (round to nearest
-even, relative error at most u = 2^-8) for the P.V matrix product and divides
-by the sum of the rounded weights, so its output is a convex combination of V
-rows whose weights are within about 1 +- 2^-7 of the exact ones: in the worst
-case |out - exact| <= 2^-7 * max_t |v_t| plus the output's own rounding (2^-8
-relative for bf16).  The seeded N(0,1) cases here (|v| < 5, worst case ~0.06)
-are held to 2e-2, which they meet with margin because the weights' rounding
-errors have both signs and largely cancel.  A zero query makes
-every weight exactly 1, so there the float32 output must equal the oracle's
-mean of the visible rows to 1e-5 - which catches a key too many or too few.
+Tolerance.  For a bf16 output the kernel rounds each softmax weight to bf16
+(round to nearest even, relative error at most u = 2^-8) for the P.V matrix
+product and divides by the sum of the rounded weights, so its output is a
+convex combination of V rows whose weights are within about 1 +- 2^-7 of the
+exact ones: in the worst case |out - exact| <= 2^-7 * max_t |v_t| plus the
+output's own rounding (2^-8 relative).  The seeded N(0,1) cases here (|v| < 5,
+worst case ~0.06) are held to 2e-2, which they meet with margin because the
+weights' rounding errors have both signs and largely cancel.  For a float32
+output each weight enters the product as three bf16 terms (within 2^-24 of
+it) and the sum adds the float32 weights, so what is left is float32
+arithmetic: those outputs are held to 1e-5, as decode's are.  A zero query
+makes every weight exactly 1, so there the float32 output must equal the
+oracle's mean of the visible rows to 1e-5 - which catches a key too many or
+too few.
 """
 
 import math
@@ -24,6 +28,14 @@ from paged_kv_cache_93_amd import lib
 from paged_kv_cache_93_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
+
+
+F32_TOL = 1e-5   # float32 outputs
+BF16_TOL = 2e-2  # bf16 outputs
+
+
+def tol(out_f32):
+    return F32_TOL if out_f32 else BF16_TOL
 
 
 def upload(w):
@@ -71,7 +83,7 @@ def test_prefill_matches_the_oracle(dtype, bs, hq, hkv):
         got = run(w, t, out_f32)
         assert np.isfinite(got).all()
         err = float(np.abs(got - ref).max())
-        assert err <= 2e-2, f"max abs error {err} (f32 out: {out_f32})"
+        assert err <= tol(out_f32), f"max abs error {err} (f32 out: {out_f32})"
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
@@ -89,7 +101,7 @@ def test_rows_of_empty_sequences_are_not_written():
     got = run(w, sentinel=123.0)
     # sequence 1 owns no rows; every row of the other two is written
     assert got.shape[0] == 8 and not (got == 123.0).any()
-    assert np.abs(got - reference(w)).max() <= 2e-2
+    assert np.abs(got - reference(w)).max() <= F32_TOL
 
 
 def test_too_many_query_tokens_give_zero_rows():
@@ -101,7 +113,7 @@ def test_too_many_query_tokens_give_zero_rows():
     w.q, w.query_start = q3, np.array([0, 3], np.int32)
     got = run(w)
     ref = reference(w)
-    assert not got[0].any() and np.abs(got - ref).max() <= 2e-2
+    assert not got[0].any() and np.abs(got - ref).max() <= F32_TOL
 
 
 @pytest.mark.parametrize("name", ["cached_preamble", "long_prompts", "mixed_step"])
@@ -123,7 +135,7 @@ def test_named_workloads_on_sampled_rows(name):
                                 np.array([p + 1], np.int32), scale, w.dtype,
                                 k_scale=w.k_scale, v_scale=w.v_scale)
             worst = max(worst, float(np.abs(got[row] - ref[0]).max()))
-    assert worst <= 2e-2, worst
+    assert worst <= F32_TOL, worst
 
 
 # ---------------------------------------------------------------------------
@@ -159,7 +171,7 @@ def test_sliding_window_matches_the_oracle(dtype, bs, hq, hkv, window):
     w = W.prefill_batch("mix", 700 + bs + hq, *MIX, num_heads=hq, num_kv_heads=hkv,
                         block_size=bs, dtype=dtype)
     got = run_variant(w, window=window)
-    assert np.abs(got - variant_reference(w, window=window)).max() <= 2e-2
+    assert np.abs(got - variant_reference(w, window=window)).max() <= F32_TOL
 
 
 @pytest.mark.parametrize("window", [1, 5, 32, 33, 64])
@@ -177,9 +189,9 @@ def test_alibi_matches_the_oracle(dtype, hq, hkv):
     for slopes in (oracle.alibi_slopes(hq), np.random.default_rng(hq).uniform(0, 0.3, hq)):
         for out_f32 in (True, False):
             got = run_variant(w, slopes=slopes, out_f32=out_f32)
-            assert np.abs(got - variant_reference(w, slopes=slopes)).max() <= 2e-2
+            assert np.abs(got - variant_reference(w, slopes=slopes)).max() <= tol(out_f32)
         both = run_variant(w, window=20, slopes=slopes)
-        assert np.abs(both - variant_reference(w, window=20, slopes=slopes)).max() <= 2e-2
+        assert np.abs(both - variant_reference(w, window=20, slopes=slopes)).max() <= F32_TOL
 
 
 def test_decode_rows_with_variants_match_the_decode_oracle():
@@ -191,7 +203,7 @@ def test_decode_rows_with_variants_match_the_decode_oracle():
     ref = oracle.decode(w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens,
                         1.0 / math.sqrt(128), "bf16", window=256,
                         alibi_slopes=np.asarray(slopes, np.float32).astype(np.float64))
-    assert np.abs(got - ref).max() <= 2e-2
+    assert np.abs(got - ref).max() <= F32_TOL
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
@@ -205,4 +217,4 @@ def test_walk_longer_than_the_table_window(dtype):
     got = run(w)
     assert np.isfinite(got).all()
     err = float(np.abs(got - ref).max())
-    assert err <= 2e-2, f"max abs error {err}"
+    assert err <= F32_TOL, f"max abs error {err}"
