@@ -308,10 +308,12 @@ size_t pa_decode_workspace_size(const pa_cache *cache, int32_t num_seqs, int32_t
  * section "Attention kernel modification"):
  *     out[row][h] = sum_{t <= p} softmax_t(scale * q[row][h] . K_t) V_t
  * The K/V of all of a sequence's context_lens[i] positions (this step's tokens
- * included, written by pa_kv_append) must be in the cache.  The softmax
- * weights are rounded to bf16 for the matrix product (round to nearest even,
- * each within 2^-8 of its value, relative) and normalised by the sum of the
- * rounded weights.
+ * included, written by pa_kv_append) must be in the cache.  For a bf16 output
+ * the softmax weights are rounded to bf16 for the matrix product (round to
+ * nearest even, each within 2^-8 of its value, relative) and normalised by the
+ * sum of the rounded weights; for a float32 output each weight enters the
+ * product as three bf16 terms (within 2^-24 of it) and is normalised by the
+ * sum of the float32 weights (three times the P.V matrix work).
  *
  *   q             DEVICE [num_tokens][num_heads][128] bfloat16
  *   block_tables  DEVICE int32 [num_seqs][max_blocks_per_seq]
