@@ -205,7 +205,10 @@ typedef struct pa_attn_variant {
  * evenly over a fixed grid of workgroups, so long and short sequences finish
  * together; the parts of a sequence split between workgroups are merged with
  * the log-sum-exp rule by a second kernel enqueued on the same stream.
- * Without one (workspace = NULL), one workgroup walks each sequence.
+ * Without one (workspace = NULL), one workgroup walks each sequence.  The
+ * split holds every sequence's first unit in LDS, which bounds it to 16,000
+ * sequences: larger batches are walked one workgroup per sequence even with
+ * a workspace (the same attention, in the single pass's order and time).
  *
  *   q             DEVICE [num_seqs][num_heads][head_dim], cache->dtype (bfloat16
  *                 for an 8-bit cache, whose K/V values are codes times scales)
