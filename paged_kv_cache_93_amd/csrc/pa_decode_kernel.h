@@ -714,17 +714,18 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   };
 
   // current piece: units [pstart, pend) of sequence seq; `whole` when it is
-  // all of the sequence (balanced mode)
+  // all of the sequence (balanced mode).  sq is unit uu's sequence, taken from
+  // the table-entry window that covers uu (no search of the prefix).
   int seq;
   int64_t pstart, pend;
   bool whole;
-  auto start_piece = [&](int64_t uu) {
+  auto start_piece = [&](int64_t uu, int sq) {
     if (fixed_seq >= 0) {
       seq = fixed_seq;
       pend = uend;
       whole = a.mode == kModeSingle;
     } else {
-      seq = __builtin_amdgcn_readfirstlane(seq_of(uu));
+      seq = sq;
       const int64_t first = s_prefix[seq], last = s_prefix[seq + 1];
       pend = min(uend, last);
       whole = uu == first && pend == last;
@@ -786,7 +787,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     for (int k = 0; k < 2; ++k)
       if (app_seq[k] >= 0) app_in[k] = new_chunk(app_seq[k]);
   }
-  start_piece(ubeg);
+  start_piece(ubeg, __builtin_amdgcn_readlane(w0.sk, 0));
   // VALU path: the current piece's query and the next piece's, swapped at a
   // piece boundary.  (The MFMA path carries the query in the tile ring.)
   u32x4 qc_next[MF ? 1 : G];
@@ -1100,7 +1101,9 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     if (next == pend) {
       emit(seq, whole);
       if (next < uend) {
-        start_piece(next);
+        const int idx = int(next - cbase);  // <= 64: the window moves after this
+        start_piece(next, idx < 64 ? __builtin_amdgcn_readlane(w0.sk, idx)
+                                   : __builtin_amdgcn_readlane(w1.sk, idx - 64));
         if constexpr (!MF) {
 #pragma unroll
           for (int h = 0; h < G; ++h) qc[h] = qc_next[h];
