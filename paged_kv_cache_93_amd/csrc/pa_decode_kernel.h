@@ -522,16 +522,30 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
         const int d0 = 4 * (lane >> 4);
         if (whole) {
           const size_t idx = (size_t(seq) * a.num_heads + head) * D + d0;
+          // Every value is computed before the first store.  The temporaries
+          // may reuse registers of a tile whose loads the compiler still counts
+          // as pending, and a wait for those issued after a store also waits
+          // for the next tile's loads, which were issued before that store.
+          if (a.out_f32) {
+            f32x4 o[NB16];
 #pragma unroll
-          for (int b = 0; b < NB16; ++b) {
-            const f32x4 o = oacc[b] * inv;
-            if (a.out_f32) {
-              *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + idx + 16 * b) = o;
-            } else {
-              const u32x2 w = {to_bf16(o[0]) | (to_bf16(o[1]) << 16),
-                               to_bf16(o[2]) | (to_bf16(o[3]) << 16)};
-              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + idx + 16 * b) = w;
+            for (int b = 0; b < NB16; ++b) o[b] = oacc[b] * inv;
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int b = 0; b < NB16; ++b)
+              *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + idx + 16 * b) = o[b];
+          } else {
+            u32x2 w[NB16];
+#pragma unroll
+            for (int b = 0; b < NB16; ++b) {
+              const f32x4 o = oacc[b] * inv;
+              w[b] = u32x2{to_bf16(o[0]) | (to_bf16(o[1]) << 16),
+                           to_bf16(o[2]) | (to_bf16(o[3]) << 16)};
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int b = 0; b < NB16; ++b)
+              *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + idx + 16 * b) = w[b];
           }
         } else {
           size_t row;
@@ -540,13 +554,19 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
           else
             row = (size_t(blockIdx.x) + seq) * a.num_heads + head;  // piece slot g + seq
           float* o = a.part_out + row * D + d0;
+          // (all values before the first store, as above)
+          f32x4 ov[NB16];
 #pragma unroll
-          for (int b = 0; b < NB16; ++b) *reinterpret_cast<f32x4*>(o + 16 * b) = oacc[b] * inv;
+          for (int b = 0; b < NB16; ++b) ov[b] = oacc[b] * inv;
+          const float lsum = mf_top == kNegInf ? 0.f : lt * fast_exp2(mf_m - mf_top);
+          // partition partials carry natural-log maxima; pieces stay in log2 units
+          const float mx = (mf_top == kNegInf || a.mode == kModeBalanced) ? mf_top
+                                                                          : mf_top * kLn2;
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int b = 0; b < NB16; ++b) *reinterpret_cast<f32x4*>(o + 16 * b) = ov[b];
           if (lane < 16) {
-            const float lsum = mf_top == kNegInf ? 0.f : lt * fast_exp2(mf_m - mf_top);
-            // partition partials carry natural-log maxima; pieces stay in log2 units
-            a.part_max[row] = (mf_top == kNegInf || a.mode == kModeBalanced) ? mf_top
-                                                                             : mf_top * kLn2;
+            a.part_max[row] = mx;
             a.part_sum[row] = lsum;
           }
         }
@@ -719,6 +739,10 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
   int seq;
   int64_t pstart, pend;
   bool whole;
+  // a piece that ended and is closed at the start of the next step
+  bool closing = false;
+  int64_t close_at = 0;
+  int close_sq = 0;
   auto start_piece = [&](int64_t uu, int sq) {
     if (fixed_seq >= 0) {
       seq = fixed_seq;
@@ -898,7 +922,13 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
         for (int mm = 0; mm < MM; ++mm) qf[mm] = lds_q[qh * QCH + 4 * mm + (lane >> 4)];
       }
     }
-    if (nvalid <= nskip) return;  // every row masked: the state would not change
+    // Every row masked: the state would not change.  The VALU path skips the
+    // tile; the MFMA path runs it like any other (all its weights are zero,
+    // its V rows are zeroed, and the state comes out bit for bit the same),
+    // so that every path through here has read the tile's registers: code
+    // after this tile may reuse them, and a wait for their loads there would
+    // come after the next tile's loads were issued and stall until they return.
+    if (!MF && nvalid <= nskip) return;
     const bool partial = nvalid < TR || nskip > 0;
     if constexpr (MF) {
       // K tile -> LDS, then read back transposed: lane 16g + t gets row t's
@@ -1095,21 +1125,38 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     }
   };
 
+  // MFMA path: the deferred end of a piece - write it and start the next one.
+  auto close_piece = [&]() {
+    closing = false;
+    emit(seq, whole);
+    start_piece(close_at, close_sq);
+    reset_state();
+  };
+
   // After the last tile of a unit: close the piece if the unit ended it, and
   // move the table-entry window when the next unit starts a new chunk.
   auto unit_done = [&](int64_t next) {
     if (next == pend) {
-      emit(seq, whole);
+      // MFMA path: closing the piece (its output or partial write) waits on
+      // the MFMA results and the stores; unless it is the last one, it is done
+      // after the next tile's loads are issued (close_piece, at the top of the
+      // next step), so that those loads are not held back behind it.
+      if (!MF || next == uend) emit(seq, whole);
       if (next < uend) {
         const int idx = int(next - cbase);  // <= 64: the window moves after this
-        start_piece(next, idx < 64 ? __builtin_amdgcn_readlane(w0.sk, idx)
-                                   : __builtin_amdgcn_readlane(w1.sk, idx - 64));
-        if constexpr (!MF) {
+        const int sq = idx < 64 ? __builtin_amdgcn_readlane(w0.sk, idx)
+                                : __builtin_amdgcn_readlane(w1.sk, idx - 64);
+        if constexpr (MF) {
+          close_at = next;
+          close_sq = sq;
+          closing = true;
+        } else {
+          start_piece(next, sq);
 #pragma unroll
           for (int h = 0; h < G; ++h) qc[h] = qc_next[h];
           load_q(pend < uend ? __builtin_amdgcn_readfirstlane(seq_of(pend)) : seq, qc_next, qf);
+          reset_state();
         }
-        reset_state();
       }
     }
     if (next == cbase + 64) {
@@ -1202,6 +1249,9 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
       const int t = t0 + k;
       load_tile(kb[(k + PF) % NB], vb[(k + PF) % NB], qb[(k + PF) % NB], t + PF);
       if (t < ntiles) {
+        if constexpr (MF) {
+          if (closing) close_piece();
+        }
         process_tile(kb[k], vb[k], qb[k], t);
         pace(t);
         if (t % TPB == TPB - 1) unit_done(ubeg + t / TPB + 1);
