@@ -114,6 +114,7 @@ def cpu_baseline(w: W.Workload, budget_s: float, window: int = 0, alibi: bool = 
     # sequences one at a time, cycling over the batch until the time budget is spent
     done = 0
     kv = 0
+    c0 = time.process_time()  # CPU time of every thread of this process
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
         i = done % w.num_seqs
@@ -125,12 +126,18 @@ def cpu_baseline(w: W.Workload, budget_s: float, window: int = 0, alibi: bool = 
         kv += n * w.num_kv_heads * w.head_dim * 2 * W.element_bytes(w.dtype)
         done += 1
     dt = time.perf_counter() - t0
-    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+    cpu = time.process_time() - c0
+    # cores actually kept busy: CPU time over wall time (the BLAS pool may be
+    # larger, but small per-sequence products leave most of it idle)
+    used = max(1, round(cpu / dt)) if dt > 0 else 1
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": int(used),
             "kind": "oracle",
             "sample": f"float64 NumPy oracle decode (gather + two-pass softmax), one sequence at "
                       f"a time, cycling over the workload's {w.num_seqs} sequences: {done} "
                       f"sequence decodes ({done / w.num_seqs:.1f} passes, {kv / 1e6:.1f} MB of "
-                      f"KV) in {dt:.1f} s; host has {os.cpu_count()} CPUs",
+                      f"KV) in {dt:.1f} s, {cpu:.1f} s of CPU time ({cpu / dt:.2f} cores busy "
+                      f"on average; BLAS pool of {threads} threads, host has {os.cpu_count()} "
+                      f"CPUs)",
             "seqs_per_s": round(done / dt, 3)}
 
 
