@@ -37,9 +37,11 @@
  *   e4m3(c) * k_scale, of the V pool for e4m3(c) * v_scale.  Queries and new
  *   tokens of an 8-bit cache are bfloat16.
  * - Device-side contents are not validated beyond what keeps every access in
- *   bounds: a block id outside [0, num_blocks) in a table or pair, or a slot
- *   outside [0, num_blocks*block_size), is skipped (its rows take no part);
- *   context lengths are clamped to max_blocks_per_seq*block_size.
+ *   bounds: a block id outside [0, num_blocks) in a pair, or a slot outside
+ *   [0, num_blocks*block_size), is skipped; such a block id in a table is
+ *   skipped by the decode entry points (its rows take no part in the softmax)
+ *   and read by pa_prefill as zero rows (keys and values of zero); context
+ *   lengths are clamped to max_blocks_per_seq*block_size.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H

@@ -661,7 +661,8 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
       __builtin_amdgcn_global_load_lds(a.v_pool + base + vo, (PA_LDS(void)*)lv, 16, 0, 0);
     }
   };
-  // V rows that must read as zero: past the context, or in a block outside the pool
+  // V rows that must read as zero: past the context, or in a block outside the
+  // pool (whose K rows read as zero too)
   auto fix_needed = [&](int kt) -> bool {
     const int k0 = kt * kKeys;
     if (k0 + kKeys > kend) return true;
@@ -675,10 +676,15 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
     constexpr int PPT = 512 / (64 * NW);        // 16-byte pieces per thread (32 rows x 16)
     const int row = tid / (16 / PPT);
     const int key = k0 + row;
-    const bool zero = key >= kend || entry(key / BS) < 0;
-    if (zero) {
-      u32x4* dst = reinterpret_cast<u32x4*>(s_mem + stage * kStageBytes + kKeys * kRowBytes +
-                                            row * kRowBytes) + PPT * (tid % (16 / PPT));
+    const bool past = key >= kend;
+    const bool out = !past && entry(key / BS) < 0;  // a block outside the pool
+    u32x4* dst = reinterpret_cast<u32x4*>(s_mem + stage * kStageBytes + row * kRowBytes) +
+                 PPT * (tid % (16 / PPT));
+    if (past || out) {
+#pragma unroll
+      for (int e = 0; e < PPT; ++e) dst[kKeys * kRowBytes / 16 + e] = u32x4{0u, 0u, 0u, 0u};
+    }
+    if (out) {  // its keys too read as zero (the DMA brought block 0's rows)
 #pragma unroll
       for (int e = 0; e < PPT; ++e) dst[e] = u32x4{0u, 0u, 0u, 0u};
     }
