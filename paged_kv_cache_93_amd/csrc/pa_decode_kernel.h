@@ -187,6 +187,17 @@ __device__ __forceinline__ float xor_max(float x) {
   }
 }
 
+// Sum and maximum over the 64 lanes of a wave, the same bits in every lane:
+// DPP row rotations inside each row of 16, then the lane swaps across rows.
+__device__ __forceinline__ float wave_sum(float x) { return xor_sum<16>(group_sum<16>(x)); }
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<0x128>(x));  // row_ror:8
+  x = fmaxf(x, dpp<0x124>(x));  // row_ror:4
+  x = fmaxf(x, dpp<0x122>(x));  // row_ror:2
+  x = fmaxf(x, dpp<0x121>(x));  // row_ror:1
+  return xor_max<16>(x);
+}
+
 // Inclusive prefix sum over the 64 lanes: shifted adds inside each row of 16
 // lanes (DPP row_shr), then the running totals of rows 0 and 0..1 carried
 // into the rows after them (DPP row_bcast:15 and row_bcast:31).
@@ -1322,9 +1333,7 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
         v[i] = p < cnt ? *reinterpret_cast<const f32x4*>(rows + size_t(p0 + p) * stride)
                        : f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      float cmax = ps > 0.f ? pm : kNegInf;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, off));
+      const float cmax = wave_max(ps > 0.f ? pm : kNegInf);
       const float nb = fmaxf(big, cmax);
       if (nb != big) {
         const float f = big == kNegInf ? 0.f : fast_exp2(big - nb);
@@ -1333,10 +1342,7 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
         big = nb;
       }
       const float w = ps > 0.f ? ps * fast_exp2(pm - big) : 0.f;
-      float ws = w;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) ws += __shfl_xor(ws, off);
-      wsum += ws;
+      wsum += wave_sum(w);
       for (int b0 = 0; b0 < cnt; b0 += PB) {
         if (b0 > 0) {
 #pragma unroll
@@ -1348,18 +1354,23 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < NBATCH; ++i) {
-          const int p = b0 + i * PPI + sub;  // < 64; lanes past cnt hold w = 0
-          const float wp = __shfl(w, p);
+          // the weight of piece b0 + i PPI + sub (< 64; lanes past cnt hold
+          // w = 0): lane reads of the PPI candidates, no LDS round trip
+          float wp = 0.f;
+#pragma unroll
+          for (int k = 0; k < PPI; ++k) {
+            const float c = __uint_as_float(__builtin_amdgcn_readlane(
+                __float_as_uint(w), b0 + i * PPI + k));
+            wp = sub == k ? c : wp;
+          }
           acc += wp * v[i];
         }
       }
     }
-    // add up the PPI pieces of each load instruction's lane groups
+    // add up the PPI pieces of each load instruction's lane groups (lane
+    // swaps for 16 and 32 lanes apart)
 #pragma unroll
-    for (int off = LR; off < 64; off <<= 1) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], off);
-    }
+    for (int e = 0; e < 4; ++e) acc[e] = xor_sum<LR>(acc[e]);
   }
   if (lane >= LR) return;
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
