@@ -744,11 +744,11 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
     }
   };
 
-  // current piece: units from its start up to pend of sequence seq; `whole` when it is
+  // current piece: units [pstart, pend) of sequence seq; `whole` when it is
   // all of the sequence (balanced mode).  sq is unit uu's sequence, taken from
   // the table-entry window that covers uu (no search of the prefix).
   int seq;
-  int64_t pend;
+  int64_t pstart, pend;
   bool whole;
   // a piece that ended and is closed at the start of the next step
   bool closing = false;
@@ -765,6 +765,7 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs a) {
       pend = min(uend, last);
       whole = uu == first && pend == last;
     }
+    pstart = uu;
   };
 
   // Windows of units [cbase, +64) and [+64, +128); tiles at most PF ahead of
