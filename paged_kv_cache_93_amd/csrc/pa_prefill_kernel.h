@@ -20,9 +20,12 @@
 //   position).  The workgroup stages each 32-key K/V tile in LDS, row-major
 //   with XOR-swizzled 16-byte pieces: the MFMA A operand of S^T = K Q^T reads
 //   16-byte K row pieces, and the A operand of O^T = V^T P^T (keys contiguous
-//   per dimension) comes from the transposed LDS read.  bf16 tiles go in by
-//   LDS DMA; 8-bit codes become bf16 in registers on the way in (exact; the
-//   scales are folded into the score scale and the output).
+//   per dimension) comes from the transposed LDS read.  Tiles go in by LDS
+//   DMA; 8-bit codes land as they are in the half of the stage that rows
+//   16..31 take and the workgroup expands them into the bf16 layout in LDS
+//   (exact; the scales are folded into the score scale and the output).  A
+//   register-staged kernel, which converts the codes on their way from
+//   memory, stays as the comparison path (PA_PREFILL_DMA / _DMA_FP8 = 0).
 // * Scores come out as S^T, so lane 16g + r holds keys 4g..4g+3 (and 16 +
 //   4g..) of query row r: the softmax weights P are already the B operand of
 //   O^T = V^T P^T in that lane (the k order of the two operands is permuted
@@ -67,6 +70,9 @@ constexpr int kTblWin = 1024;
 
 #ifndef PA_PREFILL_DMA
 #define PA_PREFILL_DMA 1  // 0: bf16 caches take the register-staged kernel too (for comparison)
+#endif
+#ifndef PA_PREFILL_DMA_FP8
+#define PA_PREFILL_DMA_FP8 1  // 0: 8-bit caches take the register-staged kernel
 #endif
 
 #ifndef PA_PREFILL_KSWZ
@@ -519,12 +525,15 @@ constexpr int kStages = 3;
 constexpr int kStageBytes = 2 * kKeys * kD * 2;  // K and V tiles, 16 KiB
 constexpr size_t kDmaLdsBytes = size_t(kStages) * kStageBytes + kTblWin * sizeof(int32_t);
 
-template <int BS, int G, bool OUT_F32, bool AL, int NRT>
-__global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
-    prefill_dma_kernel(PrefillArgs a) {
+template <int ET, int BS, int G, bool OUT_F32, bool AL, int NRT>
+__device__ __forceinline__ void prefill_dma_body(PrefillArgs a) {
   constexpr int TT = kRows / G;  // tokens per tile
   constexpr int NW = 8 / NRT;    // waves; each owns 16 NRT query rows
   static_assert(NRT == 2 || NRT == 4, "16-row tiles per wave");
+  static_assert(ET == kBF16 || (ET == kFP8 && NW == 4), "8-bit tiles: one DMA per wave");
+  // this wave's DMA instructions per tile: NRT per tensor of bf16 rows, one per
+  // tensor of 8-bit rows (eight 128-byte rows)
+  constexpr int kDmaPerWave = ET == kFP8 ? 2 : 2 * NRT;
   extern __shared__ __attribute__((aligned(1024))) uint8_t s_mem[];
 
   const int tid = threadIdx.x;
@@ -639,6 +648,22 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
   // per tile.
   auto issue = [&](int kt, int stage) {
     const int k0 = kt * kKeys;
+    if constexpr (ET == kFP8) {
+      // Rows 8w .. 8w+7 of the tile, 128 bytes each (eight share a block: block
+      // sizes are multiples of 8), land as they are in the upper half of the
+      // stage's K and V areas; convert() expands them into the bf16 layout.
+      const int r0 = 8 * wave;
+      const uint32_t key0 = uint32_t(k0 + r0);
+      int phys = __builtin_amdgcn_readfirstlane(entry(min(int(key0 / BS), nblk - 1)));
+      phys = phys < 0 ? 0 : phys;
+      const int64_t base = int64_t(phys) * (blk_stride / 2) + head_off / 2 +
+                           int64_t(key0 % BS) * (kRowBytes / 2) + lane * 16;
+      uint8_t* lk = s_mem + stage * kStageBytes + kKeys * kRowBytes / 2 + r0 * (kRowBytes / 2);
+      uint8_t* lv = lk + kKeys * kRowBytes;
+      __builtin_amdgcn_global_load_lds(a.k_pool + base, (PA_LDS(void)*)lk, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.v_pool + base, (PA_LDS(void)*)lv, 16, 0, 0);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NRT; ++i) {
       const int r0 = 4 * NRT * wave + 4 * i;  // first row of the group (wave-uniform)
@@ -690,6 +715,36 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
     }
   };
 
+  // 8-bit tiles: every thread expands one 16-byte chunk (16 codes: row
+  // tid / 8, dims 16 (tid % 8) ..) of K and of V into two 16-byte bf16 pieces
+  // at their swizzled places.  The codes sit where rows 16..31 go, so every
+  // chunk is read before any piece is written.  The scales are applied to the
+  // scores and the outputs (codes convert to bf16 exactly).
+  auto convert = [&](int stage) {
+    const int r = tid >> 3, ch = tid & 7;
+    uint8_t* lk = s_mem + stage * kStageBytes;
+    uint8_t* lv = lk + kKeys * kRowBytes;
+    const u32x4 kc = *reinterpret_cast<const u32x4*>(lk + kKeys * kRowBytes / 2 + tid * 16);
+    const u32x4 vc = *reinterpret_cast<const u32x4*>(lv + kKeys * kRowBytes / 2 + tid * 16);
+    wait_vm_lgkm<63>();  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int pc = 2 * ch + h;  // logical bf16 piece of the row
+      const u32x2 kh = {kc[2 * h], kc[2 * h + 1]};
+      const u32x2 vh = {vc[2 * h], vc[2 * h + 1]};
+      *reinterpret_cast<u32x4*>(lk + r * kRowBytes + ((pc ^ (r & (PA_PREFILL_KSWZ - 1))) << 4)) =
+          score_chunk<kFP8>(kh);
+      *reinterpret_cast<u32x4*>(lv + r * kRowBytes +
+                                ((pc ^ (2 * (r & (PA_PREFILL_VSWZ - 1)))) << 4)) =
+          score_chunk<kFP8>(vh);
+    }
+    wait_vm_lgkm<63>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
   // prologue: kStages-1 tiles in flight
 #pragma unroll
   for (int p = 0; p < kStages - 1; ++p)
@@ -702,11 +757,12 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
     // this wave's DMAs of tile kt have landed once at most 2 NRT per later tile remain
     const int later = min(kStages - 2, ntiles - 1 - kt);
     if (later >= 1)
-      wait_vm_lgkm<2 * NRT>();
+      wait_vm_lgkm<kDmaPerWave>();
     else
       wait_vm_lgkm<0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    if constexpr (ET == kFP8) convert(stage);
     if (fix_needed(kt)) {
       fix(kt, stage);
       wait_vm_lgkm<63>();  // lgkmcnt(0): the zeros are written before the barrier
@@ -815,6 +871,19 @@ __global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
   }
 }
 
+template <int BS, int G, bool OUT_F32, bool AL, int NRT>
+__global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
+    prefill_dma_kernel(PrefillArgs a) {
+  prefill_dma_body<kBF16, BS, G, OUT_F32, AL, NRT>(a);
+}
+
+// 8-bit caches: the same kernel, staging the codes and expanding them in LDS
+template <int BS, int G, bool OUT_F32, bool AL, int NRT>
+__global__ void __launch_bounds__(64 * (8 / NRT), NRT == 2 ? 2 : 1)
+    prefill_dma8_kernel(PrefillArgs a) {
+  prefill_dma_body<kFP8, BS, G, OUT_F32, AL, NRT>(a);
+}
+
 template <int ET, int BS, int G>
 int launch_g(const PrefillArgs& a, bool out_f32, dim3 grid, hipStream_t stream) {
   const bool al = a.alibi != nullptr;
@@ -830,6 +899,18 @@ int launch_g(const PrefillArgs& a, bool out_f32, dim3 grid, hipStream_t stream) 
       hipLaunchKernelGGL((prefill_dma_kernel<BS, G, false, true, NRT>), grid, block, lds, stream, a);
     else
       hipLaunchKernelGGL((prefill_dma_kernel<BS, G, false, false, NRT>), grid, block, lds, stream, a);
+    return launch_result("pa_prefill");
+  } else if constexpr (ET == kFP8 && PA_PREFILL_DMA_FP8) {
+    const size_t lds = kDmaLdsBytes;
+    const dim3 block(256);
+    if (out_f32 && al)
+      hipLaunchKernelGGL((prefill_dma8_kernel<BS, G, true, true, 2>), grid, block, lds, stream, a);
+    else if (out_f32)
+      hipLaunchKernelGGL((prefill_dma8_kernel<BS, G, true, false, 2>), grid, block, lds, stream, a);
+    else if (al)
+      hipLaunchKernelGGL((prefill_dma8_kernel<BS, G, false, true, 2>), grid, block, lds, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_dma8_kernel<BS, G, false, false, 2>), grid, block, lds, stream, a);
     return launch_result("pa_prefill");
   } else {
     const size_t lds = 2 * kBufBytes + kTblWin * sizeof(int32_t);
