@@ -467,7 +467,7 @@ def bench_prefill(args) -> dict:
                    "alibi": bool(args.alibi)},
         "workloads": rows,
         "roofline": {"bound": "mfma",
-                     "kernel": "prefill_dma_kernel" if dtype == "bf16" else "prefill_kernel",
+                     "kernel": "prefill_dma_kernel" if dtype == "bf16" else "prefill_dma8_kernel",
                      "achieved": head["tflops"],
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": head["frac"],
                      "traffic": None},
@@ -520,7 +520,8 @@ def sq_summary(root: str, dtype: str, command: str) -> str:
             for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
                 for row in csv.DictReader(open(f)):
                     name = row["Kernel_Name"]
-                    if "prefill_dma_kernel" in name or "prefill_kernel" in name:
+                    if any(k in name for k in ("prefill_dma_kernel", "prefill_dma8_kernel",
+                                               "prefill_kernel")):
                         vals[(pname, row["Counter_Name"])].append(float(row["Counter_Value"]))
         if not vals:
             continue
@@ -603,7 +604,8 @@ def prefill_ktrace_summary(root: str, dtype: str, steps: int, command: str) -> s
                 d = (int(row["Start_Timestamp"]), int(row["End_Timestamp"]))
                 if "prefill_tiles_kernel" in name:
                     tiles.append(d)
-                elif "prefill_dma_kernel" in name or "prefill_kernel" in name:
+                elif any(k in name for k in ("prefill_dma_kernel", "prefill_dma8_kernel",
+                                             "prefill_kernel")):
                     attn.append((d, name.replace("void ", "").split("(")[0]))
         if not attn:
             continue
