@@ -715,34 +715,38 @@ __device__ __forceinline__ void prefill_dma_body(PrefillArgs a) {
     }
   };
 
-  // 8-bit tiles: every thread expands one 16-byte chunk (16 codes: row
-  // tid / 8, dims 16 (tid % 8) ..) of K and of V into two 16-byte bf16 pieces
-  // at their swizzled places.  The codes sit where rows 16..31 go, so every
-  // chunk is read before any piece is written.  The scales are applied to the
-  // scores and the outputs (codes convert to bf16 exactly).
+  // 8-bit tiles: every thread expands two 8-byte halves of chunks (8 codes:
+  // piece p of row r, 16 r + p = 256 i + tid) of K and of V into 16-byte bf16
+  // pieces at their swizzled places, so the 16 lanes of a store cover the 16
+  // pieces of one row (no bank conflict).  The codes sit where rows 16..31
+  // go, so every half is read before any piece is written.  The scales are
+  // applied to the scores and the outputs (codes convert to bf16 exactly).
   auto convert = [&](int stage) {
-    const int r = tid >> 3, ch = tid & 7;
+    __builtin_amdgcn_sched_barrier(0);
     uint8_t* lk = s_mem + stage * kStageBytes;
     uint8_t* lv = lk + kKeys * kRowBytes;
-    const u32x4 kc = *reinterpret_cast<const u32x4*>(lk + kKeys * kRowBytes / 2 + tid * 16);
-    const u32x4 vc = *reinterpret_cast<const u32x4*>(lv + kKeys * kRowBytes / 2 + tid * 16);
+    u32x2 kh[2], vh[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      kh[i] = *reinterpret_cast<const u32x2*>(lk + kKeys * kRowBytes / 2 + (256 * i + tid) * 8);
+      vh[i] = *reinterpret_cast<const u32x2*>(lv + kKeys * kRowBytes / 2 + (256 * i + tid) * 8);
+    }
     wait_vm_lgkm<63>();  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int pc = 2 * ch + h;  // logical bf16 piece of the row
-      const u32x2 kh = {kc[2 * h], kc[2 * h + 1]};
-      const u32x2 vh = {vc[2 * h], vc[2 * h + 1]};
+    for (int i = 0; i < 2; ++i) {
+      const int r = 16 * i + (tid >> 4), pc = tid & 15;
       *reinterpret_cast<u32x4*>(lk + r * kRowBytes + ((pc ^ (r & (PA_PREFILL_KSWZ - 1))) << 4)) =
-          score_chunk<kFP8>(kh);
+          score_chunk<kFP8>(kh[i]);
       *reinterpret_cast<u32x4*>(lv + r * kRowBytes +
                                 ((pc ^ (2 * (r & (PA_PREFILL_VSWZ - 1)))) << 4)) =
-          score_chunk<kFP8>(vh);
+          score_chunk<kFP8>(vh[i]);
     }
     wait_vm_lgkm<63>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // prologue: kStages-1 tiles in flight
